@@ -1,0 +1,266 @@
+"""Benchmark of one ConvKV AR step on one MI355X.
+
+A step is one pass of the whole hot path for one cache (one layer, one diffusion step):
+lact_rope_reset_apply -> lact_block_attention -> lact_kv_ring_append ->
+lact_convkv_compress, at steady state (memory full: 16 slots + 8 window frames + the
+8-frame block, Lq 8192, Lk 32768 at 512x512).  Inputs are seeded synthetic tensors of the
+workload's shapes, generated before timing and resident in HBM (a pool of 7 blocks cycled
+through, so consecutive steps read different data).
+
+Prints one JSON line: whole-step latent frames/s as `value`, the attention kernel's
+achieved TFLOP/s against the bf16 MFMA peak in `roofline`, and the CPU oracle timed on a
+bounded sample of the same step in `cpu_baseline`.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload s512_bf16]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("ConvKV block-attn TFLOP/s + latent frames/s per AR step (512×512); "
+          "% of roofline")
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="s512_bf16")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--pool-blocks", type=int, default=7)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=12, help="oracle rows per head in the sample")
+    return p.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "compressed_kv_causal_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_file, launches_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    ent = d.get(launches_key)
+    if not ent or ent.get("source_hash") != source_hash(kernel_file):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the ConvKV step is built and measured for a "
+              "single MI355X (no sharding or collectives in this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import compressed_kv_causal_amd as L
+    import synth
+
+    w = synth.workload(args.workload)
+    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    B = w["block"]
+    dt = {0: "f32", 1: "bf16", 2: "fp8"}[w["kv_dtype"]]
+    io = torch.float32 if w["q_dtype"] == 0 else torch.bfloat16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs: a pool of blocks resident in HBM ------------------------------------
+    pool = []
+    for blk in range(args.pool_blocks):
+        ids = list(range(blk * B, (blk + 1) * B))
+        trip = []
+        for tensor in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V):
+            x = synth.frames(w, args.seed, tensor, ids).reshape(B * T, H, D)
+            trip.append(torch.from_numpy(x).to(io).to(dev))
+        pool.append(trip)
+    wk, bk = synth.conv_weights(w, args.seed, synth.TENSOR_WK)
+    wv, bv = synth.conv_weights(w, args.seed, synth.TENSOR_WV)
+    d_wk, d_bk, d_wv, d_bv = (torch.from_numpy(a).to(dev) for a in (wk, bk, wv, bv))
+
+    cache = L.Cache(L.make_cfg(**w), device=dev)
+    Lq = B * T
+    out = torch.empty((Lq, H, D), dtype=io, device=dev)
+    lse = torch.empty((H, Lq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    h = cache.h
+    first_block = w["first_block"]
+
+    def step(i, ev=None):
+        q, k, v = pool[i % len(pool)]
+        n = first_block if i == 0 else B
+        if n != B:
+            q, k, v = q[: n * T], k[: n * T], v[: n * T]
+        if ev is not None:
+            ev[0].record(stream)
+        L.lact_rope_reset_apply(h, q, k, v, n, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        L.lact_block_attention(h, None, out[: n * T], lse[:, : n * T] if n == B else None, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        L.lact_kv_ring_append(h, k, v, n, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        L.lact_convkv_compress(h, d_wk, d_bk, d_wv, d_bv, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    # fill the memory: after 11 blocks of 8 frames, 80 frames were evicted -> 16 slots
+    i = 0
+    while True:
+        st = cache.state()
+        if st["mem_len"] == w["mem_slots"] and st["win_len"] == w["window_frames"] and i > 0:
+            break
+        step(i)
+        i += 1
+    for _ in range(args.warmup):
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+    n_hist = cache.state()["mem_len"] + cache.state()["win_len"]
+    Lk = (n_hist + B) * T
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(i, evs[s])
+        i += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part = np.array([[evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(4)]
+                     for s in range(args.steps)])  # ms
+    ms = part.mean(axis=0)
+    ms_step_events = float(part.sum(axis=1).mean())
+    ms_per_step = wall * 1e3 / args.steps
+
+    frame_bytes = T * H * D * {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+    attn_flop = 4.0 * Lq * Lk * D * H
+    attn_tflops = attn_flop / (ms[1] * 1e-3) / 1e12
+    peak = PEAK[dt]
+    # algorithmic bytes of the streaming kernels (per step)
+    rope_bytes = frame_bytes * (2 * n_hist + 6 * B)
+    append_bytes = 4 * B * frame_bytes
+    slots_per_step = B / w["ratio"]
+    compress_bytes = slots_per_step * 2 * frame_bytes * (w["ratio"] + 1)
+    traffic = load_traffic("k_attn.hip", f"attn_{args.workload}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(B / (ms_per_step * 1e-3), 2),
+        "unit": "latent frames/s (one layer, one diffusion step, steady state)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded N(0,1) Q/K/V, N(0,0.2) conv weights; HDTF/EMTD stand-in)",
+        "config": {"workload": args.workload, "heads": H, "head_dim": D, "tokens_per_frame": T,
+                   "block_frames": B, "window_frames": w["window_frames"],
+                   "mem_slots": w["mem_slots"], "ratio": w["ratio"], "Lq": Lq, "Lk": Lk},
+        "attn_tflops": round(attn_tflops, 2),
+        "step_breakdown_ms": {"rope_reset_apply": round(ms[0], 4),
+                              "block_attention": round(ms[1], 4),
+                              "kv_ring_append": round(ms[2], 4),
+                              "convkv_compress": round(ms[3], 4),
+                              "sum_of_events": round(ms_step_events, 4)},
+        "stream_gbs": {"rope_reset_apply": round(rope_bytes / (ms[0] * 1e-3) / 1e9, 1),
+                       "kv_ring_append": round(append_bytes / (ms[2] * 1e-3) / 1e9, 1),
+                       "convkv_compress": round(compress_bytes / (ms[3] * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": traffic,
+                     "kernel": "k_attn (block attention)",
+                     "algorithmic_per_launch": f"{attn_flop:.4e} flop = 4*Lq*Lk*D*H"},
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, i, wk, bk,
+                                           wv, bv)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv, bv):
+    """The oracle, as it stands, on a bounded sample of the same steady-state step: the
+    attention of every head for a few query rows over the full key set (history rebuilt
+    by the oracle's own compressor from the same frames), extrapolated to the whole step."""
+    import oracle as O
+    from oracle.stream import OracleCache
+    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    io_bf16 = w["q_dtype"] == 1
+    import torch
+
+    # Rebuild the oracle state of the GPU cache at this step (its frames come from the pool:
+    # block n uses pool block n mod len(pool)).
+    st = cache.state()
+    oc = OracleCache(w)
+    np_pool = [[t.float().cpu().numpy().reshape(B, -1) for t in trip] for trip in pool]
+    t_setup = time.perf_counter()
+    oc.bk.F, oc.bk.G = st["F"], st["G"] - st["mem_len"]
+    # frames still needed: the groups in memory and the window
+    E = st["E"]
+    need = list(range(w["ratio"] * oc.bk.G, st["F"]))
+    for f in need:
+        blk = f // B
+        k = np_pool[blk % len(pool)][1][f % B]
+        v = np_pool[blk % len(pool)][2][f % B]
+        oc.raw[f] = (oc._store(k), oc._store(v))
+    oc.bk.F = st["F"]
+    groups = []
+    while len(groups) < st["mem_len"]:
+        # compress the groups present in memory (each from its own 5 frames)
+        groups.append(oc.bk.G)
+        g = oc.bk.G
+        r = w["ratio"]
+        xk = np.stack([oc._f32(oc.raw[r * g + k][0]) for k in range(r)])
+        xv = np.stack([oc._f32(oc.raw[r * g + k][1]) for k in range(r)])
+        oc.mem[g % w["mem_slots"]] = (g, oc._store(O.compress_chain_f32(xk, wk, bk)),
+                                      oc._store(O.compress_chain_f32(xv, wv, bv)))
+        oc.bk.G += 1
+    setup_s = time.perf_counter() - t_setup
+    assert oc.bk.E == E and len(oc.keys(0)) == n_hist
+    q, k, v = (np_pool[(next_step) % len(pool)][j].reshape(B * T, H, D) for j in range(3))
+    rows = np.linspace(0, Lq - 1, args.cpu_rows).astype(np.int64)
+    heads = np.repeat(np.arange(H, dtype=np.int32), len(rows))
+    rr = np.tile(rows, H)
+    threads = min(16, os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    oc.attention(q, k, v, sel=(heads, rr), threads=threads)
+    secs = time.perf_counter() - t0
+    frac = len(rr) / float(H * Lq)
+    full = secs / frac
+    return {"value": round(B / full, 6), "unit": "latent frames/s (one layer, one diffusion step)",
+            "cores": threads, "kind": "oracle",
+            "sample": (f"attention of all {H} heads x {len(rows)} query rows over Lk={Lk} keys "
+                       f"({secs:.1f} s, double precision), extrapolated x{1 / frac:.0f} to the "
+                       f"full step; history built by the oracle's compressor in {setup_s:.1f} s "
+                       "(not counted); rope/append/compress not counted")}
+
+
+if __name__ == "__main__":
+    main()

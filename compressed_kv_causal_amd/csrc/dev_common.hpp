@@ -1,0 +1,177 @@
+// dev_common.hpp -- device helpers: bf16 and OCP e4m3 codecs, vector loads, reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace lact {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest, ties to even; overflow goes to +-inf as IEEE rounding does; NaN stays
+// a quiet NaN of the same sign.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// OCP E4M3FN: bias 7, no infinities, S.1111.111 = NaN, largest finite 448, subnormals
+// m * 2^-9.  Exact decode.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));
+  if (e == 15 && m == 7) return __uint_as_float(0x7FC00000u | s);
+  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// Nearest e4m3 code, ties to even mantissa, |y| >= 448 saturates to +-448, NaN -> 0x7F/0xFF.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  uint32_t u = __float_as_uint(y);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;           // |y| >= 448
+  if (a < 0x3C800000u) {                                // |y| < 2^-6: multiples of 2^-9
+    float q = rintf(__uint_as_float(a) * 512.0f);       // exact scaling, then round half even
+    return sign | (uint32_t)q;                          // 8 -> 0x08 = 2^-6, also correct
+  }
+  uint32_t e = (a >> 23) - 120u;                        // biased e4m3 exponent 1..15
+  uint32_t m = (a >> 20) & 7u;
+  uint32_t rest = a & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) {
+    if (++m == 8u) {
+      m = 0;
+      ++e;
+    }
+  }
+  return sign | (e << 3) | m;
+}
+
+// Row quantiser of the FP8 cache, per (token, head): scale = amax / 448, y = x * (448 / amax)
+// (one f32 rounding each; amax = 0 -> scale 1, y = x).
+struct RowQuant {
+  float scale, inv;
+};
+__device__ __forceinline__ RowQuant row_quant(float amax) {
+  RowQuant q;
+  if (amax > 0.0f) {
+    q.scale = __fdiv_rn(amax, 448.0f);
+    q.inv = __fdiv_rn(448.0f, amax);
+  } else {
+    q.scale = 1.0f;
+    q.inv = 1.0f;
+  }
+  return q;
+}
+
+// max over groups of `width` consecutive lanes (width a power of two <= 64)
+template <int width>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, width));
+  return v;
+}
+
+// 8 consecutive elements as f32, from f32 / bf16 / fp8(code*scale) storage.
+__device__ __forceinline__ void load8_f32(const float* p, float* x) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8_bf16(const uint16_t* p, float* x) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8_fp8(const uint8_t* p, float scale, float* x) {
+  uint2 v = *reinterpret_cast<const uint2*>(p);
+  uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = e4m3_to_f32((w[i / 4] >> (8 * (i % 4))) & 0xFFu) * scale;
+}
+
+__device__ __forceinline__ void store8_f32(float* p, const float* x) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8_bf16(uint16_t* p, const float* x) {
+  uint4 v;
+  v.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+  v.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+  v.z = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
+  v.w = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
+  *reinterpret_cast<uint4*>(p) = v;
+}
+// quantises 8 values with the row's inverse scale and stores 8 codes
+__device__ __forceinline__ void store8_fp8(uint8_t* p, const float* x, float inv) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i / 4] |= f32_to_e4m3(x[i] * inv) << (8 * (i % 4));
+  *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+}
+
+// Load 8 input elements (q dtype: F32 or BF16) starting at element offset off.
+__device__ __forceinline__ void load8_in(const void* base, int32_t dtype, int64_t off, float* x) {
+  if (dtype == DT_F32)
+    load8_f32(static_cast<const float*>(base) + off, x);
+  else
+    load8_bf16(static_cast<const uint16_t*>(base) + off, x);
+}
+
+// Load 8 stored elements (kv dtype) at element offset off; row_scale used for FP8.
+__device__ __forceinline__ void load8_kv(const void* base, int32_t dtype, int64_t off,
+                                         float row_scale, float* x) {
+  if (dtype == DT_F32)
+    load8_f32(static_cast<const float*>(base) + off, x);
+  else if (dtype == DT_BF16)
+    load8_bf16(static_cast<const uint16_t*>(base) + off, x);
+  else
+    load8_fp8(static_cast<const uint8_t*>(base) + off, row_scale, x);
+}
+
+// Store 8 elements in dtype at element offset off.  FP8 quantises the row: every lane of
+// the row's group (lanes_per_row consecutive lanes) must call this together; the row's
+// scale is returned (and written by the caller).
+template <int lanes_per_row>
+__device__ __forceinline__ float store8_kv(void* base, int32_t dtype, int64_t off, const float* x) {
+  if (dtype == DT_F32) {
+    store8_f32(static_cast<float*>(base) + off, x);
+    return 1.0f;
+  }
+  if (dtype == DT_BF16) {
+    store8_bf16(static_cast<uint16_t*>(base) + off, x);
+    return 1.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = group_max<lanes_per_row>(amax);
+  RowQuant rq = row_quant(amax);
+  store8_fp8(static_cast<uint8_t*>(base) + off, x, rq.inv);
+  return rq.scale;
+}
+
+// Frame base element offset of history frame fi in memory or in the raw ring.
+__device__ __forceinline__ bool hist_is_mem(const HistMap& m, int32_t fi) { return fi < m.mem_len; }
+__device__ __forceinline__ int32_t hist_slot(const HistMap& m, int32_t fi) {
+  int32_t s;
+  if (fi < m.mem_len) {
+    s = m.mem_slot0 + fi;
+    return s >= m.M ? s - m.M : s;
+  }
+  s = m.ring_slot0 + (fi - m.mem_len);
+  return s >= m.R ? s - m.R : s;
+}
+
+}  // namespace lact

@@ -1,0 +1,238 @@
+// k_stream.hip -- the bandwidth-bound kernels of the step, for gfx950:
+//   k_ring_write   append-only ring append (+ FP8 row quantisation)
+//   k_compress     ConvKV depthwise strided temporal conv, r frames -> one memory slot
+//   k_rope_table   cos/sin table of the bounded reset positions (double, once per cache)
+//   k_rope         RoPE reset + apply: rotated history keys, rotated block Q/K, staged V
+//
+// Work unit everywhere: one (token, head) row of D channels, handled by D/8 consecutive
+// lanes, 8 channels (16 bytes of bf16) per lane, so a wave reads and writes 64 x 16 B
+// contiguous segments; FP8 row scales come from a reduction over the row's lanes.
+#include "dev_common.hpp"
+
+namespace lact {
+
+// ---------------------------------------------------------------------------------------
+// Append (walkthrough "SoulX-LiveAct", sections "ConvKV Memory" and "Streaming Pipeline":
+// cached KV stay unchanged, only the new block's KV are added).
+// ---------------------------------------------------------------------------------------
+template <int LPR>
+__global__ __launch_bounds__(256) void k_ring_write(const RingWriteArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / LPR;
+  const int li = (int)(gid % LPR);
+  const int tensor = blockIdx.y;
+  const int64_t TH = (int64_t)a.T * a.H;
+  if (row >= (int64_t)a.n_frames * TH) return;
+  const int32_t fi = (int32_t)(row / TH);
+  int32_t slot = a.slot0 + fi;
+  if (slot >= a.R) slot -= a.R;
+  const int64_t drow = (int64_t)slot * TH + (row - (int64_t)fi * TH);
+  float x[8];
+  load8_in(a.src[tensor], a.in_dtype, row * a.D + li * 8, x);
+  const float s = store8_kv<LPR>(a.ring[tensor], a.kv_dtype, drow * a.D + li * 8, x);
+  if (a.kv_dtype == DT_FP8 && li == 0) a.ring_scale[tensor][drow] = s;
+}
+
+// ---------------------------------------------------------------------------------------
+// ConvKV compression (news summary "SoulX-LiveAct - Soul App ...", technical principle,
+// ConvKV Memory bullet: 1D convolution at 5:1 into a fixed-length memory; arXiv listing,
+// Figure 3 caption: lightweight 1D convolution of the long-term KV).  Per (token u,
+// channel c): acc = b[c]; acc = fmaf(w[c][k], x_k[u][c], acc) for k = 0..r-1, in f32,
+// then stored in the cache dtype.  Each input frame is read once.
+// ---------------------------------------------------------------------------------------
+template <int LPR>
+__global__ __launch_bounds__(256) void k_compress(const CompressArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / LPR;  // (u, h) = (row / H, row % H)
+  const int li = (int)(gid % LPR);
+  const int gi = blockIdx.y >> 1, tensor = blockIdx.y & 1;
+  const int64_t TH = (int64_t)a.T * a.H;
+  if (row >= TH) return;
+  const int32_t h = (int32_t)(row % a.H);
+  const int64_t c0 = (int64_t)h * a.D + li * 8;  // first channel of this lane
+  const float* w = a.w[tensor] + c0 * a.r;
+  const float* b = a.b[tensor] + c0;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = b[e];
+  for (int k = 0; k < a.r; ++k) {
+    int32_t slot = a.in_slot0[gi] + k;
+    if (slot >= a.R) slot -= a.R;
+    const int64_t srow = (int64_t)slot * TH + row;
+    const float sc = a.kv_dtype == DT_FP8 ? a.ring_scale[tensor][srow] : 1.0f;
+    float x[8];
+    load8_kv(a.ring[tensor], a.kv_dtype, srow * a.D + li * 8, sc, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[e * a.r + k], x[e], acc[e]);
+  }
+  const int64_t drow = (int64_t)a.out_slot[gi] * TH + row;
+  const float s = store8_kv<LPR>(a.mem[tensor], a.kv_dtype, drow * a.D + li * 8, acc);
+  if (a.kv_dtype == DT_FP8 && li == 0) a.mem_scale[tensor][drow] = s;
+}
+
+// ---------------------------------------------------------------------------------------
+// RoPE (press release digi.china.com, technical-principle paragraph: RoPE Reset keeps
+// positions aligned and bounded; news summary, ConvKV Memory bullet).  Interleaved pairs
+// (2i, 2i+1) of each part, angle = pos * theta^(-2i/d_part).  Positions are bounded by the
+// reset (t < M + W + B_max), so every angle comes from a small table computed once in
+// double precision and rounded to f32.
+//   3D table: [KF][d_t/2] (t) | [grid_h][d_h/2] (row) | [grid_w][d_w/2] (column)
+//   1D table: [KF*T][D/2], position t*T + u
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rope_table(const RopeTableArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.entries) return;
+  int64_t pos;
+  int32_t pair, dpart;
+  if (a.rope_mode == 1) {
+    const int32_t half = a.D / 2;
+    pos = i / half;
+    pair = (int32_t)(i % half);
+    dpart = a.D;
+  } else {
+    const int32_t ht = a.split_t / 2, hh = a.split_h / 2, hw = a.split_w / 2;
+    const int64_t nt = (int64_t)a.key_frames_max * ht, nh = (int64_t)a.grid_h * hh;
+    if (i < nt) {
+      pos = i / ht;
+      pair = (int32_t)(i % ht);
+      dpart = a.split_t;
+    } else if (i < nt + nh) {
+      pos = (i - nt) / hh;
+      pair = (int32_t)((i - nt) % hh);
+      dpart = a.split_h;
+    } else {
+      pos = (i - nt - nh) / hw;
+      pair = (int32_t)((i - nt - nh) % hw);
+      dpart = a.split_w;
+    }
+  }
+  const double ang = (double)pos * pow(a.theta, -2.0 * (double)pair / (double)dpart);
+  a.table[i] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// Rotates the 4 pairs of one lane (channels 8*li .. 8*li+7) at temporal position t.
+__device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32_t u, int li,
+                                             float* x) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int32_t pair = li * 4 + p;
+    float2 cs;
+    if (a.rope_mode == 1) {
+      cs = a.table[((int64_t)t * a.T + u) * (a.D / 2) + pair];
+    } else {
+      const int32_t ht = a.split_t / 2, hh = a.split_h / 2, hw = a.split_w / 2;
+      if (pair < ht) {
+        cs = a.table[t * ht + pair];
+      } else if (pair < ht + hh) {
+        cs = a.table[a.key_frames_max * ht + (u / a.grid_w) * hh + (pair - ht)];
+      } else {
+        cs = a.table[a.key_frames_max * ht + a.grid_h * hh + (u % a.grid_w) * hw +
+                     (pair - ht - hh)];
+      }
+    }
+    const float x0 = x[2 * p], x1 = x[2 * p + 1];
+    x[2 * p] = x0 * cs.x - x1 * cs.y;
+    x[2 * p + 1] = x0 * cs.y + x1 * cs.x;
+  }
+}
+
+// Rows [0, hist_rows): history key frame fi = row / (T*H) of [memory | window], rotated at
+// t = fi into krot[h][fi*T + u].  Rows after: current frame fi, t = n_hist + fi: q -> qrot,
+// k -> krot[h][(n_hist + fi)*T + u], v -> vcur.  FP8 quantises every output row.
+template <int LPR>
+__global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / LPR;
+  const int li = (int)(gid % LPR);
+  const int64_t TH = (int64_t)a.T * a.H;
+  const int32_t n_hist = a.hist.mem_len + a.hist.win_len;
+  const int64_t hist_rows = a.hist_rows ? (int64_t)n_hist * TH : 0;
+  const int64_t KFT = (int64_t)a.key_frames_max * a.T;
+  const int64_t QT = (int64_t)a.block_frames_max * a.T;
+  const int64_t D = a.D;
+  const bool fp8 = a.kv_dtype == DT_FP8;
+  float x[8];
+  if (row < hist_rows) {
+    const int32_t fi = (int32_t)(row / TH);
+    const int64_t rem = row - (int64_t)fi * TH;
+    const int32_t u = (int32_t)(rem / a.H), h = (int32_t)(rem % a.H);
+    const bool mem = hist_is_mem(a.hist, fi);
+    const int64_t srow = (int64_t)hist_slot(a.hist, fi) * TH + rem;
+    const float sc = fp8 ? (mem ? a.mem_k_scale : a.ring_k_scale)[srow] : 1.0f;
+    load8_kv(mem ? a.mem_k : a.ring_k, a.kv_dtype, srow * D + li * 8, sc, x);
+    rope_rotate8(a, fi, u, li, x);
+    const int64_t drow = h * KFT + (int64_t)fi * a.T + u;
+    const float s = store8_kv<LPR>(a.krot, a.kv_dtype, drow * D + li * 8, x);
+    if (fp8 && li == 0) a.krot_scale[drow] = s;
+    return;
+  }
+  const int64_t crow = row - hist_rows;  // = (fi*T + u)*H + h of the block's [n*T][H][D]
+  if (crow >= (int64_t)a.n_cur * TH) return;
+  const int32_t fi = (int32_t)(crow / TH);
+  const int64_t rem = crow - (int64_t)fi * TH;
+  const int32_t u = (int32_t)(rem / a.H), h = (int32_t)(rem % a.H);
+  const int32_t t = n_hist + fi;
+
+  load8_in(a.q, a.in_dtype, crow * D + li * 8, x);
+  rope_rotate8(a, t, u, li, x);
+  const int64_t qrow = h * QT + (int64_t)fi * a.T + u;
+  float s = store8_kv<LPR>(a.qrot, a.kv_dtype, qrow * D + li * 8, x);
+  if (fp8 && li == 0) a.qrot_scale[qrow] = s;
+
+  load8_in(a.k_cur, a.in_dtype, crow * D + li * 8, x);
+  rope_rotate8(a, t, u, li, x);
+  const int64_t krow = h * KFT + (int64_t)t * a.T + u;
+  s = store8_kv<LPR>(a.krot, a.kv_dtype, krow * D + li * 8, x);
+  if (fp8 && li == 0) a.krot_scale[krow] = s;
+
+  load8_in(a.v_cur, a.in_dtype, crow * D + li * 8, x);
+  s = store8_kv<LPR>(a.vcur, a.kv_dtype, crow * D + li * 8, x);
+  if (fp8 && li == 0) a.vcur_scale[crow] = s;
+}
+
+// ---------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------
+static inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
+
+hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
+  if (a.entries <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_table, dim3(blocks_for(a.entries)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int lpr = a.D / 8;
+  dim3 grid(blocks_for(rows * lpr), 2);
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_ring_write<16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_ring_write<8>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
+  if (a.n_groups <= 0) return hipSuccess;
+  const int64_t rows = (int64_t)a.T * a.H;
+  dim3 grid(blocks_for(rows * (a.D / 8)), 2 * a.n_groups);
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_compress<16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_compress<8>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
+  const int64_t TH = (int64_t)a.T * a.H;
+  const int64_t rows =
+      (a.hist_rows ? (int64_t)(a.hist.mem_len + a.hist.win_len) * TH : 0) + (int64_t)a.n_cur * TH;
+  if (rows <= 0) return hipSuccess;
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_rope<16>, dim3(blocks_for(rows * 16)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_rope<8>, dim3(blocks_for(rows * 8)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lact

@@ -1,0 +1,107 @@
+// kernels.hpp -- argument blocks and host launchers of the gfx950 kernels (shared by the
+// C ABI in lact_abi.cpp and the kernel sources).  No kernel code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "lact.h"
+
+namespace lact {
+
+enum : int32_t { DT_F32 = LACT_F32, DT_BF16 = LACT_BF16, DT_FP8 = LACT_FP8_E4M3 };
+
+constexpr int kMaxGroupsPerLaunch = 16;
+
+// Where history key frame fi (attention order) lives: memory rank j < mem_len is in memory
+// slot (mem_slot0 + j) mod M (group G - mem_len + j); window rank k is in raw slot
+// (ring_slot0 + k) mod R (frame E + k).  mem_slot0 = (G - mem_len) mod M, ring_slot0 = E mod R.
+struct HistMap {
+  int32_t mem_len, win_len, M, R, mem_slot0, ring_slot0;
+};
+
+// Append: frame F + i goes to raw slot (slot0 + i) mod R, slot0 = F mod R.
+struct RingWriteArgs {
+  const void* src[2];      // K, V: [n*T][H][D] in in_dtype
+  void* ring[2];           // raw ring bases [R][T][H][D]
+  float* ring_scale[2];    // FP8: [R][T][H]
+  int32_t slot0, n_frames, R, T, H, D;
+  int32_t in_dtype, kv_dtype;
+};
+
+// Compress: group g reads raw slots (r*g + k) mod R = (in_slot0 + k) mod R and writes
+// memory slot out_slot = g mod M.
+struct CompressArgs {
+  const void* ring[2];
+  const float* ring_scale[2];
+  void* mem[2];
+  float* mem_scale[2];
+  const float* w[2];       // [C][r]
+  const float* b[2];       // [C]
+  int32_t in_slot0[kMaxGroupsPerLaunch];
+  int32_t out_slot[kMaxGroupsPerLaunch];
+  int32_t n_groups, r, R, T, H, D;
+  int32_t kv_dtype;
+};
+
+// RoPE reset + apply: rebuild rotated history keys (if hist_rows) and stage the block.
+struct RopeArgs {
+  const void* q;
+  const void* k_cur;
+  const void* v_cur;       // [n*T][H][D] in in_dtype
+  const void* ring_k;
+  const void* mem_k;
+  const float* ring_k_scale;
+  const float* mem_k_scale;
+  void* krot;              // [H][KF*T][D] operand dtype
+  float* krot_scale;       // [H][KF*T]
+  void* qrot;              // [H][B_max*T][D]
+  float* qrot_scale;       // [H][B_max*T]
+  void* vcur;              // [B_max][T][H][D] kv dtype
+  float* vcur_scale;       // [B_max][T][H]
+  const float2* table;
+  HistMap hist;
+  int32_t hist_rows;       // 1: rebuild history keys
+  int32_t n_cur, T, H, D, grid_h, grid_w, key_frames_max, block_frames_max;
+  int32_t rope_mode, split_t, split_h, split_w;
+  int32_t in_dtype, kv_dtype;
+};
+
+struct RopeTableArgs {
+  float2* table;
+  int32_t rope_mode, split_t, split_h, split_w, D, T, grid_h, grid_w, key_frames_max;
+  double theta;
+  int64_t entries;
+};
+
+// Attention of the staged block over [memory | window | current].
+struct AttnArgs {
+  const void* q;           // qrot
+  const float* q_scale;
+  const void* k;           // krot
+  const float* k_scale;
+  const void* v_ring;
+  const void* v_mem;
+  const void* v_cur;
+  const float* v_ring_scale;
+  const float* v_mem_scale;
+  const float* v_cur_scale;
+  void* out;               // [Lq][H][D] q dtype
+  float* lse;              // [H][Lq] or null
+  int64_t q_head_stride, k_head_stride;  // elements (= rows * D) between heads
+  int64_t qs_head_stride, ks_head_stride;
+  HistMap hist;
+  int32_t T, H, D, Lq, Lk, Lhist;
+  int32_t n_blocks;
+  int32_t block_end[LACT_MAX_Q_BLOCKS];  // cumulative query-token ends of the blocks
+  float scale_log2;        // log2(e) / sqrt(D)
+};
+
+hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
+hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s);
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int32_t kv_dtype, hipStream_t s);
+
+}  // namespace lact

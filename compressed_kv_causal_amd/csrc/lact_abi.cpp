@@ -1,0 +1,477 @@
+// lact_abi.cpp -- the extern "C" boundary of liblact.so (declared in include/lact.h):
+// argument and state checks, the cache buffer layout, host bookkeeping, kernel launches.
+// Every check runs before anything is enqueued; a failed call leaves the state unchanged.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kernels.hpp"
+#include "lact.h"
+#include "plan.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lact_status fail(lact_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t elem_bytes(int32_t dt) { return dt == LACT_F32 ? 4 : (dt == LACT_BF16 ? 2 : 1); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+lact_status check_cfg(const lact_cfg* c) {
+  if (!c) return fail(LACT_E_INVALID, "cfg is NULL");
+  if (c->heads < 1 || c->grid_h < 1 || c->grid_w < 1)
+    return fail(LACT_E_SHAPE, "heads, grid_h and grid_w must be >= 1");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(LACT_E_SHAPE, "head_dim must be 64 or 128");
+  if (c->window_frames < 0 || c->mem_slots < 0)
+    return fail(LACT_E_SHAPE, "window_frames and mem_slots must be >= 0");
+  if (c->ratio < 1 || c->ratio > 16) return fail(LACT_E_SHAPE, "ratio must be in 1..16");
+  if (c->max_block_frames < 1) return fail(LACT_E_SHAPE, "max_block_frames must be >= 1");
+  const int64_t kf = (int64_t)c->mem_slots + c->window_frames + c->max_block_frames;
+  if (kf > LACT_MAX_KEY_FRAMES)
+    return fail(LACT_E_CAPACITY, "mem_slots + window_frames + max_block_frames exceeds " +
+                                     std::to_string(LACT_MAX_KEY_FRAMES));
+  const int64_t T = (int64_t)c->grid_h * c->grid_w;
+  if (T * c->heads * c->head_dim > (int64_t(1) << 28) || kf * T > (int64_t(1) << 24))
+    return fail(LACT_E_CAPACITY, "frame or key length too large");
+  const bool ok_dt = (c->q_dtype == LACT_F32 && c->kv_dtype == LACT_F32) ||
+                     (c->q_dtype == LACT_BF16 &&
+                      (c->kv_dtype == LACT_BF16 || c->kv_dtype == LACT_FP8_E4M3));
+  if (!ok_dt)
+    return fail(LACT_E_DTYPE, "supported (q, kv) dtypes: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3)");
+  if (c->rope_mode == 3) {
+    for (int i = 0; i < 3; ++i)
+      if (c->rope_split[i] < 2 || (c->rope_split[i] & 1))
+        return fail(LACT_E_SHAPE, "rope_split parts must be even and >= 2");
+    if (c->rope_split[0] + c->rope_split[1] + c->rope_split[2] != c->head_dim)
+      return fail(LACT_E_SHAPE, "rope_split must sum to head_dim");
+  } else if (c->rope_mode != 1) {
+    return fail(LACT_E_SHAPE, "rope_mode must be 1 or 3");
+  }
+  if (!(c->rope_theta > 1.0f) || !std::isfinite(c->rope_theta))
+    return fail(LACT_E_INVALID, "rope_theta must be finite and > 1");
+  return LACT_OK;
+}
+
+int64_t rope_table_entries(const lact_cfg& c) {
+  const int64_t kf = (int64_t)c.mem_slots + c.window_frames + c.max_block_frames;
+  const int64_t T = (int64_t)c.grid_h * c.grid_w;
+  if (c.rope_mode == 1) return kf * T * (c.head_dim / 2);
+  return kf * (c.rope_split[0] / 2) + (int64_t)c.grid_h * (c.rope_split[1] / 2) +
+         (int64_t)c.grid_w * (c.rope_split[2] / 2);
+}
+
+void compute_layout(const lact_cfg& c, lact_layout* L) {
+  std::memset(L, 0, sizeof(*L));
+  const int64_t T = (int64_t)c.grid_h * c.grid_w;
+  const int64_t fe = T * c.heads * c.head_dim;  // elements per frame
+  const size_t kvb = elem_bytes(c.kv_dtype);
+  const int32_t R = c.window_frames + c.max_block_frames + c.ratio - 1;
+  const int32_t KF = c.mem_slots + c.window_frames + c.max_block_frames;
+  const int32_t B = c.max_block_frames, M = c.mem_slots;
+  const bool fp8 = c.kv_dtype == LACT_FP8_E4M3;
+  const size_t fb = (size_t)fe * kvb;
+  const size_t sb = (size_t)T * c.heads * 4;  // one frame of f32 row scales
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->ring_k = take(fb * R);
+  L->ring_v = take(fb * R);
+  L->mem_k = take(fb * M);
+  L->mem_v = take(fb * M);
+  L->krot = take(fb * KF);
+  L->qrot = take(fb * B);
+  L->vcur = take(fb * B);
+  if (fp8) {
+    L->ring_k_scale = take(sb * R);
+    L->ring_v_scale = take(sb * R);
+    L->mem_k_scale = take(sb * M);
+    L->mem_v_scale = take(sb * M);
+    L->krot_scale = take(sb * KF);
+    L->qrot_scale = take(sb * B);
+    L->vcur_scale = take(sb * B);
+  }
+  L->rope_table = take(sizeof(float) * 2 * (size_t)rope_table_entries(c));
+  L->total = off;
+  L->frame_bytes = fb;
+  L->ring_slots = R;
+  L->key_frames_max = KF;
+}
+
+}  // namespace
+
+struct lact_cache {
+  lact_cfg cfg;
+  lact_layout lay;
+  lact::Planner plan;
+  char* buf;
+  bool table_ready = false;
+  bool staged = false;
+  uint64_t staged_version = 0;
+  int32_t staged_frames = 0;
+  bool hist_built = false;
+  uint64_t hist_version = 0;
+  lact_cache(const lact_cfg& c, const lact_layout& l, void* b)
+      : cfg(c), lay(l), plan(c), buf(static_cast<char*>(b)) {}
+
+  int32_t T() const { return cfg.grid_h * cfg.grid_w; }
+  void* at(size_t off) const { return buf + off; }
+  float* fat(size_t off) const {
+    return cfg.kv_dtype == LACT_FP8_E4M3 ? reinterpret_cast<float*>(buf + off) : nullptr;
+  }
+  lact::HistMap hist() const {
+    lact::HistMap m;
+    m.mem_len = plan.mem_len();
+    m.win_len = plan.win_len();
+    m.M = cfg.mem_slots;
+    m.R = plan.ring_slots();
+    m.mem_slot0 = cfg.mem_slots > 0 ? (int32_t)(plan.first_mem_group() % cfg.mem_slots) : 0;
+    m.ring_slot0 = (int32_t)(plan.evicted() % plan.ring_slots());
+    return m;
+  }
+};
+
+struct lact_plan {
+  lact::Planner p;
+  explicit lact_plan(const lact_cfg& c) : p(c) {}
+};
+
+static lact_status hip_fail(hipError_t e, const char* what) {
+  return fail(LACT_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+extern "C" {
+
+const char* lact_last_error(void) { return g_last_error.c_str(); }
+
+lact_status lact_cache_footprint(const lact_cfg* cfg, size_t* device_bytes) {
+  lact_status st = check_cfg(cfg);
+  if (st != LACT_OK) return st;
+  if (!device_bytes) return fail(LACT_E_INVALID, "device_bytes is NULL");
+  lact_layout L;
+  compute_layout(*cfg, &L);
+  *device_bytes = L.total;
+  return LACT_OK;
+}
+
+lact_status lact_cache_layout(const lact_cfg* cfg, lact_layout* out) {
+  lact_status st = check_cfg(cfg);
+  if (st != LACT_OK) return st;
+  if (!out) return fail(LACT_E_INVALID, "out is NULL");
+  compute_layout(*cfg, out);
+  return LACT_OK;
+}
+
+lact_status lact_cache_init(const lact_cfg* cfg, void* device_buf, size_t bytes, lact_cache** out) {
+  lact_status st = check_cfg(cfg);
+  if (st != LACT_OK) return st;
+  if (!out) return fail(LACT_E_INVALID, "out is NULL");
+  if (!device_buf || !aligned(device_buf, 256))
+    return fail(LACT_E_INVALID, "device_buf must be non-NULL and 256-byte aligned");
+  lact_layout L;
+  compute_layout(*cfg, &L);
+  if (bytes < L.total)
+    return fail(LACT_E_CAPACITY, "device buffer of " + std::to_string(bytes) + " bytes; need " +
+                                     std::to_string(L.total));
+  lact_cache* c = new (std::nothrow) lact_cache(*cfg, L, device_buf);
+  if (!c) return fail(LACT_E_CAPACITY, "host allocation of the handle failed");
+  *out = c;
+  return LACT_OK;
+}
+
+lact_status lact_cache_destroy(lact_cache* cache) {
+  delete cache;
+  return LACT_OK;
+}
+
+lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cur, const void* v_cur,
+                                  int32_t n_frames, void* stream) {
+  if (!c) return fail(LACT_E_INVALID, "cache is NULL");
+  if (!q || !k_cur || !v_cur || !aligned(q, 16) || !aligned(k_cur, 16) || !aligned(v_cur, 16))
+    return fail(LACT_E_INVALID, "q, k_cur, v_cur must be non-NULL and 16-byte aligned");
+  if (n_frames < 1 || n_frames > c->cfg.max_block_frames)
+    return fail(LACT_E_CAPACITY, "n_frames " + std::to_string(n_frames) + " outside 1.." +
+                                     std::to_string(c->cfg.max_block_frames));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lact_cfg& g = c->cfg;
+  if (!c->table_ready) {
+    lact::RopeTableArgs t;
+    t.table = static_cast<float2*>(c->at(c->lay.rope_table));
+    t.rope_mode = g.rope_mode;
+    t.split_t = g.rope_split[0];
+    t.split_h = g.rope_split[1];
+    t.split_w = g.rope_split[2];
+    t.D = g.head_dim;
+    t.T = c->T();
+    t.grid_h = g.grid_h;
+    t.grid_w = g.grid_w;
+    t.key_frames_max = c->lay.key_frames_max;
+    t.theta = (double)g.rope_theta;
+    t.entries = rope_table_entries(g);
+    hipError_t e = lact::launch_rope_table(t, s);
+    if (e != hipSuccess) return hip_fail(e, "rope table launch");
+    c->table_ready = true;
+  }
+  lact::RopeArgs a;
+  a.q = q;
+  a.k_cur = k_cur;
+  a.v_cur = v_cur;
+  a.ring_k = c->at(c->lay.ring_k);
+  a.mem_k = c->at(c->lay.mem_k);
+  a.ring_k_scale = c->fat(c->lay.ring_k_scale);
+  a.mem_k_scale = c->fat(c->lay.mem_k_scale);
+  a.krot = c->at(c->lay.krot);
+  a.krot_scale = c->fat(c->lay.krot_scale);
+  a.qrot = c->at(c->lay.qrot);
+  a.qrot_scale = c->fat(c->lay.qrot_scale);
+  a.vcur = c->at(c->lay.vcur);
+  a.vcur_scale = c->fat(c->lay.vcur_scale);
+  a.table = static_cast<const float2*>(c->at(c->lay.rope_table));
+  a.hist = c->hist();
+  const bool rebuild = !(c->hist_built && c->hist_version == c->plan.version());
+  a.hist_rows = rebuild ? 1 : 0;
+  a.n_cur = n_frames;
+  a.T = c->T();
+  a.H = g.heads;
+  a.D = g.head_dim;
+  a.grid_h = g.grid_h;
+  a.grid_w = g.grid_w;
+  a.key_frames_max = c->lay.key_frames_max;
+  a.block_frames_max = g.max_block_frames;
+  a.rope_mode = g.rope_mode;
+  a.split_t = g.rope_split[0];
+  a.split_h = g.rope_split[1];
+  a.split_w = g.rope_split[2];
+  a.in_dtype = g.q_dtype;
+  a.kv_dtype = g.kv_dtype;
+  hipError_t e = lact::launch_rope(a, s);
+  if (e != hipSuccess) return hip_fail(e, "rope launch");
+  c->hist_built = true;
+  c->hist_version = c->plan.version();
+  c->staged = true;
+  c->staged_version = c->plan.version();
+  c->staged_frames = n_frames;
+  return LACT_OK;
+}
+
+lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, int32_t n_q_blocks,
+                                 void* out, float* lse, void* stream) {
+  if (!c) return fail(LACT_E_INVALID, "cache is NULL");
+  if (!out || !aligned(out, 16)) return fail(LACT_E_INVALID, "out must be non-NULL and 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(LACT_E_INVALID, "lse must be 4-byte aligned");
+  if (!c->staged || c->staged_version != c->plan.version())
+    return fail(LACT_E_STATE, "lact_rope_reset_apply has not run at the present state");
+  const lact_cfg& g = c->cfg;
+  const int32_t T = c->T();
+  lact::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  if (q_block_frames == nullptr) {
+    a.n_blocks = 1;
+    a.block_end[0] = c->staged_frames * T;
+  } else {
+    if (n_q_blocks < 1 || n_q_blocks > LACT_MAX_Q_BLOCKS)
+      return fail(LACT_E_CAPACITY, "n_q_blocks outside 1.." + std::to_string(LACT_MAX_Q_BLOCKS));
+    int32_t sum = 0;
+    for (int32_t b = 0; b < n_q_blocks; ++b) {
+      if (q_block_frames[b] < 1) return fail(LACT_E_SHAPE, "every query block needs >= 1 frame");
+      sum += q_block_frames[b];
+      a.block_end[b] = sum * T;
+    }
+    if (sum != c->staged_frames)
+      return fail(LACT_E_SHAPE, "q_block_frames sum to " + std::to_string(sum) + ", staged " +
+                                    std::to_string(c->staged_frames));
+    a.n_blocks = n_q_blocks;
+  }
+  a.q = c->at(c->lay.qrot);
+  a.q_scale = c->fat(c->lay.qrot_scale);
+  a.k = c->at(c->lay.krot);
+  a.k_scale = c->fat(c->lay.krot_scale);
+  a.v_ring = c->at(c->lay.ring_v);
+  a.v_mem = c->at(c->lay.mem_v);
+  a.v_cur = c->at(c->lay.vcur);
+  a.v_ring_scale = c->fat(c->lay.ring_v_scale);
+  a.v_mem_scale = c->fat(c->lay.mem_v_scale);
+  a.v_cur_scale = c->fat(c->lay.vcur_scale);
+  a.out = out;
+  a.lse = lse;
+  a.q_head_stride = (int64_t)g.max_block_frames * T * g.head_dim;
+  a.k_head_stride = (int64_t)c->lay.key_frames_max * T * g.head_dim;
+  a.qs_head_stride = (int64_t)g.max_block_frames * T;
+  a.ks_head_stride = (int64_t)c->lay.key_frames_max * T;
+  a.hist = c->hist();
+  a.T = T;
+  a.H = g.heads;
+  a.D = g.head_dim;
+  a.Lq = c->staged_frames * T;
+  a.Lhist = c->plan.history_frames() * T;
+  a.Lk = a.Lhist + a.Lq;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
+  hipError_t e = lact::launch_attention(a, g.kv_dtype, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(LACT_E_DTYPE, "attention for this kv dtype is not built");
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return LACT_OK;
+}
+
+lact_status lact_kv_ring_append(lact_cache* c, const void* k_new, const void* v_new, int32_t n_frames,
+                                void* stream) {
+  if (!c) return fail(LACT_E_INVALID, "cache is NULL");
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(LACT_E_INVALID, "k_new and v_new must be non-NULL and 16-byte aligned");
+  std::string why = c->plan.check_append(n_frames);
+  if (!why.empty())
+    return fail(n_frames < 1 || n_frames > c->plan.max_block() ? LACT_E_CAPACITY : LACT_E_STATE, why);
+  const lact_cfg& g = c->cfg;
+  lact::RingWriteArgs a;
+  a.src[0] = k_new;
+  a.src[1] = v_new;
+  a.ring[0] = c->at(c->lay.ring_k);
+  a.ring[1] = c->at(c->lay.ring_v);
+  a.ring_scale[0] = c->fat(c->lay.ring_k_scale);
+  a.ring_scale[1] = c->fat(c->lay.ring_v_scale);
+  a.slot0 = c->plan.raw_slot(c->plan.frames_appended());
+  a.n_frames = n_frames;
+  a.R = c->plan.ring_slots();
+  a.T = c->T();
+  a.H = g.heads;
+  a.D = g.head_dim;
+  a.in_dtype = g.q_dtype;
+  a.kv_dtype = g.kv_dtype;
+  hipError_t e = lact::launch_ring_write(a, (int64_t)n_frames * a.T * a.H, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  c->plan.append(n_frames);
+  return LACT_OK;
+}
+
+lact_status lact_convkv_compress(lact_cache* c, const float* w_k, const float* b_k, const float* w_v,
+                                 const float* b_v, void* stream, int32_t* slots_written) {
+  if (!c) return fail(LACT_E_INVALID, "cache is NULL");
+  if (!w_k || !b_k || !w_v || !b_v || !aligned(w_k, 16) || !aligned(b_k, 16) || !aligned(w_v, 16) ||
+      !aligned(b_v, 16))
+    return fail(LACT_E_INVALID, "weights and biases must be non-NULL and 16-byte aligned");
+  const lact_cfg& g = c->cfg;
+  const int32_t ready = c->plan.ready_groups();
+  const int32_t M = g.mem_slots;
+  const int32_t written = ready < M ? ready : M;
+  const int64_t G = c->plan.groups_compressed();
+  const int64_t first = G + ready - written;  // earlier groups would be overwritten at once
+  lact::CompressArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.ring[0] = c->at(c->lay.ring_k);
+  a.ring[1] = c->at(c->lay.ring_v);
+  a.ring_scale[0] = c->fat(c->lay.ring_k_scale);
+  a.ring_scale[1] = c->fat(c->lay.ring_v_scale);
+  a.mem[0] = c->at(c->lay.mem_k);
+  a.mem[1] = c->at(c->lay.mem_v);
+  a.mem_scale[0] = c->fat(c->lay.mem_k_scale);
+  a.mem_scale[1] = c->fat(c->lay.mem_v_scale);
+  a.w[0] = w_k;
+  a.w[1] = w_v;
+  a.b[0] = b_k;
+  a.b[1] = b_v;
+  a.r = g.ratio;
+  a.R = c->plan.ring_slots();
+  a.T = c->T();
+  a.H = g.heads;
+  a.D = g.head_dim;
+  a.kv_dtype = g.kv_dtype;
+  for (int32_t done = 0; done < written;) {
+    const int32_t n = written - done < lact::kMaxGroupsPerLaunch ? written - done : lact::kMaxGroupsPerLaunch;
+    for (int32_t i = 0; i < n; ++i) {
+      const int64_t grp = first + done + i;
+      a.in_slot0[i] = (int32_t)((grp * g.ratio) % a.R);
+      a.out_slot[i] = (int32_t)(grp % M);
+    }
+    a.n_groups = n;
+    hipError_t e = lact::launch_compress(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "compress launch");
+    done += n;
+  }
+  c->plan.consume_groups(ready);
+  if (slots_written) *slots_written = written;
+  return LACT_OK;
+}
+
+lact_status lact_cache_state(const lact_cache* c, lact_state* out) {
+  if (!c || !out) return fail(LACT_E_INVALID, "cache and out must be non-NULL");
+  c->plan.state(out);
+  out->staged_frames = c->staged ? c->staged_frames : 0;
+  out->staged_valid = (c->staged && c->staged_version == c->plan.version()) ? 1 : 0;
+  return LACT_OK;
+}
+
+lact_status lact_cache_keys(const lact_cache* c, int32_t n_cur, lact_key_frame* out, int32_t cap,
+                            int32_t* n_out) {
+  if (!c || !n_out) return fail(LACT_E_INVALID, "cache and n_out must be non-NULL");
+  if (n_cur < 0 || n_cur > c->cfg.max_block_frames) return fail(LACT_E_CAPACITY, "n_cur out of range");
+  if (cap < 0 || (cap > 0 && !out)) return fail(LACT_E_INVALID, "bad out/cap");
+  *n_out = c->plan.key_frames(n_cur, out, cap);
+  return LACT_OK;
+}
+
+lact_status lact_plan_create(const lact_cfg* cfg, lact_plan** out) {
+  lact_status st = check_cfg(cfg);
+  if (st != LACT_OK) return st;
+  if (!out) return fail(LACT_E_INVALID, "out is NULL");
+  lact_plan* p = new (std::nothrow) lact_plan(*cfg);
+  if (!p) return fail(LACT_E_CAPACITY, "host allocation failed");
+  *out = p;
+  return LACT_OK;
+}
+
+lact_status lact_plan_destroy(lact_plan* p) {
+  delete p;
+  return LACT_OK;
+}
+
+lact_status lact_plan_append(lact_plan* p, int32_t n_frames) {
+  if (!p) return fail(LACT_E_INVALID, "plan is NULL");
+  std::string why = p->p.check_append(n_frames);
+  if (!why.empty())
+    return fail(n_frames < 1 || n_frames > p->p.max_block() ? LACT_E_CAPACITY : LACT_E_STATE, why);
+  p->p.append(n_frames);
+  return LACT_OK;
+}
+
+lact_status lact_plan_compress(lact_plan* p, int64_t* groups, int32_t cap, int32_t* n_groups,
+                               int32_t* n_written) {
+  if (!p || !n_groups) return fail(LACT_E_INVALID, "plan and n_groups must be non-NULL");
+  if (cap < 0 || (cap > 0 && !groups)) return fail(LACT_E_INVALID, "bad groups/cap");
+  const int32_t ready = p->p.ready_groups();
+  const int64_t G = p->p.groups_compressed();
+  for (int32_t i = 0; i < ready && i < cap; ++i) groups[i] = G + i;
+  *n_groups = ready;
+  if (n_written) *n_written = ready < p->p.mem_slots() ? ready : p->p.mem_slots();
+  p->p.consume_groups(ready);
+  return LACT_OK;
+}
+
+lact_status lact_plan_state(const lact_plan* p, lact_state* out) {
+  if (!p || !out) return fail(LACT_E_INVALID, "plan and out must be non-NULL");
+  p->p.state(out);
+  return LACT_OK;
+}
+
+lact_status lact_plan_keys(const lact_plan* p, int32_t n_cur, lact_key_frame* out, int32_t cap,
+                           int32_t* n_out) {
+  if (!p || !n_out) return fail(LACT_E_INVALID, "plan and n_out must be non-NULL");
+  if (n_cur < 0) return fail(LACT_E_CAPACITY, "n_cur out of range");
+  if (cap < 0 || (cap > 0 && !out)) return fail(LACT_E_INVALID, "bad out/cap");
+  *n_out = p->p.key_frames(n_cur, out, cap);
+  return LACT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+"""Drives one cache through AR steps on the GPU (via the C ABI) and the oracle side by
+side, on the same seeded inputs.  Test infrastructure."""
+import numpy as np
+import torch
+
+import compressed_kv_causal_amd as L
+import synth
+from oracle.stream import OracleCache
+
+F32, BF16, FP8 = 0, 1, 2
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def io_dtype(w):
+    return torch.float32 if w["q_dtype"] == F32 else torch.bfloat16
+
+
+class Runner:
+    def __init__(self, w, seed=0, with_oracle=True, kernel=None):
+        self.w = w
+        self.seed = seed
+        self.T, self.H, self.D = w["tokens"], w["heads"], w["head_dim"]
+        self.cfg = L.make_cfg(**w)
+        self.cache = L.Cache(self.cfg)
+        self.oc = OracleCache(w) if with_oracle else None
+        if kernel is None:
+            self.wk, self.bk = synth.conv_weights(w, seed, synth.TENSOR_WK)
+            self.wv, self.bv = synth.conv_weights(w, seed, synth.TENSOR_WV)
+        else:
+            self.wk, self.bk, self.wv, self.bv = kernel
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.d_wk, self.d_bk, self.d_wv, self.d_bv = map(dev, (self.wk, self.bk, self.wv, self.bv))
+        self.f = 0
+        self.step_index = 0
+
+    def inputs(self, n, tag=False):
+        """(device tensor, host float32 values) for Q, K, V of frames f .. f+n-1."""
+        ids = list(range(self.f, self.f + n))
+        out = []
+        for tensor in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V):
+            x = synth.frames(self.w, self.seed, tensor, ids)
+            if tag and tensor == synth.TENSOR_K:
+                x[:, 0] = np.asarray(ids, np.float32)
+            t = torch.from_numpy(x.reshape(n * self.T, self.H, self.D)).to(io_dtype(self.w))
+            out.append((t.cuda(), t.float().numpy()))
+        return out
+
+    def step(self, n, attend=True, blocks=None, sel=None, lse=True, tag=False, form=1):
+        """One AR step: rope -> attention -> append -> compress, on the GPU and the oracle.
+        Returns dict(out, lse, ref) where ref = (O, LSE, heads, rows) of the oracle or None."""
+        (q, qh), (k, kh), (v, vh) = self.inputs(n, tag)
+        res = {}
+        if attend:
+            self.cache.rope_reset_apply(q, k, v)
+            Lq = n * self.T
+            lse_t = torch.empty((self.H, Lq), dtype=torch.float32, device="cuda") if lse else None
+            out = self.cache.block_attention(blocks, lse=lse_t)
+            res["out"], res["lse"] = out, lse_t
+            if self.oc is not None and sel is not False:
+                res["ref"] = self.oc.attention(qh, kh, vh, block_frames=blocks, sel=sel, form=form)
+            res["q"], res["k"], res["v"] = qh, kh, vh
+        self.cache.kv_ring_append(k, v)
+        res["slots"] = self.cache.convkv_compress(self.d_wk, self.d_bk, self.d_wv, self.d_bv)
+        if self.oc is not None:
+            self.oc.append(kh.reshape(n, -1), vh.reshape(n, -1))
+            res["groups"] = self.oc.compress(self.wk, self.bk, self.wv, self.bv)
+        self.f += n
+        self.step_index += 1
+        return res
+
+    # ---- comparisons -------------------------------------------------------------------
+    def compare_attention(self, res):
+        """(rel L2 of O over the oracle's selected rows, max |dLSE|)."""
+        O, LSE, heads, rows = res["ref"]
+        out = res["out"].float().cpu().numpy()           # [Lq][H][D]
+        got = out[rows, heads, :]
+        err = rel_l2(got, O)
+        dl = 0.0
+        if res.get("lse") is not None:
+            lse = res["lse"].cpu().numpy()
+            dl = float(np.abs(lse[heads, rows] - LSE).max())
+        return err, dl
+
+    def mem_slot_bytes(self, tensor, slot):
+        """Raw bytes of memory slot `slot` of K (0) or V (1) as stored on the device."""
+        lay = self.cache.layout
+        fb = lay.frame_bytes
+        off = (lay.mem_k if tensor == 0 else lay.mem_v) + slot * fb
+        return self.cache.buf[off: off + fb].cpu().numpy()
+
+    def ring_slot_bytes(self, tensor, slot):
+        lay = self.cache.layout
+        fb = lay.frame_bytes
+        off = (lay.ring_k if tensor == 0 else lay.ring_v) + slot * fb
+        return self.cache.buf[off: off + fb].cpu().numpy()
+
+    def scale_slot(self, name, slot):
+        lay = self.cache.layout
+        n = self.T * self.H
+        off = getattr(lay, name) + slot * n * 4
+        return self.cache.buf[off: off + n * 4].cpu().numpy().view(np.float32)
+
+    def oracle_stored_bytes(self, stored):
+        """Oracle stored representation -> (value bytes, scales or None) as the device keeps it."""
+        if stored[0] == "fp8":
+            return stored[1].view(np.uint8), stored[2]
+        if self.w["kv_dtype"] == BF16:
+            from oracle import bf16_encode
+            return bf16_encode(stored[1]).view(np.uint8), None
+        return stored[1].view(np.uint8), None
+
+
+def sample_rows(w, n_frames, seed, per_head=16, heads=None):
+    """Seeded query rows per head, always with the first and last row of every block and
+    the rows around every 128-row tile edge's tail."""
+    T = w["tokens"]
+    Lq = n_frames * T
+    base = {0, Lq - 1}
+    for f in range(n_frames):
+        base.add(f * T)
+        base.add(f * T + T - 1)
+    tail = (Lq // 128) * 128
+    base.update(r for r in (tail, tail + 1, Lq - 2) if 0 <= r < Lq)
+    u = synth.uniform(seed, synth.TENSOR_SAMPLE, 0, per_head)
+    extra = {int(x * Lq) % Lq for x in u}
+    rows = sorted(base | extra)
+    H = w["heads"]
+    hs = range(H) if heads is None else heads
+    hh = np.repeat(np.asarray(list(hs), np.int32), len(rows))
+    rr = np.tile(np.asarray(rows, np.int64), len(list(hs)))
+    return hh, rr

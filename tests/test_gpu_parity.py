@@ -1,0 +1,180 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs.  Bars: bookkeeping and indices bit-exact; compressed memory and ring
+contents bit-exact (they are f32 fma chains and RNE/e4m3 encodes on both sides);
+attention relative L2 <= 1e-5 (f32), 1e-2 (bf16), 5e-2 (FP8 KV)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from stream_helpers import BF16, F32, FP8, Runner, rel_l2, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = {F32: 1e-5, BF16: 1e-2, FP8: 5e-2}
+LSE_TOL = {F32: 1e-5, BF16: 2e-2, FP8: 1e-1}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def assert_state_matches(run):
+    st = run.cache.state()
+    ob = run.oc.bk.state()
+    for key in ("F", "E", "G", "pending", "mem_len", "win_len", "ring_slots"):
+        assert st[key] == ob[key], (key, st, ob)
+
+
+def assert_keys_match(run, n):
+    got = run.cache.keys(n)
+    want = run.oc.keys(n)
+    assert len(got) == len(want)
+    for g, k in zip(got, want):
+        assert (g["segment"], g["slot"], g["id"], g["t_pos"]) == \
+            (k["segment"], k["slot"], k["id"], k["t_pos"])
+
+
+def assert_memory_bitexact(run, slots=None):
+    M = run.w["mem_slots"]
+    for slot, (g, sk, sv) in sorted(run.oc.mem.items()):
+        if slots is not None and slot not in slots:
+            continue
+        for tensor, stored in ((0, sk), (1, sv)):
+            want, scales = run.oracle_stored_bytes(stored)
+            got = run.mem_slot_bytes(tensor, slot)
+            assert np.array_equal(got, want), f"memory slot {slot} (group {g}) tensor {tensor}"
+            if scales is not None:
+                name = "mem_k_scale" if tensor == 0 else "mem_v_scale"
+                assert np.array_equal(run.scale_slot(name, slot), scales), f"scales of slot {slot}"
+    assert len(run.oc.mem) == min(run.oc.bk.G, M)
+
+
+def assert_ring_bitexact(run):
+    for f, (sk, sv) in run.oc.raw.items():
+        slot = run.oc.bk.raw_slot(f)
+        for tensor, stored in ((0, sk), (1, sv)):
+            want, scales = run.oracle_stored_bytes(stored)
+            assert np.array_equal(run.ring_slot_bytes(tensor, slot), want), f"frame {f}"
+            if scales is not None:
+                name = "ring_k_scale" if tensor == 0 else "ring_v_scale"
+                assert np.array_equal(run.scale_slot(name, slot), scales), f"scales frame {f}"
+
+
+# ------------------------------------------------------------------------------------------
+def test_tiny_f32_stream_full_parity():
+    """Tiny f32: 27 history blocks then 20 AR steps, every step attended and compared on
+    every output row, bookkeeping and key table compared every step."""
+    w = synth.workload("tiny_f32")
+    run = Runner(w)
+    worst = 0.0
+    for s in range(w["history_blocks"] + w["steps"]):
+        assert_keys_match(run, 2)
+        res = run.step(2)
+        err, dl = run.compare_attention(res)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[F32] and dl <= LSE_TOL[F32], (s, err, dl)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    say(f"tiny f32: worst rel L2 {worst:.2e} over 47 steps")
+
+
+@pytest.mark.parametrize("blocks", [[1, 2, 3], [2, 2, 2], [3, 3], [6]])
+def test_tiny_multiblock_mask_vs_bruteforce(blocks):
+    """Several query blocks in one call: the GPU's block-causal prefix against the oracle's
+    explicit 0/-inf mask matrix (form 0), with memory and window present."""
+    w = synth.workload("tiny_f32", max_block_frames=6)
+    run = Runner(w)
+    for _ in range(14):
+        run.step(2, attend=False)
+    res = run.step(6, blocks=blocks, form=0)
+    err, dl = run.compare_attention(res)
+    assert err <= ATTN_TOL[F32] and dl <= LSE_TOL[F32], (blocks, err, dl)
+
+
+def test_tiny_window_only_and_no_memory():
+    """M = 0 (window only): groups are consumed and dropped; attention over window + block."""
+    w = synth.workload("tiny_f32", mem_slots=0)
+    run = Runner(w)
+    for s in range(12):
+        res = run.step(2)
+        err, dl = run.compare_attention(res)
+        assert err <= ATTN_TOL[F32], (s, err)
+        assert res["slots"] == 0
+        assert_state_matches(run)
+
+
+@pytest.mark.parametrize("tap", [None, 0, 3])
+def test_frame_id_tag_on_device(tap):
+    """No oracle: K element 0 of every frame holds the frame's absolute id.  With the
+    uniform 1/5 kernel memory slot g holds 5g + 2 (5-frame mean); with a delta at tap k it
+    holds exactly 5g + k."""
+    w = synth.workload("tiny_f32")
+    C = w["channels"]
+    wt = np.zeros((C, 5), np.float32)
+    if tap is None:
+        wt[:] = np.float32(0.2)
+    else:
+        wt[:, tap] = 1.0
+    b = np.zeros(C, np.float32)
+    run = Runner(w, with_oracle=False, kernel=(wt, b, wt, b))
+    for _ in range(40):
+        run.step(2, attend=False, tag=True)
+    st = run.cache.state()
+    for g in range(st["G"] - st["mem_len"], st["G"]):
+        val = run.mem_slot_bytes(0, g % w["mem_slots"]).view(np.float32)[0]
+        if tap is None:
+            assert abs(val - (5 * g + 2)) <= 1e-5 * (5 * g + 2), (g, val)
+        else:
+            assert val == 5 * g + tap, (g, val)
+
+
+def _big_step_parity(name, warm, n_last, per_head=6, first_check=False):
+    w = synth.workload(name)
+    run = Runner(w)
+    kv = w["kv_dtype"]
+    sizes = synth.block_sizes(w, warm + 1)
+    errs = []
+    for s, n in enumerate(sizes[:-1]):
+        if first_check and s == 0:
+            sel = sample_rows(w, n, seed=s, per_head=per_head)
+            res = run.step(n, sel=sel)
+            err, dl = run.compare_attention(res)
+            say(f"{name} step 1 ({n} frames, no history): rel L2 {err:.3e}, max dLSE {dl:.2e}")
+            assert err <= ATTN_TOL[kv] and dl <= LSE_TOL[kv]
+            errs.append(err)
+        else:
+            run.step(n, attend=False)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    assert_keys_match(run, n_last)
+    sel = sample_rows(w, n_last, seed=99, per_head=per_head)
+    res = run.step(n_last, sel=sel)
+    err, dl = run.compare_attention(res)
+    say(f"{name} step {warm + 1}: Lq {n_last * w['tokens']}, rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert err <= ATTN_TOL[kv] and dl <= LSE_TOL[kv]
+    return run
+
+
+def test_s512_bf16_step_parity():
+    """512x512-shaped bf16: 11 warm-up blocks (80 evicted -> 16 slots, bit-exact), then a
+    full step (Lq 8192, Lk 32768) compared on sampled rows of all 40 heads."""
+    _big_step_parity("s512_bf16", 11, 8)
+
+
+def test_s720_bf16_step_parity():
+    """720x416-shaped bf16: T = 1170 (non-power-of-two tails), first block 6 frames then 8."""
+    _big_step_parity("s720_bf16", 11, 8, first_check=True)
+
+
+def test_fp8_append_compress_bitexact():
+    """FP8 KV: ring codes and scales and the re-quantised memory slots bit-exact."""
+    w = synth.workload("fp8_kv")
+    run = Runner(w)
+    for n in synth.block_sizes(w, 12):
+        run.step(n, attend=False)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
