@@ -89,6 +89,7 @@ struct AttnArgs {
   const float* v_cur_scale;
   void* out;               // [Lq][H][D] q dtype
   float* lse;              // [H][Lq] or null
+  int32_t* flags;          // per (head, 256-row query tile): 1 = redo with the exact pass
   int64_t q_head_stride, k_head_stride;  // elements (= rows * D) between heads
   int64_t qs_head_stride, ks_head_stride;
   HistMap hist;

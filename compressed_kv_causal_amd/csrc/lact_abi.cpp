@@ -106,6 +106,7 @@ void compute_layout(const lact_cfg& c, lact_layout* L) {
     L->vcur_scale = take(sb * B);
   }
   L->rope_table = take(sizeof(float) * 2 * (size_t)rope_table_entries(c));
+  L->attn_flags = take(sizeof(int32_t) * (size_t)c.heads * (size_t)((B * T + 255) / 256));
   L->total = off;
   L->frame_bytes = fb;
   L->ring_slots = R;
@@ -308,6 +309,7 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
   a.v_cur_scale = c->fat(c->lay.vcur_scale);
   a.out = out;
   a.lse = lse;
+  a.flags = reinterpret_cast<int32_t*>(c->at(c->lay.attn_flags));
   a.q_head_stride = (int64_t)g.max_block_frames * T * g.head_dim;
   a.k_head_stride = (int64_t)c->lay.key_frames_max * T * g.head_dim;
   a.qs_head_stride = (int64_t)g.max_block_frames * T;

@@ -104,16 +104,18 @@ typedef struct {
  *   ring_k/ring_v  [R][T][H][D] kv dtype            raw ring (pre-RoPE K, V)
  *   mem_k/mem_v    [M][T][H][D] kv dtype            compressed memory slots
  *   krot           [H][(M+W+B_max)*T][D] operand    rotated keys in attention order
- *   qrot           [H][B_max*T][D] operand          rotated, pre-scaled-free queries
+ *   qrot           [H][B_max*T][D] operand          rotated queries of the block
  *   vcur           [B_max][T][H][D] kv dtype        current V staged for attention
  *   *_scale        f32 per (token, head): ring/mem/vcur [slots][T][H]; krot/qrot [H][L]
  *   rope_table     float2 (cos, sin) table
+ *   attn_flags     int32 per (head, 256-row query tile): attention work queue of the exact
+ *                  fallback pass (rows whose fast pass could not be trusted)
  * operand dtype = F32 / BF16 / FP8_E4M3 codes as kv_dtype. */
 typedef struct {
   size_t total;
   size_t ring_k, ring_v, mem_k, mem_v, krot, qrot, vcur;
   size_t ring_k_scale, ring_v_scale, mem_k_scale, mem_v_scale, krot_scale, qrot_scale, vcur_scale;
-  size_t rope_table;
+  size_t rope_table, attn_flags;
   size_t frame_bytes;    /* T*H*D * kv element size                                       */
   int32_t ring_slots, key_frames_max;
 } lact_layout;

@@ -178,3 +178,47 @@ def test_fp8_append_compress_bitexact():
         assert_state_matches(run)
     assert_memory_bitexact(run)
     assert_ring_bitexact(run)
+
+
+@pytest.mark.parametrize("blocks", [[1, 2, 3], [3, 3], [6], [2, 1, 1, 2]])
+def test_bf16_d128_multiblock_mask_vs_bruteforce(blocks):
+    """D = 128 bf16 kernel with several query blocks per call and T = 96 (tiles of 32 keys
+    and 256 query rows straddle frames and blocks): against the explicit mask matrix."""
+    w = synth.workload("s512_bf16", heads=4, grid_h=8, grid_w=12, window_frames=4,
+                       mem_slots=6, max_block_frames=6)
+    run = Runner(w)
+    for _ in range(9):
+        run.step(2, attend=False)
+    res = run.step(6, blocks=blocks, form=0)
+    err, dl = run.compare_attention(res)
+    say(f"bf16 d128 blocks {blocks}: rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16], (blocks, err, dl)
+
+
+def test_bf16_d128_overflow_falls_back_to_exact_pass():
+    """A late key whose score exceeds the first-tile reference by far more than the f32
+    range (one current-frame key scaled x2000): the fast pass flags its tiles and the exact
+    online-softmax pass redoes them; the result still matches the oracle."""
+    w = synth.workload("s512_bf16", heads=2, grid_h=8, grid_w=8, window_frames=4,
+                       mem_slots=4, max_block_frames=4)
+    run = Runner(w)
+    for _ in range(6):
+        run.step(2, attend=False)
+    (q, qh), (k, kh), (v, vh) = run.inputs(4)
+    T = w["tokens"]
+    last = 4 * T - 1
+    qh[:, :, :] = np.abs(qh)                      # every query has positive channels
+    kh[last, :, :] = 2000.0                       # the very last key aligns with all of them
+    q = torch.from_numpy(qh).to(torch.bfloat16).cuda()
+    k = torch.from_numpy(kh).to(torch.bfloat16).cuda()
+    qh, kh = q.float().cpu().numpy(), k.float().cpu().numpy()
+    run.cache.rope_reset_apply(q, k, v)
+    lse = torch.empty((w["heads"], 4 * T), dtype=torch.float32, device="cuda")
+    out = run.cache.block_attention(lse=lse)
+    flags = run.cache.buf[run.cache.layout.attn_flags:].view(torch.int32)[: w["heads"]].cpu().numpy()
+    assert flags.max() == 1, "the fast pass should have flagged its tile"
+    ref = run.oc.attention(qh, kh, vh)
+    res = dict(out=out, lse=lse, ref=ref)
+    err, dl = run.compare_attention(res)
+    say(f"overflow fallback: flags {flags.tolist()}, rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16]
