@@ -40,7 +40,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--pool-blocks", type=int, default=7)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=12, help="oracle rows per head in the sample")
+    p.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per head in the sample")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="run one device copy of MIB MiB first (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -97,6 +99,13 @@ def main():
     wk, bk = synth.conv_weights(w, args.seed, synth.TENSOR_WK)
     wv, bv = synth.conv_weights(w, args.seed, synth.TENSOR_WV)
     d_wk, d_bk, d_wv, d_bv = (torch.from_numpy(a).to(dev) for a in (wk, bk, wv, bv))
+
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cache = L.Cache(L.make_cfg(**w), device=dev)
     Lq = B * T

@@ -7,10 +7,13 @@
 // query row i sees exactly the key prefix [0, Lhist + block_end[block(i)]).
 //
 // Kernels:
-//   k_attn_bf16<D>  flash attention on v_mfma_f32_32x32x16_bf16, 4 waves x 32 query rows,
-//                   64-key tiles staged in LDS (K row-major, V transposed), online softmax
-//                   in the exp2 domain, tiles past the block-causal prefix never visited.
-//   k_attn_f32<D>   plain f32 FMA kernel (one lane per query row) for the f32 cache.
+//   k_attn_bf16_d128  the D = 128 production kernel (described at its definition).
+//   k_attn_bf16<D>    exact online-softmax flash attention on v_mfma_f32_32x32x16_bf16,
+//                     4 waves x 32 query rows, 64-key tiles staged in LDS (K row-major, V
+//                     transposed by the staging threads), running max with rescaling: the
+//                     kernel for D = 64 and T < 64, and the exact fallback of the D = 128
+//                     kernel for the query tiles it flags.
+//   k_attn_f32<D>     plain f32 FMA kernel (one lane per query row) for the f32 cache.
 //
 // bf16 kernel orientation: S^T = K Q^T (K is the MFMA A operand, Q the B operand), so a
 // lane owns one query row (column l%32 of the 32x32 result) and holds 16 of its 32 scores
@@ -219,38 +222,53 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// k_attn_bf16_d128: the D = 128 production kernel (T >= 32).
+// k_attn_bf16_d128: the D = 128 production kernel (T >= 64).
 //
-//   * 256 query rows per workgroup: 4 waves x 64 rows (two 32-row blocks rb per wave), so
-//     every K or V^T fragment read from LDS feeds two MFMAs (halves LDS read traffic per
-//     flop, which would otherwise sit at the LDS bandwidth limit).
-//   * Key tiles of BN = 32 rows are copied global -> LDS by global_load_lds (16 B per lane,
-//     no registers), two stages, row-major with an XOR swizzle of the 16-byte chunks:
-//         chunk c of key row r sits at position c ^ swz(r), swz(r) = 2 (r & 7) + ((r >> 3) & 1)
-//     which keeps both the K fragment reads (ds_read_b128 of 16 rows) and the V^T fragment
-//     reads (ds_read_b64_tr_b16 of 4 rows x 2 chunks) free of bank conflicts.
+//   * 256 query rows per workgroup, 8 waves x 32 rows: two waves per SIMD, so one wave's
+//     softmax (VALU) and barrier waits overlap the other's MFMAs.
+//   * Key tiles of BN = 64 rows are copied global -> LDS with global_load_lds (16 B per
+//     lane, no registers) into a ring of NS = 4 stages: tile j + 3 is in flight while tile
+//     j is computed.  Rows are stored with an XOR swizzle of their 16-byte chunks:
+//         chunk c of key row r sits at position c ^ swz(r), swz(r) = ((r & 3) << 2) | ((r >> 2) & 3)
+//     swz is a bijection over 16 consecutive rows (K fragment reads, ds_read_b128 of 16 rows
+//     x one chunk, hit 16 distinct 16-byte slots) and puts the low row bits above the chunk
+//     bits (a V^T fragment read, ds_read_b64_tr_b16 of 4 rows x 4 chunks per 32 lanes, hits
+//     16 distinct slots), so neither read has bank conflicts.
 //   * V^T fragments come from the transposing LDS read: within each 16-lane group, lanes
 //     4t..4t+3 address key row t (16 consecutive channels) and lane i receives channel i
 //     of rows 0..3 -- the consecutive keys of one channel the MFMA A operand needs.
+//   * V rows are read where they are stored (memory slot, raw ring or the staged block):
+//     a per-key-frame byte-offset table in LDS plus per-lane (frame, token) cursors.
 //   * Softmax with a fixed reference: m = the row's max over the first key tile (exact).
-//     Every later probability is exp2(s * log2(e)/sqrt(D) - m), so nothing is rescaled
-//     and no running max is kept; since m never exceeds the true row max, terms are only
-//     ever too large, never lost.  If a row's scores exceed m by so much that l or O stops
-//     being finite, the workgroup marks itself in `flags` and the exact online-softmax
-//     kernel below redoes exactly those rows.
+//     Every later probability is exp2(s * log2(e)/sqrt(D) - m), so O is never rescaled
+//     and no running max is kept (O stays in the MFMA accumulators); since m never exceeds
+//     the true row max, terms are only ever too large, never lost.  If a row's scores
+//     exceed m so far that l or O stops being finite, the workgroup marks itself in
+//     `flags` and the exact online-softmax kernel redoes exactly those rows.
 //   * Workgroup -> (head, query tile) mapping keeps each XCD (every 8th workgroup id) on
-//     the tiles of one head at a time, so that head's K/V stream through one L2.
+//     the tiles of one head at a time, so that head's K/V stream once through one L2.
 // ---------------------------------------------------------------------------------------
 namespace d128 {
 
-constexpr int D = 128, BM = 256, BN = 32;
-constexpr int TILE_BYTES = BN * D * 2;  // 8 KiB
+constexpr int D = 128, BM = 256, BN = 64, NS = 4, WAVES = 8;
+constexpr int TILE_BYTES = BN * D * 2;  // 16 KiB
+constexpr int VMEM_PER_TILE = 4;        // copy instructions per wave per tile (K 2, V 2)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// One 1 KiB global -> LDS copy per wave (16 B per lane, lane l lands at lds_row0 + 16 l).
+// Issued through inline asm with M0 = the LDS address: the compiler then does not treat it
+// as an LDS write it must wait for before every later LDS read (it would insert vmcnt(0)
+// right after the copy and the prefetch would never overlap); the ring's own
+// "s_waitcnt vmcnt + barrier" orders the copies with the reads.  No VGPR is written.
+__device__ __forceinline__ void copy_to_lds(const void* src, char* lds_row0) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds_row0);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
 
 // Per-lane source cursor of one 4-row group of a tile: the key row this lane copies.
 struct Cursor {
@@ -258,17 +276,36 @@ struct Cursor {
   int fi, u;    // key frame and token of that row in the next tile to copy
 };
 
-// S = K Q^T of one row block (32 keys x 32 rows), K fragments from kb.
-__device__ __forceinline__ f32x16_t qk(const char* kb, int lr, int hi, const bf16x8_t (&q)[8]) {
-  f32x16_t s = f32x16_t{};
-  const int m = perm32(lr);
+struct Ctx {
+  const AttnArgs* a;
+  const uint16_t* kbase;  // this head's rotated keys [Lk][128]
+  const char* vbase;      // origin of the V byte offsets
+  const int64_t* fbase;   // V byte offset of every key frame
+  char* lds;
+  int h, wave, lane, hi, lr, kvis;
+  float scale;
+};
+
+// Copy tile t's 64 key rows of K and V into ring slot t % NS (each wave: 8 rows as two
+// 4-row groups), then advance the V cursors by one tile.
+__device__ __forceinline__ void issue(const Ctx& c, int t, Cursor (&cur)[2]) {
+  const AttnArgs& a = *c.a;
+  char* kdst = c.lds + (t % NS) * TILE_BYTES;
+  char* vdst = c.lds + (NS + t % NS) * TILE_BYTES;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const int pos = (2 * kk + hi) ^ swz(m);
-    const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(kb + m * 256 + pos * 16);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, q[kk], s, 0, 0, 0);
+  for (int i = 0; i < 2; ++i) {
+    const int r0 = c.wave * 8 + i * 4;
+    const int chunk = (c.lane & 15) ^ swz(cur[i].r);
+    int key = t * BN + cur[i].r;
+    key = key < a.Lk ? key : a.Lk - 1;
+    copy_to_lds(c.kbase + (int64_t)key * D + chunk * 8, kdst + r0 * 256);
+    const char* vsrc = c.vbase + c.fbase[cur[i].fi] + (((int64_t)cur[i].u * a.H + c.h) * D + chunk * 8) * 2;
+    copy_to_lds(vsrc, vdst + r0 * 256);
+    const int nu = cur[i].u + BN;  // T >= BN: at most one wrap into the next frame per tile
+    const int wrap = nu >= a.T ? 1 : 0;
+    cur[i].u = nu - wrap * a.T;
+    cur[i].fi += wrap;
   }
-  return s;
 }
 
 // V^T fragment (16 keys of chunk ch, channels 32 db .. 32 db + 31) from vb.
@@ -287,18 +324,8 @@ __device__ __forceinline__ bf16x8_t vfrag(const char* vb, int lane, int hi, int 
   return vf;
 }
 
-// O += V^T P^T for one row block over the tile's 2 chunks of 16 keys.
-__device__ __forceinline__ void pv(const char* vb, int lane, int hi, const bf16x8_t (&p)[2],
-                                   f32x16_t (&o)[4]) {
-#pragma unroll
-  for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vb, lane, hi, ch, db), p[ch], o[db], 0, 0, 0);
-}
-
 template <bool MASK>
-__device__ __forceinline__ void mask_tile(f32x16_t& s, int key0, int hi, int kvis) {
+__device__ __forceinline__ void mask_block(f32x16_t& s, int key0, int hi, int kvis) {
   if (MASK) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -308,87 +335,67 @@ __device__ __forceinline__ void mask_tile(f32x16_t& s, int key0, int hi, int kvi
   }
 }
 
-// The row's reference max from its first tile (both lanes of the row agree).
-__device__ __forceinline__ float tile_max(const f32x16_t& s, float scale) {
-  float mx = fmaxf(s[0], s[1]);
+// Tile j: issue the copy of tile j + NS - 1 into the slot tile j - 1 used (every wave was
+// done with it before the last barrier), compute tile j, then wait until tile j + 1 has
+// landed (the copies of tiles j + 2 .. j + NS - 1 stay in flight) and sync.  Tiles past
+// the end are copied too (clamped rows, harmless), so the wait count is a constant.
+template <bool MASK, bool FIRST>
+__device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&o)[4],
+                                     float& m_ref, float& l_part, Cursor (&cur)[2]) {
+  const char* kb = c.lds + (j % NS) * TILE_BYTES;
+  const char* vb = c.lds + (NS + j % NS) * TILE_BYTES;
+  issue(c, j + NS - 1, cur);
+  f32x16_t s[2];
 #pragma unroll
-  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  return fmaxf(mx, __shfl_xor(mx, 32)) * scale;
-}
-
-// p = exp2(s*scale - m) as bf16 pairs into p, partial row sum into l_part.
-__device__ __forceinline__ void probs(f32x16_t& s, bf16x8_t (&p)[2], float m, float& l_part, float scale) {
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    s[kb2] = f32x16_t{};
+    const int m = kb2 * 32 + perm32(c.lr);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int pos = (2 * kk + c.hi) ^ swz(m);
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(kb + m * 256 + pos * 16);
+      s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[kb2], 0, 0, 0);
+    }
+  }
+  mask_block<MASK>(s[0], j * BN, c.hi, c.kvis);
+  mask_block<MASK>(s[1], j * BN + 32, c.hi, c.kvis);
+  if (FIRST) {
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    m_ref = fmaxf(mx, __shfl_xor(mx, 32)) * c.scale;
+  }
+  bf16x8_t p[4];
   float sum = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float e = __builtin_amdgcn_exp2f(fmaf(s[r], scale, -m));
-    s[r] = e;
-    sum += e;
-  }
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[kb2][r], c.scale, -m_ref));
+      s[kb2][r] = e;
+      sum += e;
+    }
   l_part += sum;
 #pragma unroll
-  for (int ch = 0; ch < 2; ++ch)
+  for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) p[ch][t] = (__bf16)s[8 * ch + t];
+    for (int t = 0; t < 8; ++t) p[ch][t] = (__bf16)s[ch >> 1][8 * (ch & 1) + t];
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vb, c.lane, c.hi, ch, db), p[ch], o[db], 0, 0, 0);
+  static_assert((NS - 2) * VMEM_PER_TILE == 8, "the wait count below assumes 4 stages");
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  __syncthreads();
 }
 
 }  // namespace d128
 
-// Copy tile t's BN key rows of K and V into LDS (each wave: BN/4 rows, 1 KiB per
-// instruction), then advance the V cursors by one tile.
-__device__ __forceinline__ void d128_issue(const AttnArgs& a, const uint16_t* kbase, const char* vbase,
-                                           const int64_t* fbase, int h, int wave, int lane, int t,
-                                           char* kdst, char* vdst, d128::Cursor (&cur)[2]) {
+__global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   using namespace d128;
-#pragma unroll
-  for (int i = 0; i < BN / 16; ++i) {
-    const int r0 = wave * (BN / 4) + i * 4;
-    const int chunk = (lane & 15) ^ swz(cur[i].r);
-    int key = t * BN + cur[i].r;
-    key = key < a.Lk ? key : a.Lk - 1;
-    __builtin_amdgcn_global_load_lds(kbase + (int64_t)key * D + chunk * 8, (lds_void*)(kdst + r0 * 256),
-                                     16, 0, 0);
-    const char* vsrc = vbase + fbase[cur[i].fi] + (((int64_t)cur[i].u * a.H + h) * D + chunk * 8) * 2;
-    __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + r0 * 256), 16, 0, 0);
-    const int nu = cur[i].u + BN;  // branch-free wrap into the next frame (T >= BN)
-    const int wrap = nu >= a.T ? 1 : 0;
-    cur[i].u = nu - wrap * a.T;
-    cur[i].fi += wrap;
-  }
-}
-
-template <bool MASK, bool FIRST>
-__device__ __forceinline__ void d128_tile(const AttnArgs& a, const uint16_t* kbase, const char* vbase,
-                                          const int64_t* fbase, int h, int wave, int lane, int j, int nt,
-                                          char* lds, const bf16x8_t (&qf)[2][8], f32x16_t (&o)[2][4],
-                                          float (&m_ref)[2], float (&l_part)[2], const int (&kvis)[2],
-                                          float scale, d128::Cursor (&cur)[2]) {
-  using namespace d128;
-  const int hi = lane >> 5, lr = lane & 31;
-  const char* kb = lds + (j & 1) * TILE_BYTES;
-  const char* vb = lds + (2 + (j & 1)) * TILE_BYTES;
-  if (j + 1 < nt)
-    d128_issue(a, kbase, vbase, fbase, h, wave, lane, j + 1, lds + ((j + 1) & 1) * TILE_BYTES,
-               lds + (2 + ((j + 1) & 1)) * TILE_BYTES, cur);
-  bf16x8_t p0[2], p1[2];
-  f32x16_t s0 = qk(kb, lr, hi, qf[0]);
-  f32x16_t s1 = qk(kb, lr, hi, qf[1]);
-  mask_tile<MASK>(s0, j * BN, hi, kvis[0]);
-  if (FIRST) m_ref[0] = tile_max(s0, scale);
-  probs(s0, p0, m_ref[0], l_part[0], scale);
-  mask_tile<MASK>(s1, j * BN, hi, kvis[1]);
-  if (FIRST) m_ref[1] = tile_max(s1, scale);
-  pv(vb, lane, hi, p0, o[0]);
-  probs(s1, p1, m_ref[1], l_part[1], scale);
-  pv(vb, lane, hi, p1, o[1]);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(256, 1) void k_attn_bf16_d128(const AttnArgs a) {
-  using namespace d128;
-  __shared__ __align__(1024) char lds[4 * TILE_BYTES];
-  __shared__ int64_t fbase[LACT_MAX_KEY_FRAMES + 2];
+  __shared__ __align__(1024) char lds[2 * NS * TILE_BYTES];
+  __shared__ int64_t fbase[LACT_MAX_KEY_FRAMES + NS + 2];
 
   // XCD-aware mapping: workgroup id b runs on XCD b % 8; give each XCD a contiguous range
   // of (head, query tile) items so one head's tiles run on one XCD together.
@@ -400,106 +407,97 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16_d128(const AttnArgs a) {
   const int item = x < r8 ? x * (q8 + 1) + jx : r8 * (q8 + 1) + (x - r8) * q8 + jx;
   const int h = item / n_qt, qt = item - h * n_qt;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int hi = lane >> 5, lr = lane & 31;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + (int64_t)h * a.k_head_stride;
+  Ctx c;
+  c.a = &a;
+  c.h = h;
+  c.wave = threadIdx.x >> 6;
+  c.lane = threadIdx.x & 63;
+  c.hi = c.lane >> 5;
+  c.lr = c.lane & 31;
+  c.lds = lds;
+  c.fbase = fbase;
+  c.kbase = static_cast<const uint16_t*>(a.k) + (int64_t)h * a.k_head_stride;
+  c.vbase = static_cast<const char*>(a.v_ring);
+  c.scale = a.scale_log2;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.q_head_stride;
-  const char* vbase = static_cast<const char*>(a.v_ring);
   const int q0 = qt * BM;
 
-  // byte offset (from the raw ring) of every key frame's V; two spare entries repeat the
-  // last frame so that rows past Lk in the last tile read finite data
+  // byte offset (from the raw ring) of every key frame's V; spare entries repeat the last
+  // frame so that rows past Lk (last tile, and the copies issued past the end) read
+  // finite data inside the buffer (a tile is 64 <= T rows, so NS + 2 spares suffice)
   const int n_frames = a.Lk / a.T;
-  for (int fi = threadIdx.x; fi < n_frames + 2; fi += blockDim.x) {
+  for (int fi = threadIdx.x; fi < n_frames + NS + 2; fi += blockDim.x) {
     const int f = fi < n_frames ? fi : n_frames - 1;
     int32_t w;
     const int64_t off = v_row_off(a, f * a.T, 0, &w);
-    const char* base = reinterpret_cast<const char*>(v_base<uint16_t>(a, w));
-    fbase[fi] = (base - vbase) + off * 2;
+    fbase[fi] = (reinterpret_cast<const char*>(v_base<uint16_t>(a, w)) - c.vbase) + off * 2;
   }
 
-  bf16x8_t qf[2][8];
-  int rows[2], kvis[2];
+  const int row = q0 + c.wave * 32 + c.lr;
+  const int rr = row < a.Lq ? row : a.Lq - 1;
+  c.kvis = a.Lhist + a.block_end[block_of_row(a, rr)];
+  bf16x8_t qf[8];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    rows[rb] = q0 + wave * 64 + rb * 32 + lr;
-    const int rr = rows[rb] < a.Lq ? rows[rb] : a.Lq - 1;
-    kvis[rb] = a.Lhist + a.block_end[block_of_row(a, rr)];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[rb][kk] = rows[rb] < a.Lq
-                       ? *reinterpret_cast<const bf16x8_t*>(qb + (int64_t)rows[rb] * D + kk * 16 + hi * 8)
-                       : bf16x8_t{};
-  }
+  for (int kk = 0; kk < 8; ++kk)
+    qf[kk] = row < a.Lq ? *reinterpret_cast<const bf16x8_t*>(qb + (int64_t)row * D + kk * 16 + c.hi * 8)
+                        : bf16x8_t{};
   const int last = (q0 + BM < a.Lq ? q0 + BM : a.Lq) - 1;
   const int kend = a.Lhist + a.block_end[block_of_row(a, last)];
   const int kfree = a.Lhist + a.block_end[block_of_row(a, q0)];
   const int nt = (kend + BN - 1) / BN;
   const int n_free = kfree / BN;  // tiles every row of the workgroup sees completely
-  const float scale = a.scale_log2;
 
-  f32x16_t o[2][4];
+  f32x16_t o[4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[rb][db] = f32x16_t{};
-  float m_ref[2] = {0.0f, 0.0f}, l_part[2] = {0.0f, 0.0f};
-
+  for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
+  float m_ref = 0.0f, l_part = 0.0f;
   Cursor cur[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    cur[i].r = wave * (BN / 4) + i * 4 + (lane >> 4);
+    cur[i].r = c.wave * 8 + i * 4 + (c.lane >> 4);
     cur[i].fi = cur[i].r / a.T;
     cur[i].u = cur[i].r - cur[i].fi * a.T;
   }
   __syncthreads();  // fbase ready
-  d128_issue(a, kbase, vbase, fbase, h, wave, lane, 0, lds, lds + 2 * TILE_BYTES, cur);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int t = 0; t < NS - 1; ++t) issue(c, t, cur);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile 0 landed
   __syncthreads();
 
   if (n_free > 0)
-    d128_tile<false, true>(a, kbase, vbase, fbase, h, wave, lane, 0, nt, lds, qf, o, m_ref, l_part, kvis,
-                           scale, cur);
+    tile<false, true>(c, 0, qf, o, m_ref, l_part, cur);
   else
-    d128_tile<true, true>(a, kbase, vbase, fbase, h, wave, lane, 0, nt, lds, qf, o, m_ref, l_part, kvis,
-                          scale, cur);
+    tile<true, true>(c, 0, qf, o, m_ref, l_part, cur);
   int j = 1;
-  for (; j < n_free && j < nt; ++j)
-    d128_tile<false, false>(a, kbase, vbase, fbase, h, wave, lane, j, nt, lds, qf, o, m_ref, l_part, kvis,
-                            scale, cur);
-  for (; j < nt; ++j)
-    d128_tile<true, false>(a, kbase, vbase, fbase, h, wave, lane, j, nt, lds, qf, o, m_ref, l_part, kvis,
-                           scale, cur);
+  for (; j < n_free && j < nt; ++j) tile<false, false>(c, j, qf, o, m_ref, l_part, cur);
+  for (; j < nt; ++j) tile<true, false>(c, j, qf, o, m_ref, l_part, cur);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
 
-  int bad = 0;
+  const float l = l_part + __shfl_xor(l_part, 32);
+  const float inv = 1.0f / l;
+  bool ok = l > 0.0f && l < 3.0e38f;
+  float outv[4][16];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float l = l_part[rb] + __shfl_xor(l_part[rb], 32);
-    const float inv = 1.0f / l;
-    bool ok = l > 0.0f && l < 3.0e38f;
-    float outv[4][16];
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      outv[db][r] = o[db][r] * inv;
+      ok = ok && (fabsf(outv[db][r]) < 3.0e38f);
+    }
+  int bad = 0;
+  if (row < a.Lq) {
+    bad = ok ? 0 : 1;
+    uint16_t* ob = static_cast<uint16_t*>(a.out) + ((int64_t)row * a.H + h) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        outv[db][r] = o[rb][db][r] * inv;
-        ok = ok && (fabsf(outv[db][r]) < 3.0e38f);
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d0 = db * 32 + jg * 8 + c.hi * 4;
+        uint2 w2;
+        w2.x = (uint32_t)f32_to_bf16(outv[db][jg * 4 + 0]) | ((uint32_t)f32_to_bf16(outv[db][jg * 4 + 1]) << 16);
+        w2.y = (uint32_t)f32_to_bf16(outv[db][jg * 4 + 2]) | ((uint32_t)f32_to_bf16(outv[db][jg * 4 + 3]) << 16);
+        *reinterpret_cast<uint2*>(ob + d0) = w2;
       }
-    if (rows[rb] < a.Lq) {
-      bad |= ok ? 0 : 1;
-      uint16_t* ob = static_cast<uint16_t*>(a.out) + ((int64_t)rows[rb] * a.H + h) * D;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int d0 = db * 32 + jg * 8 + hi * 4;
-          uint2 w;
-          w.x = (uint32_t)f32_to_bf16(outv[db][jg * 4 + 0]) | ((uint32_t)f32_to_bf16(outv[db][jg * 4 + 1]) << 16);
-          w.y = (uint32_t)f32_to_bf16(outv[db][jg * 4 + 2]) | ((uint32_t)f32_to_bf16(outv[db][jg * 4 + 3]) << 16);
-          *reinterpret_cast<uint2*>(ob + d0) = w;
-        }
-      if (hi == 0 && a.lse) a.lse[(int64_t)h * a.Lq + rows[rb]] = (m_ref[rb] + log2f(l)) * 0.6931471805599453f;
-    }
+    if (c.hi == 0 && a.lse) a.lse[(int64_t)h * a.Lq + row] = (m_ref + log2f(l)) * 0.6931471805599453f;
   }
   bad = __syncthreads_or(bad);
   if (threadIdx.x == 0 && a.flags) a.flags[item] = bad;
@@ -584,7 +582,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t kv_dtype, hipStream_t s) 
     dim3 grid((a.Lq + 127) / 128, a.H);
     if (a.D == 128 && a.T >= d128::BN && a.flags) {
       const int items = ((a.Lq + d128::BM - 1) / d128::BM) * a.H;
-      hipLaunchKernelGGL(k_attn_bf16_d128, dim3(items), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_attn_bf16_d128, dim3(items), dim3(64 * d128::WAVES), 0, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(256), 0, s, a);  // flagged tiles only

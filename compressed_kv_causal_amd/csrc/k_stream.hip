@@ -17,18 +17,19 @@ namespace lact {
 // ---------------------------------------------------------------------------------------
 template <int LPR>
 __global__ __launch_bounds__(256) void k_ring_write(const RingWriteArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / LPR;
-  const int li = (int)(gid % LPR);
-  const int tensor = blockIdx.y;
-  const int64_t TH = (int64_t)a.T * a.H;
-  if (row >= (int64_t)a.n_frames * TH) return;
-  const int32_t fi = (int32_t)(row / TH);
+  // blockIdx.y = frame of the block, blockIdx.z = tensor (K, V); rows of a frame are
+  // (token, head) pairs, LPR lanes each
+  const int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int32_t rows = a.T * a.H;
+  const int32_t row = e / LPR, li = e % LPR;
+  if (row >= rows) return;
+  const int32_t fi = blockIdx.y, tensor = blockIdx.z;
   int32_t slot = a.slot0 + fi;
   if (slot >= a.R) slot -= a.R;
-  const int64_t drow = (int64_t)slot * TH + (row - (int64_t)fi * TH);
+  const int64_t srow = (int64_t)fi * rows + row;
+  const int64_t drow = (int64_t)slot * rows + row;
   float x[8];
-  load8_in(a.src[tensor], a.in_dtype, row * a.D + li * 8, x);
+  load8_in(a.src[tensor], a.in_dtype, srow * a.D + li * 8, x);
   const float s = store8_kv<LPR>(a.ring[tensor], a.kv_dtype, drow * a.D + li * 8, x);
   if (a.kv_dtype == DT_FP8 && li == 0) a.ring_scale[tensor][drow] = s;
 }
@@ -40,34 +41,56 @@ __global__ __launch_bounds__(256) void k_ring_write(const RingWriteArgs a) {
 // channel c): acc = b[c]; acc = fmaf(w[c][k], x_k[u][c], acc) for k = 0..r-1, in f32,
 // then stored in the cache dtype.  Each input frame is read once.
 // ---------------------------------------------------------------------------------------
-template <int LPR>
-__global__ __launch_bounds__(256) void k_compress(const CompressArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / LPR;  // (u, h) = (row / H, row % H)
-  const int li = (int)(gid % LPR);
-  const int gi = blockIdx.y >> 1, tensor = blockIdx.y & 1;
-  const int64_t TH = (int64_t)a.T * a.H;
-  if (row >= TH) return;
-  const int32_t h = (int32_t)(row % a.H);
-  const int64_t c0 = (int64_t)h * a.D + li * 8;  // first channel of this lane
-  const float* w = a.w[tensor] + c0 * a.r;
-  const float* b = a.b[tensor] + c0;
-  float acc[8];
+// Work split: a workgroup is one wave; lane = one 8-channel chunk of 64 consecutive chunks
+// (blockIdx.x), so a wave reads and writes 1 KiB contiguous per token; blockIdx.y = a run of
+// TOK tokens, blockIdx.z = (group, tensor).  The lane keeps its 8 x R weights and 8 biases
+// in registers across the tokens.  D/8 lanes form one (token, head) row, which is what
+// the FP8 row quantiser reduces over.
+template <int LPR, int R>
+__global__ __launch_bounds__(64) void k_compress(const CompressArgs a) {
+  constexpr int TOK = 16;
+  const int32_t C = a.H * a.D;
+  const int32_t c0 = (blockIdx.x * 64 + threadIdx.x) * 8;  // first channel of this lane
+  const int gi = blockIdx.z >> 1, tensor = blockIdx.z & 1;
+  const bool active = c0 < C;                              // whole LPR groups are (in)active together
+  const int32_t r = R > 0 ? R : a.r;
+  float w[8][R > 0 ? R : 1], b[8];
+  if (active) {
+    const float* wp = a.w[tensor] + (int64_t)c0 * r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = b[e];
-  for (int k = 0; k < a.r; ++k) {
-    int32_t slot = a.in_slot0[gi] + k;
-    if (slot >= a.R) slot -= a.R;
-    const int64_t srow = (int64_t)slot * TH + row;
-    const float sc = a.kv_dtype == DT_FP8 ? a.ring_scale[tensor][srow] : 1.0f;
-    float x[8];
-    load8_kv(a.ring[tensor], a.kv_dtype, srow * a.D + li * 8, sc, x);
+    for (int e = 0; e < 8; ++e) {
+      b[e] = a.b[tensor][c0 + e];
+      if (R > 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[e * a.r + k], x[e], acc[e]);
+        for (int k = 0; k < R; ++k) w[e][k] = wp[e * R + k];
+      }
+    }
   }
-  const int64_t drow = (int64_t)a.out_slot[gi] * TH + row;
-  const float s = store8_kv<LPR>(a.mem[tensor], a.kv_dtype, drow * a.D + li * 8, acc);
-  if (a.kv_dtype == DT_FP8 && li == 0) a.mem_scale[tensor][drow] = s;
+  const int32_t u0 = blockIdx.y * TOK;
+  for (int32_t u = u0; u < u0 + TOK && u < a.T; ++u) {
+    if (!active) continue;
+    const int64_t el = (int64_t)u * C + c0;                // element offset inside a frame
+    const int32_t hrow = u * a.H + c0 / a.D;               // (token, head) row inside a frame
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = b[e];
+    for (int k = 0; k < r; ++k) {
+      int32_t slot = a.in_slot0[gi] + k;
+      if (slot >= a.R) slot -= a.R;
+      const float sc = a.kv_dtype == DT_FP8 ? a.ring_scale[tensor][(int64_t)slot * a.T * a.H + hrow] : 1.0f;
+      float x[8];
+      load8_kv(a.ring[tensor], a.kv_dtype, (int64_t)slot * a.T * C + el, sc, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float wk = R > 0 ? w[e][R > 0 ? k : 0] : a.w[tensor][(int64_t)(c0 + e) * r + k];
+        acc[e] = fmaf(wk, x[e], acc[e]);
+      }
+    }
+    const int64_t dst = (int64_t)a.out_slot[gi] * a.T * C + el;
+    const float s = store8_kv<LPR>(a.mem[tensor], a.kv_dtype, dst, acc);
+    if (a.kv_dtype == DT_FP8 && (threadIdx.x % LPR) == 0)
+      a.mem_scale[tensor][(int64_t)a.out_slot[gi] * a.T * a.H + hrow] = s;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -136,28 +159,27 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32
   }
 }
 
-// Rows [0, hist_rows): history key frame fi = row / (T*H) of [memory | window], rotated at
-// t = fi into krot[h][fi*T + u].  Rows after: current frame fi, t = n_hist + fi: q -> qrot,
-// k -> krot[h][(n_hist + fi)*T + u], v -> vcur.  FP8 quantises every output row.
+// blockIdx.y = key frame: frames [0, n_hist) are history frames of [memory | window],
+// rotated at t = fi into krot[h][fi*T + u] (only when the history is rebuilt, else the grid
+// starts at the block's frames); frames after are the block's frames i = fi - n_hist at
+// t = fi: q -> qrot, k -> krot[h][t*T + u], v -> vcur.  FP8 quantises every output row.
 template <int LPR>
 __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / LPR;
-  const int li = (int)(gid % LPR);
-  const int64_t TH = (int64_t)a.T * a.H;
+  const int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int32_t rows = a.T * a.H;
+  const int32_t row = e / LPR, li = e % LPR;              // row = u * H + h inside the frame
+  if (row >= rows) return;
+  const int32_t u = row / a.H, h = row - u * a.H;
   const int32_t n_hist = a.hist.mem_len + a.hist.win_len;
-  const int64_t hist_rows = a.hist_rows ? (int64_t)n_hist * TH : 0;
+  const int32_t fi = blockIdx.y + (a.hist_rows ? 0 : n_hist);
   const int64_t KFT = (int64_t)a.key_frames_max * a.T;
   const int64_t QT = (int64_t)a.block_frames_max * a.T;
   const int64_t D = a.D;
   const bool fp8 = a.kv_dtype == DT_FP8;
   float x[8];
-  if (row < hist_rows) {
-    const int32_t fi = (int32_t)(row / TH);
-    const int64_t rem = row - (int64_t)fi * TH;
-    const int32_t u = (int32_t)(rem / a.H), h = (int32_t)(rem % a.H);
+  if (fi < n_hist) {
     const bool mem = hist_is_mem(a.hist, fi);
-    const int64_t srow = (int64_t)hist_slot(a.hist, fi) * TH + rem;
+    const int64_t srow = (int64_t)hist_slot(a.hist, fi) * rows + row;
     const float sc = fp8 ? (mem ? a.mem_k_scale : a.ring_k_scale)[srow] : 1.0f;
     load8_kv(mem ? a.mem_k : a.ring_k, a.kv_dtype, srow * D + li * 8, sc, x);
     rope_rotate8(a, fi, u, li, x);
@@ -166,22 +188,17 @@ __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
     if (fp8 && li == 0) a.krot_scale[drow] = s;
     return;
   }
-  const int64_t crow = row - hist_rows;  // = (fi*T + u)*H + h of the block's [n*T][H][D]
-  if (crow >= (int64_t)a.n_cur * TH) return;
-  const int32_t fi = (int32_t)(crow / TH);
-  const int64_t rem = crow - (int64_t)fi * TH;
-  const int32_t u = (int32_t)(rem / a.H), h = (int32_t)(rem % a.H);
-  const int32_t t = n_hist + fi;
-
+  const int32_t i = fi - n_hist;                           // frame inside the block
+  const int64_t crow = (int64_t)i * rows + row;            // row of the block's [n*T][H][D]
   load8_in(a.q, a.in_dtype, crow * D + li * 8, x);
-  rope_rotate8(a, t, u, li, x);
-  const int64_t qrow = h * QT + (int64_t)fi * a.T + u;
+  rope_rotate8(a, fi, u, li, x);
+  const int64_t qrow = h * QT + (int64_t)i * a.T + u;
   float s = store8_kv<LPR>(a.qrot, a.kv_dtype, qrow * D + li * 8, x);
   if (fp8 && li == 0) a.qrot_scale[qrow] = s;
 
   load8_in(a.k_cur, a.in_dtype, crow * D + li * 8, x);
-  rope_rotate8(a, t, u, li, x);
-  const int64_t krow = h * KFT + (int64_t)t * a.T + u;
+  rope_rotate8(a, fi, u, li, x);
+  const int64_t krow = h * KFT + (int64_t)fi * a.T + u;
   s = store8_kv<LPR>(a.krot, a.kv_dtype, krow * D + li * 8, x);
   if (fp8 && li == 0) a.krot_scale[krow] = s;
 
@@ -204,7 +221,7 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
 hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const int lpr = a.D / 8;
-  dim3 grid(blocks_for(rows * lpr), 2);
+  dim3 grid(blocks_for((int64_t)a.T * a.H * lpr), a.n_frames, 2);
   if (a.D == 128)
     hipLaunchKernelGGL(k_ring_write<16>, grid, dim3(256), 0, s, a);
   else
@@ -214,24 +231,32 @@ hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n_groups <= 0) return hipSuccess;
-  const int64_t rows = (int64_t)a.T * a.H;
-  dim3 grid(blocks_for(rows * (a.D / 8)), 2 * a.n_groups);
-  if (a.D == 128)
-    hipLaunchKernelGGL(k_compress<16>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_compress<8>, grid, dim3(256), 0, s, a);
+  const int32_t chunks = a.H * a.D / 8;
+  dim3 grid((chunks + 63) / 64, (a.T + 15) / 16, 2 * a.n_groups);
+  if (a.D == 128) {
+    if (a.r == 5)
+      hipLaunchKernelGGL((k_compress<16, 5>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_compress<16, 0>), grid, dim3(64), 0, s, a);
+  } else {
+    if (a.r == 5)
+      hipLaunchKernelGGL((k_compress<8, 5>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_compress<8, 0>), grid, dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
-  const int64_t TH = (int64_t)a.T * a.H;
-  const int64_t rows =
-      (a.hist_rows ? (int64_t)(a.hist.mem_len + a.hist.win_len) * TH : 0) + (int64_t)a.n_cur * TH;
-  if (rows <= 0) return hipSuccess;
+  const int32_t n_hist = a.hist.mem_len + a.hist.win_len;
+  const int32_t frames = (a.hist_rows ? n_hist : 0) + a.n_cur;
+  if (frames <= 0) return hipSuccess;
+  const int lpr = a.D / 8;
+  dim3 grid(blocks_for((int64_t)a.T * a.H * lpr), frames);
   if (a.D == 128)
-    hipLaunchKernelGGL(k_rope<16>, dim3(blocks_for(rows * 16)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rope<16>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_rope<8>, dim3(blocks_for(rows * 8)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rope<8>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -219,6 +219,11 @@ def test_bf16_d128_overflow_falls_back_to_exact_pass():
     assert flags.max() == 1, "the fast pass should have flagged its tile"
     ref = run.oc.attention(qh, kh, vh)
     res = dict(out=out, lse=lse, ref=ref)
-    err, dl = run.compare_attention(res)
-    say(f"overflow fallback: flags {flags.tolist()}, rel L2 {err:.3e}, max dLSE {dl:.2e}")
-    assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16]
+    err, _ = run.compare_attention(res)
+    O_ref, LSE_ref, heads, rows = ref
+    lse_got = lse.cpu().numpy()[heads, rows]
+    # scores here are ~2e4; bf16 storage of the rotated keys (~2000, ulp 8) moves them by
+    # tens, so the LSE is held to a relative bar
+    rel_lse = float(np.abs(lse_got - LSE_ref).max() / np.abs(LSE_ref).max())
+    say(f"overflow fallback: flags {flags.tolist()}, rel L2 {err:.3e}, rel dLSE {rel_lse:.2e}")
+    assert err <= ATTN_TOL[BF16] and rel_lse <= 2e-3

@@ -1,0 +1,205 @@
+"""Host-side tests of liblact.so (no GPU needed): exported symbols, sizing, configuration
+checks, the C++ planner against the oracle's bookkeeping (bit-exact over 1000 steps for
+every workload's schedule), and the error paths of the C ABI that fail before anything is
+enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_kv_causal_amd as L
+import synth
+from oracle.bookkeeping import Bookkeeping, OracleCapacityError, OracleStateError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_every_declared_symbol_is_exported():
+    with open(os.path.join(ROOT, "include", "lact.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"\b(lact_\w+)\s*\(", text))
+    assert len(declared) >= 17
+    lib = L.lib()
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in lact.h but not exported"
+    assert declared == set(L.EXPORTS)
+
+
+def _cfg(name="s512_bf16", **kw):
+    return L.make_cfg(**synth.workload(name, **kw))
+
+
+def test_footprint_is_pure_and_matches_layout():
+    for name in synth.WORKLOADS:
+        c = _cfg(name)
+        a, b = L.lact_cache_footprint(c), L.lact_cache_footprint(c)
+        assert a == b
+        lay = L.lact_cache_layout(c)
+        assert lay.total == a
+        w = synth.workload(name)
+        R = w["window_frames"] + w["max_block_frames"] + w["ratio"] - 1
+        assert lay.ring_slots == R
+        assert lay.key_frames_max == w["mem_slots"] + w["window_frames"] + w["max_block_frames"]
+        esize = {0: 4, 1: 2, 2: 1}[w["kv_dtype"]]
+        assert lay.frame_bytes == w["tokens"] * w["channels"] * esize
+        offs = [getattr(lay, n) for n in ("ring_k", "ring_v", "mem_k", "mem_v", "krot", "qrot", "vcur")]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    # 512x512 bf16: 2R + 2M + KF + 2 B_max = 120 frames of 10 MiB, plus the small tables
+    mib = L.lact_cache_footprint(_cfg("s512_bf16")) / 2 ** 20
+    assert 1200 <= mib < 1201
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(head_dim=96), 2), (dict(heads=0), 2), (dict(ratio=0), 2), (dict(ratio=17), 2),
+    (dict(max_block_frames=0), 2), (dict(mem_slots=-1), 2),
+    (dict(mem_slots=200, window_frames=50, max_block_frames=8), 3),
+    (dict(kv_dtype=0, q_dtype=1), 4), (dict(kv_dtype=2, q_dtype=0), 4),
+    (dict(rope_split=(44, 42, 40)), 2), (dict(rope_split=(43, 43, 42)), 2), (dict(rope_mode=2), 2),
+    (dict(rope_theta=0.5), 1),
+])
+def test_config_validation(kw, status):
+    with pytest.raises(L.LactError) as e:
+        L.lact_cache_footprint(_cfg(**kw))
+    assert e.value.status == status
+    assert L.lib().lact_last_error().decode()
+
+
+def _planner_matches_oracle(name, steps):
+    w = synth.workload(name)
+    cfg = L.make_cfg(**w)
+    plan = L.Plan(cfg)
+    bk = Bookkeeping(w["window_frames"], w["mem_slots"], w["ratio"], w["max_block_frames"])
+    for s in range(steps):
+        n = w["first_block"] if s == 0 else w["block"]
+        got, want = plan.state(), bk.state()
+        for key in ("F", "E", "G", "win_len", "mem_len", "pending", "ring_slots", "version"):
+            assert got[key] == want[key], (name, s, key, got, want)
+        gk, wk = plan.keys(n), bk.keys(n)
+        assert [(k["segment"], k["slot"], k["id"], k["t_pos"]) for k in gk] == \
+               [(k["segment"], k["slot"], k["id"], k["t_pos"]) for k in wk], (name, s)
+        plan.append(n)
+        bk.append(n)
+        groups, written = plan.compress()
+        want_groups = bk.compress()
+        assert groups == want_groups, (name, s)
+        assert written == min(len(want_groups), w["mem_slots"])
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_planner_bitexact_vs_oracle_1000_steps(name):
+    _planner_matches_oracle(name, 1000)
+
+
+@pytest.mark.parametrize("W, M, r, B", [(0, 4, 5, 3), (3, 1, 2, 7), (5, 0, 5, 8), (2, 7, 3, 1),
+                                         (8, 16, 5, 8), (1, 1, 1, 1)])
+def test_planner_bitexact_odd_shapes(W, M, r, B):
+    """Odd sizes, including a memory of one slot (groups overwritten inside one call) and
+    no window at all, with blocks of varying sizes."""
+    w = synth.workload("tiny_f32", window_frames=W, mem_slots=M, ratio=r, max_block_frames=B)
+    plan = L.Plan(L.make_cfg(**w))
+    bk = Bookkeeping(W, M, r, B)
+    for s in range(300):
+        n = 1 + (s * 7) % B
+        assert plan.state()["G"] == bk.G
+        plan.append(n)
+        bk.append(n)
+        g1, written = plan.compress()
+        g2 = bk.compress()
+        assert g1 == g2 and written == min(len(g2), M)
+        assert [(k["segment"], k["slot"], k["id"], k["t_pos"]) for k in plan.keys(n)] == \
+               [(k["segment"], k["slot"], k["id"], k["t_pos"]) for k in bk.keys(n)]
+
+
+def test_planner_errors_leave_state_unchanged():
+    w = synth.workload("tiny_f32")
+    plan = L.Plan(L.make_cfg(**w))
+    bk = Bookkeeping(4, 10, 5, 2)
+    with pytest.raises(L.LactError) as e:
+        plan.append(3)
+    assert e.value.status == 3
+    with pytest.raises(OracleCapacityError):
+        bk.append(3)
+    for _ in range(5):
+        plan.append(2)
+        bk.append(2)
+    before = plan.state()
+    with pytest.raises(L.LactError) as e:
+        plan.append(2)                    # a complete group is waiting
+    assert e.value.status == 5
+    with pytest.raises(OracleStateError):
+        bk.append(2)
+    assert plan.state() == before
+
+
+class _HostOnlyCache:
+    """A cache handle over a host address of the right alignment: lact_cache_init does no
+    device work, and every call below fails its checks before anything is enqueued."""
+
+    def __init__(self, name="tiny_f32", **kw):
+        self.cfg = _cfg(name, **kw)
+        self.nbytes = L.lact_cache_footprint(self.cfg)
+        self.h = L.lact_cache_init(self.cfg, 0x10000000, self.nbytes)
+
+    def close(self):
+        L.lact_cache_destroy(self.h)
+
+
+def _call(fn, *args):
+    return fn(*args)
+
+
+def test_abi_error_paths_before_enqueue():
+    lib = L.lib()
+    c = _HostOnlyCache()
+    h = c.h
+    vp = ctypes.c_void_p
+    dev = vp(0x20000000)
+    # attention before any RoPE pass at this state
+    assert lib.lact_block_attention(h, None, 0, dev, None, None) == 5
+    assert "rope" in lib.lact_last_error().decode().lower()
+    # null / misaligned pointers
+    assert lib.lact_rope_reset_apply(h, None, dev, dev, 2, None) == 1
+    assert lib.lact_rope_reset_apply(h, vp(0x20000004), dev, dev, 2, None) == 1
+    assert lib.lact_kv_ring_append(h, dev, None, 2, None) == 1
+    assert lib.lact_convkv_compress(h, None, dev, dev, dev, None, None) == 1
+    assert lib.lact_block_attention(h, None, 0, None, None, None) == 1
+    # frame counts out of range
+    assert lib.lact_rope_reset_apply(h, dev, dev, dev, 0, None) == 3
+    assert lib.lact_rope_reset_apply(h, dev, dev, dev, 3, None) == 3
+    assert lib.lact_kv_ring_append(h, dev, dev, 3, None) == 3
+    assert lib.lact_kv_ring_append(h, dev, dev, 0, None) == 3
+    # nothing changed
+    st = L.lact_cache_state(h)
+    assert (st["F"], st["G"], st["version"], st["staged_valid"]) == (0, 0, 0, 0)
+    # keys of an empty cache: only the current frames, at positions 0..n-1
+    keys = L.lact_cache_keys(h, 2)
+    assert [(k["segment"], k["t_pos"]) for k in keys] == [(2, 0), (2, 1)]
+    # compress with nothing ready enqueues nothing and succeeds
+    n = ctypes.c_int32(-1)
+    w = vp(0x30000000)
+    assert lib.lact_convkv_compress(h, w, w, w, w, None, ctypes.byref(n)) == 0 and n.value == 0
+    c.close()
+
+
+def test_cache_init_checks():
+    lib = L.lib()
+    cfg = _cfg("tiny_f32")
+    nbytes = L.lact_cache_footprint(cfg)
+    out = ctypes.c_void_p()
+    assert lib.lact_cache_init(ctypes.byref(cfg), ctypes.c_void_p(0x10000010), nbytes,
+                               ctypes.byref(out)) == 1          # not 256-aligned
+    assert lib.lact_cache_init(ctypes.byref(cfg), ctypes.c_void_p(0x10000000), nbytes - 1,
+                               ctypes.byref(out)) == 3          # too small
+    assert lib.lact_cache_init(ctypes.byref(cfg), None, nbytes, ctypes.byref(out)) == 1
+    assert lib.lact_cache_destroy(None) == 0
+
+
+def test_multiblock_argument_checks():
+    lib = L.lib()
+    c = _HostOnlyCache("tiny_f32", max_block_frames=6)
+    dev = ctypes.c_void_p(0x20000000)
+    blocks = (ctypes.c_int32 * 2)(1, 2)
+    # still no RoPE pass: state error comes first
+    assert lib.lact_block_attention(c.h, blocks, 2, dev, None, None) == 5
+    c.close()
