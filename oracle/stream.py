@@ -55,6 +55,25 @@ class OracleCache:
             return vals.reshape(self.T, self.H, self.D), s[2].reshape(self.T, self.H)
         return s[1].reshape(self.T, self.H, self.D), None
 
+    @classmethod
+    def at_state(cls, cfg, F, frame_kv, wk, bk, wv, bv):
+        """The cache after F frames were appended and every complete group compressed,
+        built directly: memory slots are each compressed once from their own r frames, so
+        only the groups still present and the live raw frames are needed.
+        frame_kv(f) -> (k, v) float32 [T*C] input values of absolute frame f."""
+        oc = cls(cfg)
+        bk_ = oc.bk
+        bk_.F = F
+        G = bk_.E // bk_.r
+        first = max(0, G - bk_.M) if bk_.M > 0 else G
+        bk_.G = first
+        for f in range(bk_.r * first, F):
+            k, v = frame_kv(f)
+            oc.raw[f] = (oc._store(k), oc._store(v))
+        oc.compress(wk, bk, wv, bv)
+        assert bk_.G == G
+        return oc
+
     # ---- the four operations ---------------------------------------------------------
     def append(self, k_new, v_new):
         """k_new, v_new: [n][T*C] float32 input values."""

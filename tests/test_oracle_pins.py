@@ -581,3 +581,32 @@ def test_stream_frame_id_tag_uniform():
     oc = _tag_stream(None)
     for slot, (g, sk, _) in oc.mem.items():
         assert abs(sk[1][0] - (5 * g + 2)) <= 1e-5 * (5 * g + 2)
+
+
+def test_stream_at_state_equals_sequential_stream():
+    """Building the cache state at frame F directly equals streaming to F block by block
+    (non-recursive FIFO memory: each slot comes from its own r frames only)."""
+    cfg = synth.workload("tiny_f32", pool_blocks=3)
+    T, C = cfg["tokens"], cfg["channels"]
+    wk, bk = synth.conv_weights(cfg, 0, synth.TENSOR_WK)
+    wv, bv = synth.conv_weights(cfg, 0, synth.TENSOR_WV)
+
+    def frame_kv(f):
+        return (synth.frames(cfg, 0, synth.TENSOR_K, [f])[0], synth.frames(cfg, 0, synth.TENSOR_V, [f])[0])
+
+    seq = OracleCache(cfg)
+    for step in range(40):
+        ks = np.stack([frame_kv(seq.bk.F + i)[0] for i in range(2)])
+        vs = np.stack([frame_kv(seq.bk.F + i)[1] for i in range(2)])
+        seq.append(ks, vs)
+        seq.compress(wk, bk, wv, bv)
+        if step in (3, 17, 39):
+            ff = OracleCache.at_state(cfg, seq.bk.F, frame_kv, wk, bk, wv, bv)
+            assert ff.bk.state() == {**seq.bk.state(), "version": ff.bk.version}
+            assert sorted(ff.mem) == sorted(seq.mem)
+            for slot in seq.mem:
+                assert ff.mem[slot][0] == seq.mem[slot][0]
+                assert np.array_equal(ff.mem[slot][1][1], seq.mem[slot][1][1])
+                assert np.array_equal(ff.mem[slot][2][1], seq.mem[slot][2][1])
+            for f in range(seq.bk.E, seq.bk.F):
+                assert np.array_equal(ff.raw[f][0][1], seq.raw[f][0][1])
