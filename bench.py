@@ -82,7 +82,8 @@ def main():
     w = synth.workload(args.workload)
     T, H, D = w["tokens"], w["heads"], w["head_dim"]
     B = w["block"]
-    dt = {0: "f32", 1: "bf16", 2: "fp8"}[w["kv_dtype"]]
+    dt = {0: "f32", 1: "bf16", 2: "fp8"}[w["kv_dtype"]]   # storage of the cache
+    op = "f32" if w["q_dtype"] == 0 else "bf16"          # arithmetic of the attention
     io = torch.float32 if w["q_dtype"] == 0 else torch.bfloat16
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -164,16 +165,25 @@ def main():
     ms_step_events = float(part.sum(axis=1).mean())
     ms_per_step = wall * 1e3 / args.steps
 
-    frame_bytes = T * H * D * {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+    fe = T * H * D                                   # elements per frame
+    kvb = {"f32": 4, "bf16": 2, "fp8": 1}[dt]        # stored bytes per element
+    ob = 4 if w["q_dtype"] == 0 else 2               # input / staged operand bytes
+    sb = T * H * 4 if dt == "fp8" else 0             # f32 row scales per stored frame
     attn_flop = 4.0 * Lq * Lk * D * H
     attn_tflops = attn_flop / (ms[1] * 1e-3) / 1e12
-    peak = PEAK[dt]
+    peak = PEAK[op]
     # algorithmic bytes of the streaming kernels (per step)
-    rope_bytes = frame_bytes * (2 * n_hist + 6 * B)
-    append_bytes = 4 * B * frame_bytes
+    hist_k = n_hist * (fe * (kvb + ob) + sb)         # stored K read, rotated operand written
+    hist_v = n_hist * (fe * (kvb + ob) + sb) if dt == "fp8" else 0   # V dequantised
+    rope_bytes = hist_k + hist_v + 3 * B * fe * 2 * ob
+    append_bytes = 2 * B * (fe * (ob + kvb) + sb)
     slots_per_step = B / w["ratio"]
-    compress_bytes = slots_per_step * 2 * frame_bytes * (w["ratio"] + 1)
+    compress_bytes = slots_per_step * 2 * (fe * kvb + sb) * (w["ratio"] + 1)
     traffic = load_traffic("k_attn.hip", f"attn_{args.workload}")
+    # query tiles the fast attention pass handed to the exact pass in the last step
+    n_flags = H * ((Lq + 255) // 256)
+    flags = cache.buf[cache.layout.attn_flags:].view(torch.int32)[:n_flags]
+    exact_tiles = int(flags.sum().item()) if w["q_dtype"] != 0 else 0
 
     rec = {
         "metric": METRIC,
@@ -186,12 +196,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dt,
+        "dtype": op,
         "data": "synthetic (seeded N(0,1) Q/K/V, N(0,0.2) conv weights; HDTF/EMTD stand-in)",
-        "config": {"workload": args.workload, "heads": H, "head_dim": D, "tokens_per_frame": T,
+        "config": {"workload": args.workload, "kv_storage": dt, "heads": H, "head_dim": D, "tokens_per_frame": T,
                    "block_frames": B, "window_frames": w["window_frames"],
                    "mem_slots": w["mem_slots"], "ratio": w["ratio"], "Lq": Lq, "Lk": Lk},
         "attn_tflops": round(attn_tflops, 2),
+        "attn_exact_pass_tiles": f"{exact_tiles}/{n_flags}",
         "step_breakdown_ms": {"rope_reset_apply": round(ms[0], 4),
                               "block_attention": round(ms[1], 4),
                               "kv_ring_append": round(ms[2], 4),

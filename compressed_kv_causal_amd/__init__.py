@@ -50,9 +50,9 @@ class lact_state(ctypes.Structure):
                 ("staged_valid", ctypes.c_int32)]
 
 
-_LAYOUT_FIELDS = ["total", "ring_k", "ring_v", "mem_k", "mem_v", "krot", "qrot", "vcur",
-                  "ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale", "krot_scale",
-                  "qrot_scale", "vcur_scale", "rope_table", "attn_flags", "frame_bytes"]
+_LAYOUT_FIELDS = ["total", "ring_k", "ring_v", "mem_k", "mem_v", "krot", "qrot", "vcur", "vhist",
+                  "ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale", "rope_table",
+                  "attn_flags", "frame_bytes"]
 
 
 class lact_layout(ctypes.Structure):

@@ -140,6 +140,14 @@ __device__ __forceinline__ void load8_kv(const void* base, int32_t dtype, int64_
     load8_fp8(static_cast<const uint8_t*>(base) + off, row_scale, x);
 }
 
+// Store 8 elements in an operand dtype (F32 or BF16) at element offset off.
+__device__ __forceinline__ void store8_op(void* base, int32_t dtype, int64_t off, const float* x) {
+  if (dtype == DT_F32)
+    store8_f32(static_cast<float*>(base) + off, x);
+  else
+    store8_bf16(static_cast<uint16_t*>(base) + off, x);
+}
+
 // Store 8 elements in dtype at element offset off.  FP8 quantises the row: every lane of
 // the row's group (lanes_per_row consecutive lanes) must call this together; the row's
 // scale is returned (and written by the caller).

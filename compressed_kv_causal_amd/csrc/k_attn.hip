@@ -239,12 +239,13 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
 //     of rows 0..3 -- the consecutive keys of one channel the MFMA A operand needs.
 //   * V rows are read where they are stored (memory slot, raw ring or the staged block):
 //     a per-key-frame byte-offset table in LDS plus per-lane (frame, token) cursors.
-//   * Softmax with a fixed reference: m = the row's max over the first key tile (exact).
-//     Every later probability is exp2(s * log2(e)/sqrt(D) - m), so O is never rescaled
-//     and no running max is kept (O stays in the MFMA accumulators); since m never exceeds
-//     the true row max, terms are only ever too large, never lost.  If a row's scores
-//     exceed m so far that l or O stops being finite, the workgroup marks itself in
-//     `flags` and the exact online-softmax kernel redoes exactly those rows.
+//   * Softmax with a lazily raised reference: m = the row's max over the first key tile.
+//     Every later probability is exp2(s * log2(e)/sqrt(D) - m), so there is no running
+//     max and no per-tile rescale of O; since m never exceeds the true row max, terms are
+//     only ever too large, never lost.  Only when a lane's tile sum reaches 2^64 (scores
+//     far above m, e.g. from outlier channels) does the wave raise m by a power of two and
+//     scale O and l exactly (see tile()).  If l or O still ends up not finite, the
+//     workgroup marks itself in `flags` and the exact online-softmax kernel redoes its rows.
 //   * Workgroup -> (head, query tile) mapping keeps each XCD (every 8th workgroup id) on
 //     the tiles of one head at a time, so that head's K/V stream once through one L2.
 // ---------------------------------------------------------------------------------------
@@ -335,17 +336,10 @@ __device__ __forceinline__ void mask_block(f32x16_t& s, int key0, int hi, int kv
   }
 }
 
-// Tile j: issue the copy of tile j + NS - 1 into the slot tile j - 1 used (every wave was
-// done with it before the last barrier), compute tile j, then wait until tile j + 1 has
-// landed (the copies of tiles j + 2 .. j + NS - 1 stay in flight) and sync.  Tiles past
-// the end are copied too (clamped rows, harmless), so the wait count is a constant.
-template <bool MASK, bool FIRST>
-__device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&o)[4],
-                                     float& m_ref, float& l_part, Cursor (&cur)[2]) {
-  const char* kb = c.lds + (j % NS) * TILE_BYTES;
-  const char* vb = c.lds + (NS + j % NS) * TILE_BYTES;
-  issue(c, j + NS - 1, cur);
-  f32x16_t s[2];
+// S^T of one 64-key tile (two 32-key blocks) from the K rows in LDS, masked.
+template <bool MASK>
+__device__ __forceinline__ void qk_tile(const Ctx& c, int j, const char* kb, const bf16x8_t (&qf)[8],
+                                        f32x16_t (&s)[2]) {
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
     s[kb2] = f32x16_t{};
@@ -359,23 +353,70 @@ __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8
   }
   mask_block<MASK>(s[0], j * BN, c.hi, c.kvis);
   mask_block<MASK>(s[1], j * BN + 32, c.hi, c.kvis);
+}
+
+// p = exp2(s * scale - m_ref) in place; returns this lane's sum of the 32 probabilities.
+__device__ __forceinline__ float exp_tile(f32x16_t (&s)[2], float scale, float m_ref) {
+  float sum = 0.0f;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[kb2][r], scale, -m_ref));
+      s[kb2][r] = e;
+      sum += e;
+    }
+  return sum;
+}
+
+// Tile j: issue the copy of tile j + NS - 1 into the slot tile j - 1 used (every wave was
+// done with it before the last barrier), compute tile j, then wait until tile j + 1 has
+// landed (the copies of tiles j + 2 .. j + NS - 1 stay in flight) and sync.  Tiles past
+// the end are copied too (clamped rows, harmless), so the wait count is a constant.
+//
+// Reference raise: a lane sum of 2^64 or more means a row met scores far above its
+// reference.  The wave then takes each such row's largest probability of the tile, 2^e *
+// [1, 2), and divides that row's probabilities, O and l by 2^e (exact power-of-two scaling)
+// while m_ref moves up by e.  Ordinary data never takes this branch; scores with large
+// outliers take it a few times per row at most.  A probability that is already infinite
+// (a score >= 128 above the reference) cannot be rescaled: l and O become infinite and the
+// workgroup hands its rows to the exact pass.
+template <bool MASK, bool FIRST>
+__device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&o)[4],
+                                     float& m_ref, float& l_part, Cursor (&cur)[2]) {
+  const char* kb = c.lds + (j % NS) * TILE_BYTES;
+  const char* vb = c.lds + (NS + j % NS) * TILE_BYTES;
+  issue(c, j + NS - 1, cur);
+  f32x16_t s[2];
+  qk_tile<MASK>(c, j, kb, qf, s);
   if (FIRST) {
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
     m_ref = fmaxf(mx, __shfl_xor(mx, 32)) * c.scale;
   }
-  bf16x8_t p[4];
-  float sum = 0.0f;
+  float sum = exp_tile(s, c.scale, m_ref);
+  if (!FIRST && __builtin_expect(__any(!(sum < 0x1p64f)), 0)) {
+    float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // e = floor(log2(mx)) for a finite mx >= 2, else 0
+    const int e = (mx >= 2.0f && mx < INFINITY) ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[kb2][r], c.scale, -m_ref));
-      s[kb2][r] = e;
-      sum += e;
-    }
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb2][r] = __builtin_ldexpf(s[kb2][r], -e);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = __builtin_ldexpf(o[db][r], -e);
+    l_part = __builtin_ldexpf(l_part, -e);
+    sum = __builtin_ldexpf(sum, -e);
+    m_ref += (float)e;
+  }
   l_part += sum;
+  bf16x8_t p[4];
 #pragma unroll
   for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
@@ -576,9 +617,9 @@ __global__ __launch_bounds__(64) void k_attn_f32(const AttnArgs a) {
   }
 }
 
-hipError_t launch_attention(const AttnArgs& a, int32_t kv_dtype, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& a, int32_t op_dtype, hipStream_t s) {
   if (a.Lq <= 0) return hipSuccess;
-  if (kv_dtype == DT_BF16) {
+  if (op_dtype == DT_BF16) {
     dim3 grid((a.Lq + 127) / 128, a.H);
     if (a.D == 128 && a.T >= d128::BN && a.flags) {
       const int items = ((a.Lq + d128::BM - 1) / d128::BM) * a.H;
@@ -594,7 +635,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t kv_dtype, hipStream_t s) 
       else
         hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(256), 0, s, g);
     }
-  } else if (kv_dtype == DT_F32) {
+  } else if (op_dtype == DT_F32) {
     dim3 grid((a.Lq + 63) / 64, a.H);
     if (a.D == 128)
       hipLaunchKernelGGL(k_attn_f32<128>, grid, dim3(64), 0, s, a);

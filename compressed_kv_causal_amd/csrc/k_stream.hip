@@ -162,7 +162,9 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32
 // blockIdx.y = key frame: frames [0, n_hist) are history frames of [memory | window],
 // rotated at t = fi into krot[h][fi*T + u] (only when the history is rebuilt, else the grid
 // starts at the block's frames); frames after are the block's frames i = fi - n_hist at
-// t = fi: q -> qrot, k -> krot[h][t*T + u], v -> vcur.  FP8 quantises every output row.
+// t = fi: q -> qrot, k -> krot[h][t*T + u], v -> vcur.  Every output is in the operand
+// dtype (in_dtype).  An FP8 cache is dequantised on the way (code * row scale), and its
+// history V rows are dequantised into vhist in attention order as well.
 template <int LPR>
 __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
   const int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
@@ -184,27 +186,26 @@ __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
     load8_kv(mem ? a.mem_k : a.ring_k, a.kv_dtype, srow * D + li * 8, sc, x);
     rope_rotate8(a, fi, u, li, x);
     const int64_t drow = h * KFT + (int64_t)fi * a.T + u;
-    const float s = store8_kv<LPR>(a.krot, a.kv_dtype, drow * D + li * 8, x);
-    if (fp8 && li == 0) a.krot_scale[drow] = s;
+    store8_op(a.krot, a.in_dtype, drow * D + li * 8, x);
+    if (fp8) {
+      const float sv = (mem ? a.mem_v_scale : a.ring_v_scale)[srow];
+      load8_kv(mem ? a.mem_v : a.ring_v, DT_FP8, srow * D + li * 8, sv, x);
+      store8_op(a.vhist, a.in_dtype, ((int64_t)fi * rows + row) * D + li * 8, x);
+    }
     return;
   }
   const int32_t i = fi - n_hist;                           // frame inside the block
   const int64_t crow = (int64_t)i * rows + row;            // row of the block's [n*T][H][D]
   load8_in(a.q, a.in_dtype, crow * D + li * 8, x);
   rope_rotate8(a, fi, u, li, x);
-  const int64_t qrow = h * QT + (int64_t)i * a.T + u;
-  float s = store8_kv<LPR>(a.qrot, a.kv_dtype, qrow * D + li * 8, x);
-  if (fp8 && li == 0) a.qrot_scale[qrow] = s;
+  store8_op(a.qrot, a.in_dtype, (h * QT + (int64_t)i * a.T + u) * D + li * 8, x);
 
   load8_in(a.k_cur, a.in_dtype, crow * D + li * 8, x);
   rope_rotate8(a, fi, u, li, x);
-  const int64_t krow = h * KFT + (int64_t)fi * a.T + u;
-  s = store8_kv<LPR>(a.krot, a.kv_dtype, krow * D + li * 8, x);
-  if (fp8 && li == 0) a.krot_scale[krow] = s;
+  store8_op(a.krot, a.in_dtype, (h * KFT + (int64_t)fi * a.T + u) * D + li * 8, x);
 
   load8_in(a.v_cur, a.in_dtype, crow * D + li * 8, x);
-  s = store8_kv<LPR>(a.vcur, a.kv_dtype, crow * D + li * 8, x);
-  if (fp8 && li == 0) a.vcur_scale[crow] = s;
+  store8_op(a.vcur, a.in_dtype, crow * D + li * 8, x);
 }
 
 // ---------------------------------------------------------------------------------------

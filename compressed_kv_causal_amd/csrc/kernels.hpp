@@ -46,23 +46,27 @@ struct CompressArgs {
 };
 
 // RoPE reset + apply: rebuild rotated history keys (if hist_rows) and stage the block.
+// Staged operands (krot, qrot, vcur, vhist) are in the operand dtype = in_dtype (the q
+// dtype): an FP8 cache is dequantised here, once per step, and attention runs on bf16.
 struct RopeArgs {
   const void* q;
   const void* k_cur;
   const void* v_cur;       // [n*T][H][D] in in_dtype
   const void* ring_k;
   const void* mem_k;
+  const void* ring_v;
+  const void* mem_v;
   const float* ring_k_scale;
   const float* mem_k_scale;
+  const float* ring_v_scale;
+  const float* mem_v_scale;
   void* krot;              // [H][KF*T][D] operand dtype
-  float* krot_scale;       // [H][KF*T]
   void* qrot;              // [H][B_max*T][D]
-  float* qrot_scale;       // [H][B_max*T]
-  void* vcur;              // [B_max][T][H][D] kv dtype
-  float* vcur_scale;       // [B_max][T][H]
+  void* vcur;              // [B_max][T][H][D]
+  void* vhist;             // FP8 only: [M+W][T][H][D] dequantised V of [memory | window]
   const float2* table;
   HistMap hist;
-  int32_t hist_rows;       // 1: rebuild history keys
+  int32_t hist_rows;       // 1: rebuild history keys (and, FP8, history values)
   int32_t n_cur, T, H, D, grid_h, grid_w, key_frames_max, block_frames_max;
   int32_t rope_mode, split_t, split_h, split_w;
   int32_t in_dtype, kv_dtype;
@@ -75,23 +79,17 @@ struct RopeTableArgs {
   int64_t entries;
 };
 
-// Attention of the staged block over [memory | window | current].
+// Attention of the staged block over [memory | window | current] (operand dtype).
 struct AttnArgs {
   const void* q;           // qrot
-  const float* q_scale;
   const void* k;           // krot
-  const float* k_scale;
-  const void* v_ring;
-  const void* v_mem;
-  const void* v_cur;
-  const float* v_ring_scale;
-  const float* v_mem_scale;
-  const float* v_cur_scale;
+  const void* v_ring;      // V rows of window frames (raw ring slots)
+  const void* v_mem;       // V rows of memory frames (memory slots)
+  const void* v_cur;       // V rows of the block's frames
   void* out;               // [Lq][H][D] q dtype
   float* lse;              // [H][Lq] or null
   int32_t* flags;          // per (head, 256-row query tile): 1 = redo with the exact pass
   int64_t q_head_stride, k_head_stride;  // elements (= rows * D) between heads
-  int64_t qs_head_stride, ks_head_stride;
   HistMap hist;
   int32_t T, H, D, Lq, Lk, Lhist;
   int32_t n_blocks;
@@ -103,6 +101,6 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
 hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
-hipError_t launch_attention(const AttnArgs& a, int32_t kv_dtype, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int32_t op_dtype, hipStream_t s);
 
 }  // namespace lact

@@ -82,6 +82,7 @@ void compute_layout(const lact_cfg& c, lact_layout* L) {
   const int32_t B = c.max_block_frames, M = c.mem_slots;
   const bool fp8 = c.kv_dtype == LACT_FP8_E4M3;
   const size_t fb = (size_t)fe * kvb;
+  const size_t ob = (size_t)fe * elem_bytes(c.q_dtype);  // one frame in the operand dtype
   const size_t sb = (size_t)T * c.heads * 4;  // one frame of f32 row scales
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -93,17 +94,15 @@ void compute_layout(const lact_cfg& c, lact_layout* L) {
   L->ring_v = take(fb * R);
   L->mem_k = take(fb * M);
   L->mem_v = take(fb * M);
-  L->krot = take(fb * KF);
-  L->qrot = take(fb * B);
-  L->vcur = take(fb * B);
+  L->krot = take(ob * KF);
+  L->qrot = take(ob * B);
+  L->vcur = take(ob * B);
+  L->vhist = take(fp8 ? ob * (size_t)(M + c.window_frames) : 0);
   if (fp8) {
     L->ring_k_scale = take(sb * R);
     L->ring_v_scale = take(sb * R);
     L->mem_k_scale = take(sb * M);
     L->mem_v_scale = take(sb * M);
-    L->krot_scale = take(sb * KF);
-    L->qrot_scale = take(sb * B);
-    L->vcur_scale = take(sb * B);
   }
   L->rope_table = take(sizeof(float) * 2 * (size_t)rope_table_entries(c));
   L->attn_flags = take(sizeof(int32_t) * (size_t)c.heads * (size_t)((B * T + 255) / 256));
@@ -233,14 +232,16 @@ lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cu
   a.v_cur = v_cur;
   a.ring_k = c->at(c->lay.ring_k);
   a.mem_k = c->at(c->lay.mem_k);
+  a.ring_v = c->at(c->lay.ring_v);
+  a.mem_v = c->at(c->lay.mem_v);
   a.ring_k_scale = c->fat(c->lay.ring_k_scale);
   a.mem_k_scale = c->fat(c->lay.mem_k_scale);
+  a.ring_v_scale = c->fat(c->lay.ring_v_scale);
+  a.mem_v_scale = c->fat(c->lay.mem_v_scale);
   a.krot = c->at(c->lay.krot);
-  a.krot_scale = c->fat(c->lay.krot_scale);
   a.qrot = c->at(c->lay.qrot);
-  a.qrot_scale = c->fat(c->lay.qrot_scale);
   a.vcur = c->at(c->lay.vcur);
-  a.vcur_scale = c->fat(c->lay.vcur_scale);
+  a.vhist = g.kv_dtype == LACT_FP8_E4M3 ? c->at(c->lay.vhist) : nullptr;
   a.table = static_cast<const float2*>(c->at(c->lay.rope_table));
   a.hist = c->hist();
   const bool rebuild = !(c->hist_built && c->hist_version == c->plan.version());
@@ -298,23 +299,28 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
     a.n_blocks = n_q_blocks;
   }
   a.q = c->at(c->lay.qrot);
-  a.q_scale = c->fat(c->lay.qrot_scale);
   a.k = c->at(c->lay.krot);
-  a.k_scale = c->fat(c->lay.krot_scale);
-  a.v_ring = c->at(c->lay.ring_v);
-  a.v_mem = c->at(c->lay.mem_v);
   a.v_cur = c->at(c->lay.vcur);
-  a.v_ring_scale = c->fat(c->lay.ring_v_scale);
-  a.v_mem_scale = c->fat(c->lay.mem_v_scale);
-  a.v_cur_scale = c->fat(c->lay.vcur_scale);
   a.out = out;
   a.lse = lse;
   a.flags = reinterpret_cast<int32_t*>(c->at(c->lay.attn_flags));
   a.q_head_stride = (int64_t)g.max_block_frames * T * g.head_dim;
   a.k_head_stride = (int64_t)c->lay.key_frames_max * T * g.head_dim;
-  a.qs_head_stride = (int64_t)g.max_block_frames * T;
-  a.ks_head_stride = (int64_t)c->lay.key_frames_max * T;
   a.hist = c->hist();
+  if (g.kv_dtype == LACT_FP8_E4M3) {
+    // history V was dequantised into vhist in attention order: memory ranks from its
+    // start, window ranks after them
+    const size_t ob = (size_t)T * g.heads * g.head_dim * elem_bytes(g.q_dtype);
+    a.v_mem = c->at(c->lay.vhist);
+    a.v_ring = c->at(c->lay.vhist + ob * (size_t)a.hist.mem_len);
+    a.hist.mem_slot0 = 0;
+    a.hist.ring_slot0 = 0;
+    a.hist.M = a.hist.mem_len > 0 ? a.hist.mem_len : 1;
+    a.hist.R = a.hist.win_len > 0 ? a.hist.win_len : 1;
+  } else {
+    a.v_ring = c->at(c->lay.ring_v);
+    a.v_mem = c->at(c->lay.mem_v);
+  }
   a.T = T;
   a.H = g.heads;
   a.D = g.head_dim;
@@ -322,8 +328,7 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
   a.Lhist = c->plan.history_frames() * T;
   a.Lk = a.Lhist + a.Lq;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
-  hipError_t e = lact::launch_attention(a, g.kv_dtype, static_cast<hipStream_t>(stream));
-  if (e == hipErrorNotSupported) return fail(LACT_E_DTYPE, "attention for this kv dtype is not built");
+  hipError_t e = lact::launch_attention(a, g.q_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return LACT_OK;
 }

@@ -100,21 +100,25 @@ typedef struct {
 } lact_state;
 
 /* Offsets (bytes, 256-aligned) of the regions inside the single cache buffer, so a caller
- * can inspect or snapshot it.  Scale regions are 0-sized unless kv_dtype is FP8_E4M3.
+ * can inspect or snapshot it.  Scale regions and vhist are 0-sized unless kv_dtype is
+ * FP8_E4M3.
  *   ring_k/ring_v  [R][T][H][D] kv dtype            raw ring (pre-RoPE K, V)
  *   mem_k/mem_v    [M][T][H][D] kv dtype            compressed memory slots
  *   krot           [H][(M+W+B_max)*T][D] operand    rotated keys in attention order
  *   qrot           [H][B_max*T][D] operand          rotated queries of the block
- *   vcur           [B_max][T][H][D] kv dtype        current V staged for attention
- *   *_scale        f32 per (token, head): ring/mem/vcur [slots][T][H]; krot/qrot [H][L]
+ *   vcur           [B_max][T][H][D] operand         current V staged for attention
+ *   vhist          [M+W][T][H][D] operand           FP8: memory + window V dequantised
+ *   *_scale        f32 per (token, head): ring/mem [slots][T][H]
  *   rope_table     float2 (cos, sin) table
  *   attn_flags     int32 per (head, 256-row query tile): attention work queue of the exact
  *                  fallback pass (rows whose fast pass could not be trusted)
- * operand dtype = F32 / BF16 / FP8_E4M3 codes as kv_dtype. */
+ * The persistent state is ring_* and mem_* (and their scales); the rest is rewritten by
+ * every step.  operand dtype = q_dtype: an FP8 cache is dequantised (code * scale) when the
+ * RoPE pass stages a step, and attention runs on bf16 operands. */
 typedef struct {
   size_t total;
-  size_t ring_k, ring_v, mem_k, mem_v, krot, qrot, vcur;
-  size_t ring_k_scale, ring_v_scale, mem_k_scale, mem_v_scale, krot_scale, qrot_scale, vcur_scale;
+  size_t ring_k, ring_v, mem_k, mem_v, krot, qrot, vcur, vhist;
+  size_t ring_k_scale, ring_v_scale, mem_k_scale, mem_v_scale;
   size_t rope_table, attn_flags;
   size_t frame_bytes;    /* T*H*D * kv element size                                       */
   int32_t ring_slots, key_frames_max;
@@ -147,8 +151,11 @@ lact_status lact_cache_destroy(lact_cache* cache);
  * memory rank j -> t = j; window rank k -> t = mem_len + k; current frame i ->
  * t = mem_len + win_len + i; (h, w) = the token's grid cell.  Rotation of interleaved
  * channel pairs (2i, 2i+1) of each part by pos * theta^(-2i/d_part).
- * Writes krot (memory + window + current keys), qrot and vcur.  For FP8_E4M3 it
- * quantises per (token, head): scale = amax/448, codes = e4m3(x * 448/amax).
+ * Writes krot (memory + window + current keys), qrot and vcur in the operand dtype
+ * (q_dtype).  The stored history is read as stored (FP8_E4M3: code * per-(token, head)
+ * scale; the model card's FP8 KV cache option keeps K/V in FP8 and widens them for the
+ * attention), and an FP8 cache also gets its memory + window V dequantised into vhist.  The history part
+ * is rebuilt only when the state changed since the last call.
  *   q, k_cur, v_cur: [n_frames*T][H][D] in q_dtype.  1 <= n_frames <= B_max. */
 lact_status lact_rope_reset_apply(lact_cache* cache, const void* q, const void* k_cur,
                                   const void* v_cur, int32_t n_frames, void* stream);
@@ -166,7 +173,8 @@ lact_status lact_block_attention(lact_cache* cache, const int32_t* q_block_frame
 
 /* Append-only ring append (walkthrough, "ConvKV Memory" and "Streaming Pipeline": only the
  * new tokens' KV are added, cached KV stay unchanged).  Frame F + i goes to raw slot
- * (F + i) mod R; F += n_frames.  FP8_E4M3 quantises per (token, head) as above.
+ * (F + i) mod R; F += n_frames.  FP8_E4M3 quantises per (token, head): scale = amax/448
+ * (1 if amax = 0), code = e4m3(x * (448/amax)) rounded to nearest even, saturating.
  *   k_new, v_new: [n_frames*T][H][D] in q_dtype (pre-RoPE K).  1 <= n_frames <= B_max.
  * LACT_E_STATE if pending >= r (compress first). */
 lact_status lact_kv_ring_append(lact_cache* cache, const void* k_new, const void* v_new,

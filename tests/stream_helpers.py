@@ -63,6 +63,8 @@ class Runner:
             res["out"], res["lse"] = out, lse_t
             if self.oc is not None and sel is not False:
                 res["ref"] = self.oc.attention(qh, kh, vh, block_frames=blocks, sel=sel, form=form)
+                if self.w["kv_dtype"] == FP8:
+                    res["hist_kmax"] = self._hist_kmax()
             res["q"], res["k"], res["v"] = qh, kh, vh
         self.cache.kv_ring_append(k, v)
         res["slots"] = self.cache.convkv_compress(self.d_wk, self.d_bk, self.d_wv, self.d_bv)
@@ -85,6 +87,38 @@ class Runner:
             lse = res["lse"].cpu().numpy()
             dl = float(np.abs(lse[heads, rows] - LSE).max())
         return err, dl
+
+    def _hist_kmax(self):
+        """Per head, the largest norm of a stored history key at the present state."""
+        from oracle.bookkeeping import SEG_MEMORY
+        kmax = np.zeros(self.H)
+        for kf in self.oc.keys(0):
+            if kf["segment"] == SEG_MEMORY:
+                sk = self.oc.mem[kf["slot"]][1]
+            else:
+                sk = self.oc.raw[kf["id"]][0]
+            vals, scales = self.oc.stored_value(sk)
+            n = np.linalg.norm(vals.astype(np.float64), axis=2)
+            if scales is not None:
+                n = n * scales
+            kmax = np.maximum(kmax, n.max(axis=0))
+        return kmax
+
+    def lse_bound(self, res):
+        """Per selected row, a bound on |dLSE| from bf16 operands: RoPE'd q and k are rounded
+        to bf16 (relative error <= 2^-9 per element), so every score moves by at most
+        2^-8 |q_i| |k_j| / sqrt(D) (Cauchy-Schwarz), and the LSE, 1-Lipschitz in the
+        max-norm of the scores, by at most the largest such move.  RoPE keeps norms, so the
+        norms of the unrotated stored / input vectors serve.  10% slack + 1e-4 for the f32
+        exp/log/sum arithmetic."""
+        O_, LSE_, heads, rows = res["ref"]
+        kmax = np.maximum(np.linalg.norm(res["k"], axis=2).max(axis=0), res["hist_kmax"])
+        qn = np.linalg.norm(res["q"][rows, heads, :].astype(np.float64), axis=1)
+        return 2.0 ** -8 * qn * kmax[heads] / np.sqrt(self.D) * 1.1 + 1e-4
+
+    def lse_errors(self, res):
+        O_, LSE_, heads, rows = res["ref"]
+        return np.abs(res["lse"].cpu().numpy()[heads, rows] - LSE_)
 
     def mem_slot_bytes(self, tensor, slot):
         """Raw bytes of memory slot `slot` of K (0) or V (1) as stored on the device."""

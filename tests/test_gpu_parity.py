@@ -12,7 +12,7 @@ from stream_helpers import BF16, F32, FP8, Runner, rel_l2, sample_rows
 pytestmark = pytest.mark.gpu
 
 ATTN_TOL = {F32: 1e-5, BF16: 1e-2, FP8: 5e-2}
-LSE_TOL = {F32: 1e-5, BF16: 2e-2, FP8: 1e-1}
+LSE_TOL = {F32: 1e-5, BF16: 2e-2}
 
 
 def say(msg):
@@ -130,6 +130,18 @@ def test_frame_id_tag_on_device(tap):
             assert val == 5 * g + tap, (g, val)
 
 
+def assert_lse(run, res, kv):
+    """FP8 workload (x8 outliers make scores large): the per-row bound that bf16 operand
+    rounding implies; otherwise the fixed bar."""
+    if kv == FP8:
+        dl, bound = run.lse_errors(res), run.lse_bound(res)
+        worst = int(np.argmax(dl / bound))
+        say(f"  dLSE/bound worst {dl[worst]:.3e} / {bound[worst]:.3e}")
+        assert np.all(dl <= bound)
+    else:
+        assert run.compare_attention(res)[1] <= LSE_TOL[kv]
+
+
 def _big_step_parity(name, warm, n_last, per_head=6, first_check=False):
     w = synth.workload(name)
     run = Runner(w)
@@ -142,7 +154,8 @@ def _big_step_parity(name, warm, n_last, per_head=6, first_check=False):
             res = run.step(n, sel=sel)
             err, dl = run.compare_attention(res)
             say(f"{name} step 1 ({n} frames, no history): rel L2 {err:.3e}, max dLSE {dl:.2e}")
-            assert err <= ATTN_TOL[kv] and dl <= LSE_TOL[kv]
+            assert err <= ATTN_TOL[kv]
+            assert_lse(run, res, kv)
             errs.append(err)
         else:
             run.step(n, attend=False)
@@ -154,7 +167,8 @@ def _big_step_parity(name, warm, n_last, per_head=6, first_check=False):
     res = run.step(n_last, sel=sel)
     err, dl = run.compare_attention(res)
     say(f"{name} step {warm + 1}: Lq {n_last * w['tokens']}, rel L2 {err:.3e}, max dLSE {dl:.2e}")
-    assert err <= ATTN_TOL[kv] and dl <= LSE_TOL[kv]
+    assert err <= ATTN_TOL[kv]
+    assert_lse(run, res, kv)
     return run
 
 
@@ -180,6 +194,46 @@ def test_fp8_append_compress_bitexact():
     assert_ring_bitexact(run)
 
 
+def test_fp8_kv_step_parity():
+    """512x512-shaped FP8 KV cache with 1% x8 outliers: first step (no history) and the
+    step after 11 warm-up blocks, attention over the stored e4m3 history against the oracle
+    on sampled rows of all 40 heads; ring and memory codes and scales bit-exact."""
+    _big_step_parity("fp8_kv", 11, 8, first_check=True)
+
+
+@pytest.mark.parametrize("blocks", [[1, 2, 3], [6]])
+def test_fp8_d128_multiblock_mask_vs_bruteforce(blocks):
+    """FP8 KV with D = 128 and T = 96 against the explicit mask matrix (several blocks)."""
+    w = synth.workload("fp8_kv", heads=4, grid_h=8, grid_w=12, window_frames=4,
+                       mem_slots=6, max_block_frames=6)
+    run = Runner(w)
+    for _ in range(9):
+        run.step(2, attend=False)
+    res = run.step(6, blocks=blocks, form=0)
+    err, dl = run.compare_attention(res)
+    say(f"fp8 d128 blocks {blocks}: rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert err <= ATTN_TOL[FP8], (blocks, err, dl)
+    assert_lse(run, res, FP8)
+
+
+def test_fp8_d64_small_stream():
+    """FP8 KV at D = 64, T = 16 (the generic kernel): 20 steps of the tiny schedule with
+    bf16 inputs, every step's attention against the oracle, state and memory bit-exact."""
+    w = synth.workload("tiny_f32", kv_dtype=FP8, q_dtype=BF16, outliers=True)
+    run = Runner(w)
+    worst = 0.0
+    for s in range(20):
+        res = run.step(2)
+        err, dl = run.compare_attention(res)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[FP8], (s, err, dl)
+        assert_lse(run, res, FP8)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    say(f"fp8 d64 stream: worst rel L2 {worst:.3e}")
+
+
 @pytest.mark.parametrize("blocks", [[1, 2, 3], [3, 3], [6], [2, 1, 1, 2]])
 def test_bf16_d128_multiblock_mask_vs_bruteforce(blocks):
     """D = 128 bf16 kernel with several query blocks per call and T = 96 (tiles of 32 keys
@@ -193,6 +247,36 @@ def test_bf16_d128_multiblock_mask_vs_bruteforce(blocks):
     err, dl = run.compare_attention(res)
     say(f"bf16 d128 blocks {blocks}: rel L2 {err:.3e}, max dLSE {dl:.2e}")
     assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16], (blocks, err, dl)
+
+
+def test_bf16_d128_reference_raise_in_kernel():
+    """A late key that every query prefers by ~60 nats (finite probabilities near 2^85 under
+    the first tile's reference): the fast pass raises its reference in-kernel, hands
+    nothing to the exact pass, and matches the oracle."""
+    w = synth.workload("s512_bf16", heads=2, grid_h=8, grid_w=8, window_frames=4,
+                       mem_slots=4, max_block_frames=4)
+    run = Runner(w)
+    for _ in range(6):
+        run.step(2, attend=False)
+    (q, qh), (k, kh), (v, vh) = run.inputs(4)
+    T = w["tokens"]
+    last = 4 * T - 1
+    qh[:, :, :] = np.abs(qh)
+    kh[last, :, :] = 7.0
+    q = torch.from_numpy(qh).to(torch.bfloat16).cuda()
+    k = torch.from_numpy(kh).to(torch.bfloat16).cuda()
+    qh, kh = q.float().cpu().numpy(), k.float().cpu().numpy()
+    run.cache.rope_reset_apply(q, k, v)
+    lse = torch.empty((w["heads"], 4 * T), dtype=torch.float32, device="cuda")
+    out = run.cache.block_attention(lse=lse)
+    flags = run.cache.buf[run.cache.layout.attn_flags:].view(torch.int32)[: w["heads"]].cpu().numpy()
+    ref = run.oc.attention(qh, kh, vh)
+    err, dl = run.compare_attention(dict(out=out, lse=lse, ref=ref))
+    say(f"reference raise: flags {flags.tolist()}, rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert flags.max() == 0, "the fast pass should have handled the large scores itself"
+    O_ref, LSE_ref, heads, rows = ref
+    assert err <= ATTN_TOL[BF16]
+    assert float(np.abs(lse.cpu().numpy()[heads, rows] - LSE_ref).max() / np.abs(LSE_ref).max()) <= 2e-3
 
 
 def test_bf16_d128_overflow_falls_back_to_exact_pass():

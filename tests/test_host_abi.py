@@ -43,8 +43,18 @@ def test_footprint_is_pure_and_matches_layout():
         assert lay.key_frames_max == w["mem_slots"] + w["window_frames"] + w["max_block_frames"]
         esize = {0: 4, 1: 2, 2: 1}[w["kv_dtype"]]
         assert lay.frame_bytes == w["tokens"] * w["channels"] * esize
-        offs = [getattr(lay, n) for n in ("ring_k", "ring_v", "mem_k", "mem_v", "krot", "qrot", "vcur")]
+        names = ("ring_k", "ring_v", "mem_k", "mem_v", "krot", "qrot", "vcur", "vhist")
+        offs = [getattr(lay, n) for n in names]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        # staged operands are in the q dtype; FP8 adds the dequantised history V
+        ob = w["tokens"] * w["channels"] * {0: 4, 1: 2}[w["q_dtype"]]
+        KF = lay.key_frames_max
+        assert lay.qrot - lay.krot >= ob * KF and lay.vcur - lay.qrot >= ob * w["max_block_frames"]
+        if w["kv_dtype"] == 2:
+            assert lay.vhist - lay.vcur >= ob * w["max_block_frames"]
+            assert lay.ring_k_scale - lay.vhist >= ob * (w["mem_slots"] + w["window_frames"])
+        else:
+            assert lay.ring_k_scale == 0 and lay.vhist == lay.rope_table
     # 512x512 bf16: 2R + 2M + KF + 2 B_max = 120 frames of 10 MiB, plus the small tables
     mib = L.lact_cache_footprint(_cfg("s512_bf16")) / 2 ** 20
     assert 1200 <= mib < 1201
