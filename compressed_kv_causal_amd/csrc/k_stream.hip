@@ -7,6 +7,8 @@
 // Work unit everywhere: one (token, head) row of D channels, handled by D/8 consecutive
 // lanes, 8 channels (16 bytes of bf16) per lane, so a wave reads and writes 64 x 16 B
 // contiguous segments; FP8 row scales come from a reduction over the row's lanes.
+#include <type_traits>
+
 #include "dev_common.hpp"
 
 namespace lact {
@@ -42,33 +44,98 @@ __global__ __launch_bounds__(256) void k_ring_write(const RingWriteArgs a) {
 // then stored in the cache dtype.  Each input frame is read once.
 // ---------------------------------------------------------------------------------------
 // Work split: a workgroup is one wave; lane = one 8-channel chunk of 64 consecutive chunks
-// (blockIdx.x), so a wave reads and writes 1 KiB contiguous per token; blockIdx.y = a run of
-// TOK tokens, blockIdx.z = (group, tensor).  The lane keeps its 8 x R weights and 8 biases
-// in registers across the tokens.  D/8 lanes form one (token, head) row, which is what
-// the FP8 row quantiser reduces over.
-template <int LPR, int R>
+// (blockIdx.x), so a wave reads and writes 1 KiB contiguous per token and frame (512 B for
+// FP8); blockIdx.y = a run of TOK tokens, blockIdx.z = (group, tensor).  D/8 lanes form one
+// (token, head) row, which is what the FP8 row quantiser reduces over.
+//
+// k_compress_r: the ratio is a compile-time R.  The lane keeps its 8 x R weights and 8
+// biases in registers and issues every load of its TOK tokens x R frames before the first
+// use, so a wave has TOK * R * 1 KiB in flight (a store to the memory slot cannot alias
+// the ring in this kernel, but the compiler cannot know that and would otherwise wait for
+// each token's loads in turn).
+template <int LPR, int R, int TOK, int KV>
+__global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
+  using Raw = typename std::conditional<KV == DT_FP8, uint2, uint4>::type;  // 8 stored elements
+  const int32_t C = a.H * a.D;
+  const int32_t c0 = (blockIdx.x * 64 + threadIdx.x) * 8;  // first channel of this lane
+  const int gi = blockIdx.z >> 1, tensor = blockIdx.z & 1;
+  if (c0 >= C) return;                                     // whole LPR groups leave together
+  const int32_t u0 = blockIdx.y * TOK;
+  const int32_t rows = a.T * a.H;
+  const char* ring = static_cast<const char*>(a.ring[tensor]);
+  constexpr int EB = KV == DT_FP8 ? 1 : 2;                 // stored bytes per element
+
+  Raw raw[TOK][R];
+  float sc[TOK][R];
+  int32_t slot[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    slot[k] = a.in_slot0[gi] + k;
+    if (slot[k] >= a.R) slot[k] -= a.R;
+  }
+#pragma unroll
+  for (int t = 0; t < TOK; ++t) {
+    const int32_t u = u0 + t < a.T ? u0 + t : a.T - 1;     // tail tokens repeat the last one
+    const int32_t hrow = u * a.H + c0 / a.D;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int64_t el = (int64_t)slot[k] * a.T * C + (int64_t)u * C + c0;
+      raw[t][k] = *reinterpret_cast<const Raw*>(ring + el * EB);
+      sc[t][k] = KV == DT_FP8 ? a.ring_scale[tensor][(int64_t)slot[k] * rows + hrow] : 1.0f;
+    }
+  }
+  float w[8][R], b[8];
+  const float* wp = a.w[tensor] + (int64_t)c0 * R;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    b[e] = a.b[tensor][c0 + e];
+#pragma unroll
+    for (int k = 0; k < R; ++k) w[e][k] = wp[e * R + k];
+  }
+#pragma unroll
+  for (int t = 0; t < TOK; ++t) {
+    const int32_t u = u0 + t;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = b[e];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      float x[8];
+      if (KV == DT_FP8) {
+        const uint32_t wd[2] = {raw[t][k].x, raw[t][k].y};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = e4m3_to_f32((wd[e / 4] >> (8 * (e % 4))) & 0xFFu) * sc[t][k];
+      } else {
+        const uint4 v = reinterpret_cast<const uint4&>(raw[t][k]);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32((uint16_t)(wd[e / 2] >> (16 * (e % 2))));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[e][k], x[e], acc[e]);
+    }
+    if (u >= a.T) continue;        // uniform per LPR group: a row's lanes share u
+    const int64_t dst = (int64_t)a.out_slot[gi] * a.T * C + (int64_t)u * C + c0;
+    const float s = store8_kv<LPR>(a.mem[tensor], KV, dst, acc);
+    if (KV == DT_FP8 && (threadIdx.x % LPR) == 0)
+      a.mem_scale[tensor][(int64_t)a.out_slot[gi] * rows + u * a.H + c0 / a.D] = s;
+  }
+}
+
+// k_compress: any ratio and the f32 cache; tokens one after another.
+template <int LPR>
 __global__ __launch_bounds__(64) void k_compress(const CompressArgs a) {
   constexpr int TOK = 16;
   const int32_t C = a.H * a.D;
   const int32_t c0 = (blockIdx.x * 64 + threadIdx.x) * 8;  // first channel of this lane
   const int gi = blockIdx.z >> 1, tensor = blockIdx.z & 1;
-  const bool active = c0 < C;                              // whole LPR groups are (in)active together
-  const int32_t r = R > 0 ? R : a.r;
-  float w[8][R > 0 ? R : 1], b[8];
-  if (active) {
-    const float* wp = a.w[tensor] + (int64_t)c0 * r;
+  if (c0 >= C) return;
+  const int32_t r = a.r;
+  float b[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      b[e] = a.b[tensor][c0 + e];
-      if (R > 0) {
-#pragma unroll
-        for (int k = 0; k < R; ++k) w[e][k] = wp[e * R + k];
-      }
-    }
-  }
+  for (int e = 0; e < 8; ++e) b[e] = a.b[tensor][c0 + e];
   const int32_t u0 = blockIdx.y * TOK;
   for (int32_t u = u0; u < u0 + TOK && u < a.T; ++u) {
-    if (!active) continue;
     const int64_t el = (int64_t)u * C + c0;                // element offset inside a frame
     const int32_t hrow = u * a.H + c0 / a.D;               // (token, head) row inside a frame
     float acc[8];
@@ -81,10 +148,7 @@ __global__ __launch_bounds__(64) void k_compress(const CompressArgs a) {
       float x[8];
       load8_kv(a.ring[tensor], a.kv_dtype, (int64_t)slot * a.T * C + el, sc, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float wk = R > 0 ? w[e][R > 0 ? k : 0] : a.w[tensor][(int64_t)(c0 + e) * r + k];
-        acc[e] = fmaf(wk, x[e], acc[e]);
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(a.w[tensor][(int64_t)(c0 + e) * r + k], x[e], acc[e]);
     }
     const int64_t dst = (int64_t)a.out_slot[gi] * a.T * C + el;
     const float s = store8_kv<LPR>(a.mem[tensor], a.kv_dtype, dst, acc);
@@ -233,18 +297,28 @@ hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n_groups <= 0) return hipSuccess;
   const int32_t chunks = a.H * a.D / 8;
-  dim3 grid((chunks + 63) / 64, (a.T + 15) / 16, 2 * a.n_groups);
-  if (a.D == 128) {
-    if (a.r == 5)
-      hipLaunchKernelGGL((k_compress<16, 5>), grid, dim3(64), 0, s, a);
+  constexpr int TOK = 4;
+  if (a.D == 128 && a.r == 5 && a.kv_dtype != DT_F32) {
+    dim3 grid((chunks + 63) / 64, (a.T + TOK - 1) / TOK, 2 * a.n_groups);
+    if (a.kv_dtype == DT_BF16)
+      hipLaunchKernelGGL((k_compress_r<16, 5, TOK, DT_BF16>), grid, dim3(64), 0, s, a);
     else
-      hipLaunchKernelGGL((k_compress<16, 0>), grid, dim3(64), 0, s, a);
-  } else {
-    if (a.r == 5)
-      hipLaunchKernelGGL((k_compress<8, 5>), grid, dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_compress<8, 0>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((k_compress_r<16, 5, TOK, DT_FP8>), grid, dim3(64), 0, s, a);
+    return hipGetLastError();
   }
+  if (a.D == 64 && a.r == 5 && a.kv_dtype != DT_F32) {
+    dim3 grid((chunks + 63) / 64, (a.T + TOK - 1) / TOK, 2 * a.n_groups);
+    if (a.kv_dtype == DT_BF16)
+      hipLaunchKernelGGL((k_compress_r<8, 5, TOK, DT_BF16>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_compress_r<8, 5, TOK, DT_FP8>), grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
+  dim3 grid((chunks + 63) / 64, (a.T + 15) / 16, 2 * a.n_groups);
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_compress<16>, grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_compress<8>, grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
