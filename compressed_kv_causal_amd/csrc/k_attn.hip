@@ -237,8 +237,13 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
 //   * V^T fragments come from the transposing LDS read: within each 16-lane group, lanes
 //     4t..4t+3 address key row t (16 consecutive channels) and lane i receives channel i
 //     of rows 0..3 -- the consecutive keys of one channel the MFMA A operand needs.
-//   * V rows are read where they are stored (memory slot, raw ring or the staged block):
-//     a per-key-frame byte-offset table in LDS plus per-lane (frame, token) cursors.
+//   * Addressing costs almost no VALU work per tile.  Copies: the tile's first key frame
+//     and token and the V bases of that frame and the next (memory slot, raw ring slot or
+//     staged block frame) are scalar state; a lane adds its constant row offset to one of
+//     the two (a 64-key tile spans at most two frames since T >= 64).  Fragment reads: the
+//     per-lane LDS offsets of all K and V^T fragments are loop invariants; the ring slot
+//     and the fragment's key block or chunk are the instruction's immediate offset, with
+//     the unmasked tile loop unrolled by NS so the slot is a compile-time constant.
 //   * Softmax with a lazily raised reference: m = the row's max over the first key tile.
 //     Every later probability is exp2(s * log2(e)/sqrt(D) - m), so there is no running
 //     max and no per-tile rescale of O; since m never exceeds the true row max, terms are
@@ -252,78 +257,115 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
 namespace d128 {
 
 constexpr int D = 128, BM = 256, BN = 64, NS = 4, WAVES = 8;
-constexpr int TILE_BYTES = BN * D * 2;  // 16 KiB
-constexpr int VMEM_PER_TILE = 4;        // copy instructions per wave per tile (K 2, V 2)
+constexpr int ROW_BYTES = D * 2;
+constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
+constexpr int V_RING = NS * TILE_BYTES;     // V slots follow the K slots in LDS
+constexpr int VMEM_PER_TILE = 4;            // copy instructions per wave per tile (K 2, V 2)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// One 1 KiB global -> LDS copy per wave (16 B per lane, lane l lands at lds_row0 + 16 l).
-// Issued through inline asm with M0 = the LDS address: the compiler then does not treat it
-// as an LDS write it must wait for before every later LDS read (it would insert vmcnt(0)
-// right after the copy and the prefetch would never overlap); the ring's own
+// One 1 KiB global -> LDS copy per wave (16 B per lane, lane l lands at LDS address
+// m0 + 16 l; m0 is wave-uniform).  Issued through inline asm: the compiler then does not
+// treat it as an LDS write it must wait for before every later LDS read (it would insert
+// vmcnt(0) right after the copy and the prefetch would never overlap); the ring's own
 // "s_waitcnt vmcnt + barrier" orders the copies with the reads.  No VGPR is written.
-__device__ __forceinline__ void copy_to_lds(const void* src, char* lds_row0) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds_row0);
+__device__ __forceinline__ void copy_to_lds(const void* src, unsigned m0) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
-// Per-lane source cursor of one 4-row group of a tile: the key row this lane copies.
-struct Cursor {
-  int r;        // row inside the tile
-  int fi, u;    // key frame and token of that row in the next tile to copy
+// The scalars the copies need, as plain values (the kernel's argument block stays in the
+// constant kernarg segment: taking a field by a computed offset would make the compiler
+// copy the whole block into scratch memory and every use of it per-lane).
+struct Geo {
+  const char* v_mem;
+  const char* v_ring;
+  const char* v_cur;
+  int64_t frame_bytes;  // one V frame, T * H * D * 2
+  int T, Lk, nf, mem_len, nh, M, R, mem_slot0, ring_slot0;
 };
+
+// V base address of key frame f of [memory | window | block] (frames past the end repeat
+// the last one, so copies issued past the end read finite data inside the buffers).
+__device__ __forceinline__ const char* frame_base(const Geo& g, int f) {
+  f = f < g.nf ? f : g.nf - 1;
+  int ms = g.mem_slot0 + f;
+  ms = ms >= g.M ? ms - g.M : ms;
+  int rs = g.ring_slot0 + (f - g.mem_len);
+  rs = rs >= g.R ? rs - g.R : rs;
+  const char* mb = g.v_mem + ms * g.frame_bytes;
+  const char* rb = g.v_ring + rs * g.frame_bytes;
+  const char* cb = g.v_cur + (f - g.nh) * g.frame_bytes;
+  return f < g.mem_len ? mb : (f < g.nh ? rb : cb);
+}
 
 struct Ctx {
-  const AttnArgs* a;
-  const uint16_t* kbase;  // this head's rotated keys [Lk][128]
-  const char* vbase;      // origin of the V byte offsets
-  const int64_t* fbase;   // V byte offset of every key frame
+  Geo g;
+  const char* kbase;  // this head's rotated keys [Lk][128]
   char* lds;
+  unsigned lds_u32;   // LDS address of the ring (for M0)
   int h, wave, lane, hi, lr, kvis;
   float scale;
+  int64_t hrow;       // bytes between consecutive tokens of one V frame (H * D * 2)
+  // copies: the two 4-row groups of a tile this lane copies
+  int crow[2];        // row inside the tile
+  int koff[2];        // crow * 256 + chunk * 16 (bytes from the tile's first K row)
+  int voff[2];        // (crow * H + h) * 256 + chunk * 16 (bytes from the V row of token 0)
+  // fragment reads: LDS byte offsets from the ring base (slot 0)
+  int kread[8];       // K fragment kk of key block 0 (+ 8 KiB for block 1)
+  int vread[4][2];    // the two transposed reads of V^T fragment db, chunk 0 (+ 4 KiB per chunk)
 };
 
-// Copy tile t's 64 key rows of K and V into ring slot t % NS (each wave: 8 rows as two
-// 4-row groups), then advance the V cursors by one tile.
-__device__ __forceinline__ void issue(const Ctx& c, int t, Cursor (&cur)[2]) {
-  const AttnArgs& a = *c.a;
-  char* kdst = c.lds + (t % NS) * TILE_BYTES;
-  char* vdst = c.lds + (NS + t % NS) * TILE_BYTES;
+// Scalar stream state of the copies: frame and token of the first key of the next tile,
+// and the V bases of that frame and the next (recomputed when a tile crosses a frame).
+struct Stream {
+  int f0, u0;
+  const char* baseA;
+  const char* baseB;
+};
+
+// Copy tile t's 64 key rows of K and V into ring slot t % NS, then advance the stream.
+__device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
+  const Geo& a = c.g;
+  const unsigned slot = (unsigned)(t % NS);
+  const unsigned kdst = c.lds_u32 + slot * TILE_BYTES + (unsigned)c.wave * 8 * ROW_BYTES;
+  const unsigned vdst = kdst + V_RING;
+  if ((t + 1) * BN <= a.Lk) {
+    const char* ktile = c.kbase + (int64_t)t * TILE_BYTES;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r0 = c.wave * 8 + i * 4;
-    const int chunk = (c.lane & 15) ^ swz(cur[i].r);
-    int key = t * BN + cur[i].r;
-    key = key < a.Lk ? key : a.Lk - 1;
-    copy_to_lds(c.kbase + (int64_t)key * D + chunk * 8, kdst + r0 * 256);
-    const char* vsrc = c.vbase + c.fbase[cur[i].fi] + (((int64_t)cur[i].u * a.H + c.h) * D + chunk * 8) * 2;
-    copy_to_lds(vsrc, vdst + r0 * 256);
-    const int nu = cur[i].u + BN;  // T >= BN: at most one wrap into the next frame per tile
-    const int wrap = nu >= a.T ? 1 : 0;
-    cur[i].u = nu - wrap * a.T;
-    cur[i].fi += wrap;
+    for (int i = 0; i < 2; ++i) copy_to_lds(ktile + c.koff[i], kdst + i * 4 * ROW_BYTES);
+  } else {  // rows past the last key repeat it
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int key = t * BN + c.crow[i];
+      key = key < a.Lk ? key : a.Lk - 1;
+      copy_to_lds(c.kbase + (int64_t)key * ROW_BYTES + (c.koff[i] & (ROW_BYTES - 1)), kdst + i * 4 * ROW_BYTES);
+    }
+  }
+  const char* vA = st.baseA + st.u0 * c.hrow;
+  if (st.u0 + BN <= a.T) {  // the whole tile lies in frame f0
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy_to_lds(vA + c.voff[i], vdst + i * 4 * ROW_BYTES);
+  } else {
+    const char* vB = st.baseB + (st.u0 - a.T) * c.hrow;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      copy_to_lds((st.u0 + c.crow[i] >= a.T ? vB : vA) + c.voff[i], vdst + i * 4 * ROW_BYTES);
+  }
+  st.u0 += BN;  // T >= BN: at most one frame boundary per tile
+  if (st.u0 >= a.T) {
+    st.u0 -= a.T;
+    st.f0 += 1;
+    st.baseA = st.baseB;
+    st.baseB = frame_base(c.g, st.f0 + 1);
   }
 }
 
-// V^T fragment (16 keys of chunk ch, channels 32 db .. 32 db + 31) from vb.
-__device__ __forceinline__ bf16x8_t vfrag(const char* vb, int lane, int hi, int ch, int db) {
-  const int g = lane >> 4, i = lane & 15;
-  const int row = ch * 16 + hi * 8 + (i >> 2);
-  const int chunk = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
-  const int half = (i & 1) * 8;
-  const char* p0 = vb + row * 256 + ((chunk ^ swz(row)) * 16) + half;
-  const char* p1 = vb + (row + 4) * 256 + ((chunk ^ swz(row + 4)) * 16) + half;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
-  const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
-  bf16x8_t vf;
-  __builtin_memcpy(&vf, &lo, 8);
-  __builtin_memcpy(reinterpret_cast<char*>(&vf) + 8, &up, 8);
-  return vf;
-}
+// LDS address helpers: SLOT >= 0 is a compile-time ring slot, SLOT < 0 takes tile j's.
+template <int SLOT>
+__device__ __forceinline__ int slot_of(int j) { return SLOT >= 0 ? SLOT : j % NS; }
 
 template <bool MASK>
 __device__ __forceinline__ void mask_block(f32x16_t& s, int key0, int hi, int kvis) {
@@ -337,22 +379,30 @@ __device__ __forceinline__ void mask_block(f32x16_t& s, int key0, int hi, int kv
 }
 
 // S^T of one 64-key tile (two 32-key blocks) from the K rows in LDS, masked.
-template <bool MASK>
-__device__ __forceinline__ void qk_tile(const Ctx& c, int j, const char* kb, const bf16x8_t (&qf)[8],
-                                        f32x16_t (&s)[2]) {
+template <bool MASK, int SLOT>
+__device__ __forceinline__ void qk_tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&s)[2]) {
+  const char* kb = c.lds + slot_of<SLOT>(j) * TILE_BYTES;
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
     s[kb2] = f32x16_t{};
-    const int m = kb2 * 32 + perm32(c.lr);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const int pos = (2 * kk + c.hi) ^ swz(m);
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(kb + m * 256 + pos * 16);
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(kb + c.kread[kk] + kb2 * 32 * ROW_BYTES);
       s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[kb2], 0, 0, 0);
     }
   }
   mask_block<MASK>(s[0], j * BN, c.hi, c.kvis);
   mask_block<MASK>(s[1], j * BN + 32, c.hi, c.kvis);
+}
+
+// V^T fragment (16 keys of chunk ch, channels 32 db .. 32 db + 31).
+__device__ __forceinline__ bf16x8_t vfrag(const char* vb, const Ctx& c, int ch, int db) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + c.vread[db][0] + ch * 16 * ROW_BYTES));
+  const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + c.vread[db][1] + ch * 16 * ROW_BYTES));
+  bf16x8_t vf;
+  __builtin_memcpy(&vf, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&vf) + 8, &up, 8);
+  return vf;
 }
 
 // p = exp2(s * scale - m_ref) in place; returns this lane's sum of the 32 probabilities.
@@ -381,14 +431,13 @@ __device__ __forceinline__ float exp_tile(f32x16_t (&s)[2], float scale, float m
 // outliers take it a few times per row at most.  A probability that is already infinite
 // (a score >= 128 above the reference) cannot be rescaled: l and O become infinite and the
 // workgroup hands its rows to the exact pass.
-template <bool MASK, bool FIRST>
+template <bool MASK, bool FIRST, int SLOT>
 __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&o)[4],
-                                     float& m_ref, float& l_part, Cursor (&cur)[2]) {
-  const char* kb = c.lds + (j % NS) * TILE_BYTES;
-  const char* vb = c.lds + (NS + j % NS) * TILE_BYTES;
-  issue(c, j + NS - 1, cur);
+                                     float& m_ref, float& l_part, Stream& st) {
+  const char* vb = c.lds + slot_of<SLOT>(j) * TILE_BYTES;  // + vread (which holds V_RING)
+  issue(c, j + NS - 1, st);
   f32x16_t s[2];
-  qk_tile<MASK>(c, j, kb, qf, s);
+  qk_tile<MASK, SLOT>(c, j, qf, s);
   if (FIRST) {
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
@@ -425,7 +474,7 @@ __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8
   for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vb, c.lane, c.hi, ch, db), p[ch], o[db], 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vb, c, ch, db), p[ch], o[db], 0, 0, 0);
   static_assert((NS - 2) * VMEM_PER_TILE == 8, "the wait count below assumes 4 stages");
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   __syncthreads();
@@ -436,7 +485,6 @@ __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8
 __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   using namespace d128;
   __shared__ __align__(1024) char lds[2 * NS * TILE_BYTES];
-  __shared__ int64_t fbase[LACT_MAX_KEY_FRAMES + NS + 2];
 
   // XCD-aware mapping: workgroup id b runs on XCD b % 8; give each XCD a contiguous range
   // of (head, query tile) items so one head's tiles run on one XCD together.
@@ -449,30 +497,53 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   const int h = item / n_qt, qt = item - h * n_qt;
 
   Ctx c;
-  c.a = &a;
+  c.g.v_mem = static_cast<const char*>(a.v_mem);
+  c.g.v_ring = static_cast<const char*>(a.v_ring);
+  c.g.v_cur = static_cast<const char*>(a.v_cur);
+  c.g.frame_bytes = (int64_t)a.T * a.H * ROW_BYTES;
+  c.g.T = a.T;
+  c.g.Lk = a.Lk;
+  c.g.nf = a.Lk / a.T;
+  c.g.mem_len = a.hist.mem_len;
+  c.g.nh = a.hist.mem_len + a.hist.win_len;
+  c.g.M = a.hist.M;
+  c.g.R = a.hist.R;
+  c.g.mem_slot0 = a.hist.mem_slot0;
+  c.g.ring_slot0 = a.hist.ring_slot0;
   c.h = h;
-  c.wave = threadIdx.x >> 6;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   c.lane = threadIdx.x & 63;
   c.hi = c.lane >> 5;
   c.lr = c.lane & 31;
   c.lds = lds;
-  c.fbase = fbase;
-  c.kbase = static_cast<const uint16_t*>(a.k) + (int64_t)h * a.k_head_stride;
-  c.vbase = static_cast<const char*>(a.v_ring);
+  c.lds_u32 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  c.kbase = static_cast<const char*>(a.k) + (int64_t)h * a.k_head_stride * 2;
   c.scale = a.scale_log2;
+  c.hrow = (int64_t)a.H * ROW_BYTES;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = c.wave * 8 + i * 4 + (c.lane >> 4);
+    const int chunk = (c.lane & 15) ^ swz(r);
+    c.crow[i] = r;
+    c.koff[i] = r * ROW_BYTES + chunk * 16;
+    c.voff[i] = (r * a.H + h) * ROW_BYTES + chunk * 16;
+  }
+  {
+    const int m = perm32(c.lr);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) c.kread[kk] = m * ROW_BYTES + (((2 * kk + c.hi) ^ swz(m)) * 16);
+    const int g = c.lane >> 4, i = c.lane & 15;
+    const int row = c.hi * 8 + (i >> 2);
+    const int half = (i & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int chunk = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
+      c.vread[db][0] = V_RING + row * ROW_BYTES + ((chunk ^ swz(row)) * 16) + half;
+      c.vread[db][1] = V_RING + (row + 4) * ROW_BYTES + ((chunk ^ swz(row + 4)) * 16) + half;
+    }
+  }
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.q_head_stride;
   const int q0 = qt * BM;
-
-  // byte offset (from the raw ring) of every key frame's V; spare entries repeat the last
-  // frame so that rows past Lk (last tile, and the copies issued past the end) read
-  // finite data inside the buffer (a tile is 64 <= T rows, so NS + 2 spares suffice)
-  const int n_frames = a.Lk / a.T;
-  for (int fi = threadIdx.x; fi < n_frames + NS + 2; fi += blockDim.x) {
-    const int f = fi < n_frames ? fi : n_frames - 1;
-    int32_t w;
-    const int64_t off = v_row_off(a, f * a.T, 0, &w);
-    fbase[fi] = (reinterpret_cast<const char*>(v_base<uint16_t>(a, w)) - c.vbase) + off * 2;
-  }
 
   const int row = q0 + c.wave * 32 + c.lr;
   const int rr = row < a.Lq ? row : a.Lq - 1;
@@ -492,25 +563,26 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
   float m_ref = 0.0f, l_part = 0.0f;
-  Cursor cur[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    cur[i].r = c.wave * 8 + i * 4 + (c.lane >> 4);
-    cur[i].fi = cur[i].r / a.T;
-    cur[i].u = cur[i].r - cur[i].fi * a.T;
-  }
-  __syncthreads();  // fbase ready
-  for (int t = 0; t < NS - 1; ++t) issue(c, t, cur);
+  Stream st{0, 0, frame_base(c.g, 0), frame_base(c.g, 1)};
+  for (int t = 0; t < NS - 1; ++t) issue(c, t, st);
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile 0 landed
   __syncthreads();
 
   if (n_free > 0)
-    tile<false, true>(c, 0, qf, o, m_ref, l_part, cur);
+    tile<false, true, 0>(c, 0, qf, o, m_ref, l_part, st);
   else
-    tile<true, true>(c, 0, qf, o, m_ref, l_part, cur);
+    tile<true, true, 0>(c, 0, qf, o, m_ref, l_part, st);
   int j = 1;
-  for (; j < n_free && j < nt; ++j) tile<false, false>(c, j, qf, o, m_ref, l_part, cur);
-  for (; j < nt; ++j) tile<true, false>(c, j, qf, o, m_ref, l_part, cur);
+  const int free_end = n_free < nt ? n_free : nt;
+  static_assert(NS == 4, "the unrolled loop below walks the slots 1, 2, 3, 0");
+  for (; j + 4 <= free_end; j += 4) {
+    tile<false, false, 1>(c, j, qf, o, m_ref, l_part, st);
+    tile<false, false, 2>(c, j + 1, qf, o, m_ref, l_part, st);
+    tile<false, false, 3>(c, j + 2, qf, o, m_ref, l_part, st);
+    tile<false, false, 0>(c, j + 3, qf, o, m_ref, l_part, st);
+  }
+  for (; j < free_end; ++j) tile<false, false, -1>(c, j, qf, o, m_ref, l_part, st);
+  for (; j < nt; ++j) tile<true, false, -1>(c, j, qf, o, m_ref, l_part, st);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
 
   const float l = l_part + __shfl_xor(l_part, 32);
