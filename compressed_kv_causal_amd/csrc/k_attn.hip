@@ -378,18 +378,39 @@ __device__ __forceinline__ void mask_block(f32x16_t& s, int key0, int hi, int kv
   }
 }
 
-// S^T of one 64-key tile (two 32-key blocks) from the K rows in LDS, masked.
+// Scheduling fence between pipeline steps (no instruction crosses it): without it the
+// compiler moves each MFMA up next to its fragment read and reuses one fragment register,
+// exposing the full LDS latency on every MFMA.
+__device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// S^T of one 64-key tile (two 32-key blocks) from the K rows in LDS, masked.  The two
+// key blocks are independent MFMA chains, interleaved; K fragments are read three steps
+// ahead of their MFMAs.
 template <bool MASK, int SLOT>
 __device__ __forceinline__ void qk_tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&s)[2]) {
   const char* kb = c.lds + slot_of<SLOT>(j) * TILE_BYTES;
+  auto kfrag = [&](int kk, int kb2) {
+    return *reinterpret_cast<const bf16x8_t*>(kb + c.kread[kk] + kb2 * 32 * ROW_BYTES);
+  };
+  constexpr int AHEAD = 3;  // steps of two MFMAs (64 cycles) between a read and its use
+  bf16x8_t kf[AHEAD + 1][2];
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    s[kb2] = f32x16_t{};
+  for (int kk = 0; kk < AHEAD; ++kk) {
+    kf[kk][0] = kfrag(kk, 0);
+    kf[kk][1] = kfrag(kk, 1);
+  }
+  step_fence();
+  s[0] = f32x16_t{};
+  s[1] = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(kb + c.kread[kk] + kb2 * 32 * ROW_BYTES);
-      s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[kb2], 0, 0, 0);
+  for (int kk = 0; kk < 8; ++kk) {
+    if (kk + AHEAD < 8) {
+      kf[(kk + AHEAD) % (AHEAD + 1)][0] = kfrag(kk + AHEAD, 0);
+      kf[(kk + AHEAD) % (AHEAD + 1)][1] = kfrag(kk + AHEAD, 1);
     }
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % (AHEAD + 1)][0], qf[kk], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % (AHEAD + 1)][1], qf[kk], s[1], 0, 0, 0);
+    step_fence();
   }
   mask_block<MASK>(s[0], j * BN, c.hi, c.kvis);
   mask_block<MASK>(s[1], j * BN + 32, c.hi, c.kvis);
@@ -470,11 +491,19 @@ __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8
   for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
     for (int t = 0; t < 8; ++t) p[ch][t] = (__bf16)s[ch >> 1][8 * (ch & 1) + t];
+  // O^T += V^T P^T: 16 MFMAs (chunk ch, channel block db) in 4 independent chains, V^T
+  // fragments read four MFMAs (128 cycles) ahead
+  constexpr int VAHEAD = 4;
+  bf16x8_t vf[VAHEAD + 1];
 #pragma unroll
-  for (int ch = 0; ch < 4; ++ch)
+  for (int i = 0; i < VAHEAD; ++i) vf[i] = vfrag(vb, c, i >> 2, i & 3);
+  step_fence();
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vb, c, ch, db), p[ch], o[db], 0, 0, 0);
+  for (int i = 0; i < 16; ++i) {
+    if (i + VAHEAD < 16) vf[(i + VAHEAD) % (VAHEAD + 1)] = vfrag(vb, c, (i + VAHEAD) >> 2, (i + VAHEAD) & 3);
+    o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (VAHEAD + 1)], p[i >> 2], o[i & 3], 0, 0, 0);
+    step_fence();
+  }
   static_assert((NS - 2) * VMEM_PER_TILE == 8, "the wait count below assumes 4 stages");
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   __syncthreads();
