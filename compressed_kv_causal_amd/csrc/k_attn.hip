@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float v = s[kb][j] * a.scale_log2;
+        float v = s[kb][j];
         if (need_mask) {
           const int key = k0 + kb * 32 + perm32(((j >> 2) << 3) + (hi << 2) + (j & 3));
           if (key >= kvis) v = -INFINITY;
@@ -245,8 +245,11 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
 //     and the fragment's key block or chunk are the instruction's immediate offset, with
 //     the unmasked tile loop unrolled by NS so the slot is a compile-time constant.
 //   * Softmax with a lazily raised reference: m = the row's max over the first key tile.
-//     Every later probability is exp2(s * log2(e)/sqrt(D) - m), so there is no running
-//     max and no per-tile rescale of O; since m never exceeds the true row max, terms are
+//     The staged queries carry log2(e)/sqrt(D), and every QK^T MFMA chain starts from the
+//     broadcast -m instead of 0, so the chain's output q.k - m is already the base-2
+//     exponent of the probability: the softmax spends one v_exp per score and nothing
+//     else.  There is no running max and no per-tile rescale of O; since m never exceeds
+//     the true row max, terms are
 //     only ever too large, never lost.  Only when a lane's tile sum reaches 2^64 (scores
 //     far above m, e.g. from outlier channels) does the wave raise m by a power of two and
 //     scale O and l exactly (see tile()).  If l or O still ends up not finite, the
@@ -307,7 +310,6 @@ struct Ctx {
   char* lds;
   unsigned lds_u32;   // LDS address of the ring (for M0)
   int h, wave, lane, hi, lr, kvis;
-  float scale;
   int64_t hrow;       // bytes between consecutive tokens of one V frame (H * D * 2)
   // copies: the two 4-row groups of a tile this lane copies
   int crow[2];        // row inside the tile
@@ -383,11 +385,13 @@ __device__ __forceinline__ void mask_block(f32x16_t& s, int key0, int hi, int kv
 // exposing the full LDS latency on every MFMA.
 __device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// S^T of one 64-key tile (two 32-key blocks) from the K rows in LDS, masked.  The two
-// key blocks are independent MFMA chains, interleaved; K fragments are read three steps
-// ahead of their MFMAs.
+// S^T of one 64-key tile (two 32-key blocks) from the K rows in LDS, masked, on top of
+// `init` (the broadcast -m_ref of the lane's row: the chains then produce the exponents
+// of the probabilities directly).  The two key blocks are independent MFMA chains,
+// interleaved; K fragments are read three steps ahead of their MFMAs.
 template <bool MASK, int SLOT>
-__device__ __forceinline__ void qk_tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&s)[2]) {
+__device__ __forceinline__ void qk_tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], const f32x16_t& init,
+                                        f32x16_t (&s)[2]) {
   const char* kb = c.lds + slot_of<SLOT>(j) * TILE_BYTES;
   auto kfrag = [&](int kk, int kb2) {
     return *reinterpret_cast<const bf16x8_t*>(kb + c.kread[kk] + kb2 * 32 * ROW_BYTES);
@@ -400,8 +404,8 @@ __device__ __forceinline__ void qk_tile(const Ctx& c, int j, const bf16x8_t (&qf
     kf[kk][1] = kfrag(kk, 1);
   }
   step_fence();
-  s[0] = f32x16_t{};
-  s[1] = f32x16_t{};
+  s[0] = init;
+  s[1] = init;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     if (kk + AHEAD < 8) {
@@ -426,14 +430,16 @@ __device__ __forceinline__ bf16x8_t vfrag(const char* vb, const Ctx& c, int ch, 
   return vf;
 }
 
-// p = exp2(s * scale - m_ref) in place; returns this lane's sum of the 32 probabilities.
-__device__ __forceinline__ float exp_tile(f32x16_t (&s)[2], float scale, float m_ref) {
+// p = exp2(s - sub) in place (sub = 0 when s already holds the exponents); returns this
+// lane's sum of the 32 probabilities.
+template <bool SUB>
+__device__ __forceinline__ float exp_tile(f32x16_t (&s)[2], float sub) {
   float sum = 0.0f;
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[kb2][r], scale, -m_ref));
+      const float e = __builtin_amdgcn_exp2f(SUB ? s[kb2][r] - sub : s[kb2][r]);
       s[kb2][r] = e;
       sum += e;
     }
@@ -454,18 +460,23 @@ __device__ __forceinline__ float exp_tile(f32x16_t (&s)[2], float scale, float m
 // workgroup hands its rows to the exact pass.
 template <bool MASK, bool FIRST, int SLOT>
 __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&o)[4],
-                                     float& m_ref, float& l_part, Stream& st) {
+                                     float& m_ref, f32x16_t& negm, float& l_part, Stream& st) {
   const char* vb = c.lds + slot_of<SLOT>(j) * TILE_BYTES;  // + vread (which holds V_RING)
   issue(c, j + NS - 1, st);
   f32x16_t s[2];
-  qk_tile<MASK, SLOT>(c, j, qf, s);
+  qk_tile<MASK, SLOT>(c, j, qf, negm, s);  // tile 0: negm = 0
+  float sum;
   if (FIRST) {
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    m_ref = fmaxf(mx, __shfl_xor(mx, 32)) * c.scale;
+    m_ref = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
+    sum = exp_tile<true>(s, m_ref);
+  } else {
+    sum = exp_tile<false>(s, 0.0f);
   }
-  float sum = exp_tile(s, c.scale, m_ref);
   if (!FIRST && __builtin_expect(__any(!(sum < 0x1p64f)), 0)) {
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
@@ -484,6 +495,8 @@ __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8
     l_part = __builtin_ldexpf(l_part, -e);
     sum = __builtin_ldexpf(sum, -e);
     m_ref += (float)e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
   }
   l_part += sum;
   bf16x8_t p[4];
@@ -547,7 +560,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   c.lds = lds;
   c.lds_u32 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   c.kbase = static_cast<const char*>(a.k) + (int64_t)h * a.k_head_stride * 2;
-  c.scale = a.scale_log2;
   c.hrow = (int64_t)a.H * ROW_BYTES;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -592,26 +604,27 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
   float m_ref = 0.0f, l_part = 0.0f;
+  f32x16_t negm = f32x16_t{};  // -m_ref in every element (the QK^T chains' starting value)
   Stream st{0, 0, frame_base(c.g, 0), frame_base(c.g, 1)};
   for (int t = 0; t < NS - 1; ++t) issue(c, t, st);
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile 0 landed
   __syncthreads();
 
   if (n_free > 0)
-    tile<false, true, 0>(c, 0, qf, o, m_ref, l_part, st);
+    tile<false, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st);
   else
-    tile<true, true, 0>(c, 0, qf, o, m_ref, l_part, st);
+    tile<true, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st);
   int j = 1;
   const int free_end = n_free < nt ? n_free : nt;
   static_assert(NS == 4, "the unrolled loop below walks the slots 1, 2, 3, 0");
   for (; j + 4 <= free_end; j += 4) {
-    tile<false, false, 1>(c, j, qf, o, m_ref, l_part, st);
-    tile<false, false, 2>(c, j + 1, qf, o, m_ref, l_part, st);
-    tile<false, false, 3>(c, j + 2, qf, o, m_ref, l_part, st);
-    tile<false, false, 0>(c, j + 3, qf, o, m_ref, l_part, st);
+    tile<false, false, 1>(c, j, qf, o, m_ref, negm, l_part, st);
+    tile<false, false, 2>(c, j + 1, qf, o, m_ref, negm, l_part, st);
+    tile<false, false, 3>(c, j + 2, qf, o, m_ref, negm, l_part, st);
+    tile<false, false, 0>(c, j + 3, qf, o, m_ref, negm, l_part, st);
   }
-  for (; j < free_end; ++j) tile<false, false, -1>(c, j, qf, o, m_ref, l_part, st);
-  for (; j < nt; ++j) tile<true, false, -1>(c, j, qf, o, m_ref, l_part, st);
+  for (; j < free_end; ++j) tile<false, false, -1>(c, j, qf, o, m_ref, negm, l_part, st);
+  for (; j < nt; ++j) tile<true, false, -1>(c, j, qf, o, m_ref, negm, l_part, st);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
 
   const float l = l_part + __shfl_xor(l_part, 32);
@@ -689,7 +702,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(const AttnArgs a) {
       float dot = 0.0f;
 #pragma unroll
       for (int d = 0; d < D; ++d) dot = fmaf(q[d], Ks[jj * D + d], dot);
-      float v = dot * a.scale_log2;
+      float v = dot;
       if (k0 + jj >= kvis) v = -INFINITY;
       sc[jj] = v;
       mx = fmaxf(mx, v);

@@ -226,7 +226,8 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32
 // blockIdx.y = key frame: frames [0, n_hist) are history frames of [memory | window],
 // rotated at t = fi into krot[h][fi*T + u] (only when the history is rebuilt, else the grid
 // starts at the block's frames); frames after are the block's frames i = fi - n_hist at
-// t = fi: q -> qrot, k -> krot[h][t*T + u], v -> vcur.  Every output is in the operand
+// t = fi: q -> qrot (times q_scale = log2(e)/sqrt(D), so that q . k is the base-2 exponent
+// of the softmax), k -> krot[h][t*T + u], v -> vcur.  Every output is in the operand
 // dtype (in_dtype).  An FP8 cache is dequantised on the way (code * row scale), and its
 // history V rows are dequantised into vhist in attention order as well.
 template <int LPR>
@@ -262,6 +263,8 @@ __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
   const int64_t crow = (int64_t)i * rows + row;            // row of the block's [n*T][H][D]
   load8_in(a.q, a.in_dtype, crow * D + li * 8, x);
   rope_rotate8(a, fi, u, li, x);
+#pragma unroll
+  for (int e2 = 0; e2 < 8; ++e2) x[e2] *= a.q_scale;
   store8_op(a.qrot, a.in_dtype, (h * QT + (int64_t)i * a.T + u) * D + li * 8, x);
 
   load8_in(a.k_cur, a.in_dtype, crow * D + li * 8, x);

@@ -70,6 +70,7 @@ struct RopeArgs {
   int32_t n_cur, T, H, D, grid_h, grid_w, key_frames_max, block_frames_max;
   int32_t rope_mode, split_t, split_h, split_w;
   int32_t in_dtype, kv_dtype;
+  float q_scale;           // qrot = RoPE(q) * q_scale, q_scale = log2(e) / sqrt(D)
 };
 
 struct RopeTableArgs {
@@ -79,7 +80,9 @@ struct RopeTableArgs {
   int64_t entries;
 };
 
-// Attention of the staged block over [memory | window | current] (operand dtype).
+// Attention of the staged block over [memory | window | current] (operand dtype).  The
+// staged queries carry the softmax scale and the change to base 2: q . k is already the
+// exponent of 2 that softmax(q k / sqrt(D)) takes.
 struct AttnArgs {
   const void* q;           // qrot
   const void* k;           // krot
@@ -94,7 +97,6 @@ struct AttnArgs {
   int32_t T, H, D, Lq, Lk, Lhist;
   int32_t n_blocks;
   int32_t block_end[LACT_MAX_Q_BLOCKS];  // cumulative query-token ends of the blocks
-  float scale_log2;        // log2(e) / sqrt(D)
 };
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);

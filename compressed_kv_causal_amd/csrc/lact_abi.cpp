@@ -260,6 +260,7 @@ lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cu
   a.split_w = g.rope_split[2];
   a.in_dtype = g.q_dtype;
   a.kv_dtype = g.kv_dtype;
+  a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
   hipError_t e = lact::launch_rope(a, s);
   if (e != hipSuccess) return hip_fail(e, "rope launch");
   c->hist_built = true;
@@ -327,7 +328,6 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
   a.Lq = c->staged_frames * T;
   a.Lhist = c->plan.history_frames() * T;
   a.Lk = a.Lhist + a.Lq;
-  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
   hipError_t e = lact::launch_attention(a, g.q_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return LACT_OK;

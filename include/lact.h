@@ -105,7 +105,9 @@ typedef struct {
  *   ring_k/ring_v  [R][T][H][D] kv dtype            raw ring (pre-RoPE K, V)
  *   mem_k/mem_v    [M][T][H][D] kv dtype            compressed memory slots
  *   krot           [H][(M+W+B_max)*T][D] operand    rotated keys in attention order
- *   qrot           [H][B_max*T][D] operand          rotated queries of the block
+ *   qrot           [H][B_max*T][D] operand          rotated queries of the block, times
+ *                                                   log2(e)/sqrt(D) (the softmax scale
+ *                                                   and the change to base 2)
  *   vcur           [B_max][T][H][D] operand         current V staged for attention
  *   vhist          [M+W][T][H][D] operand           FP8: memory + window V dequantised
  *   *_scale        f32 per (token, head): ring/mem [slots][T][H]
