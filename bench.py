@@ -80,6 +80,8 @@ def main():
     import synth
 
     w = synth.workload(args.workload)
+    if w.get("train_blocks"):
+        return train_main(args, w)
     T, H, D = w["tokens"], w["heads"], w["head_dim"]
     B = w["block"]
     dt = {0: "f32", 1: "bf16", 2: "fp8"}[w["kv_dtype"]]   # storage of the cache
@@ -222,6 +224,98 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, i, wk, bk,
                                            wv, bv)
+    print(json.dumps(rec), flush=True)
+
+
+def train_main(args, w):
+    """Training form of the block-causal attention: one RoPE pass and one attention call
+    over the whole sequence of blocks (no history), timed per call.  The attention work
+    counted is the visible part only: block b of n_b frames sees the frames of blocks
+    0..b, so flop = 4 D H T^2 sum_b n_b * (n_0 + .. + n_b)."""
+    import torch
+    import compressed_kv_causal_amd as L
+    import synth
+    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    blocks = list(w["train_blocks"])
+    n = sum(blocks)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ids = list(range(n))
+    q, k, v = (torch.from_numpy(synth.frames(w, args.seed, t, ids).reshape(n * T, H, D))
+               .to(torch.bfloat16).to(dev) for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V))
+    cache = L.Cache(L.make_cfg(**w), device=dev)
+    Lq = n * T
+    out = torch.empty((Lq, H, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    h = cache.h
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        L.lact_rope_reset_apply(h, q, k, v, n, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        L.lact_block_attention(h, blocks, out, None, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(2)] for e in evs])
+    ms = part.mean(axis=0)
+    cum, pairs = 0, 0
+    for nb in blocks:
+        cum += nb
+        pairs += nb * cum
+    attn_flop = 4.0 * D * H * T * T * pairs
+    attn_tflops = attn_flop / (ms[1] * 1e-3) / 1e12
+    ms_per_step = wall * 1e3 / args.steps
+    rec = {
+        "metric": METRIC,
+        "value": round(n / (ms_per_step * 1e-3), 2),
+        "unit": "latent frames/s (training-form call: RoPE + block-causal attention over the whole sequence)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V)",
+        "config": {"workload": args.workload, "heads": H, "head_dim": D, "tokens_per_frame": T,
+                   "blocks_frames": blocks, "Lq": Lq, "Lk": Lq,
+                   "visible_fraction": round(pairs / float(n * n), 4)},
+        "attn_tflops": round(attn_tflops, 2),
+        "step_breakdown_ms": {"rope_reset_apply": round(ms[0], 4), "block_attention": round(ms[1], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK["bf16"],
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK["bf16"], 4), "traffic": None,
+                     "kernel": "k_attn (block attention)",
+                     "algorithmic_per_launch": f"{attn_flop:.4e} flop = 4*D*H*T^2*sum_b n_b*cum_b"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle.stream import OracleCache
+        oc = OracleCache(w)
+        qh, kh, vh = (t.float().cpu().numpy() for t in (q, k, v))
+        rows = np.linspace(0, Lq - 1, args.cpu_rows).astype(np.int64)
+        heads = np.repeat(np.arange(H, dtype=np.int32), len(rows))
+        rr = np.tile(rows, H)
+        threads = min(16, os.cpu_count() or 1)
+        t1 = time.perf_counter()
+        oc.attention(qh, kh, vh, block_frames=blocks, sel=(heads, rr), threads=threads)
+        secs = time.perf_counter() - t1
+        ends = np.cumsum(blocks) * T
+        vis = ends[np.searchsorted(ends, rows, side="right")]
+        frac = H * float(vis.sum()) / (H * T * T * pairs)
+        full = secs / frac
+        rec["cpu_baseline"] = {
+            "value": round(n / full, 6), "unit": rec["unit"], "cores": threads, "kind": "oracle",
+            "sample": (f"attention of all {H} heads x {len(rows)} query rows over their visible "
+                       f"keys ({secs:.1f} s, double precision), extrapolated by visible key "
+                       f"pairs (x{1 / frac:.0f}) to the whole call; RoPE not counted")}
     print(json.dumps(rec), flush=True)
 
 

@@ -111,7 +111,20 @@ WORKLOADS = {
                    rope_mode=3, rope_split=(44, 42, 42), rope_theta=10000.0,
                    first_block=8, block=8, history_blocks=11, steps=1, pool_blocks=7,
                    outliers=True),
+    # Training form of the block-causal attention (walkthrough "Neighbor Forcing"): one
+    # call over 46 frames in blocks of 6, 8, 8, 8, 8, 8, no history, block-causal mask.
+    "train_s512": dict(heads=40, head_dim=128, grid_h=32, grid_w=32, window_frames=8,
+                       mem_slots=16, ratio=5, max_block_frames=46, kv_dtype=BF16, q_dtype=BF16,
+                       rope_mode=3, rope_split=(44, 42, 42), rope_theta=10000.0,
+                       first_block=6, block=8, history_blocks=0, steps=1, pool_blocks=7,
+                       train_blocks=(6, 8, 8, 8, 8, 8)),
 }
+
+# The memory-block / current-block grid of the model card's ablation table (Table 5):
+# window ("memory block") W and block B in frames, 512x512 shapes, memory 16 slots at 5:1.
+for _w, _b in ((6, 6), (8, 8), (6, 8)):
+    WORKLOADS[f"grid_w{_w}_b{_b}"] = dict(WORKLOADS["s512_bf16"], window_frames=_w,
+                                          max_block_frames=_b, first_block=_b, block=_b)
 
 CFG_KEYS = ("heads", "head_dim", "grid_h", "grid_w", "window_frames", "mem_slots", "ratio",
             "max_block_frames", "kv_dtype", "q_dtype", "rope_mode", "rope_split", "rope_theta")

@@ -183,6 +183,27 @@ def test_s720_bf16_step_parity():
     _big_step_parity("s720_bf16", 11, 8, first_check=True)
 
 
+def test_grid_w6_b8_step_parity():
+    """The model card's chosen memory-block / current-block pair (6 / 8): window 6, blocks
+    of 8, memory 16 -- ring R = 17, memory and ring bit-exact, step attention vs oracle."""
+    _big_step_parity("grid_w6_b8", 11, 8)
+
+
+def test_train_form_long_sequence():
+    """Training form: one call over 46 frames in blocks 6, 8, 8, 8, 8, 8 (47104 query and
+    key tokens, no history) under the block-causal mask; sampled rows of all 40 heads,
+    always the first and last row of every frame, against the oracle."""
+    w = synth.workload("train_s512")
+    blocks = list(w["train_blocks"])
+    n = sum(blocks)
+    run = Runner(w)
+    sel = sample_rows(w, n, seed=7, per_head=4)
+    res = run.step(n, blocks=blocks, sel=sel)
+    err, dl = run.compare_attention(res)
+    say(f"train form {blocks}: Lq {n * w['tokens']}, rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16]
+
+
 def test_fp8_append_compress_bitexact():
     """FP8 KV: ring codes and scales and the re-quantised memory slots bit-exact."""
     w = synth.workload("fp8_kv")
