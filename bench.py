@@ -111,6 +111,11 @@ def main():
         del src, dst
 
     cache = L.Cache(L.make_cfg(**w), device=dev)
+    if w.get("ref_frames", 0):
+        kr, vr = synth.ref_frames(w, args.seed)
+        n_ref = kr.shape[0]
+        cache.ref_set(*(torch.from_numpy(x.reshape(n_ref * T, H, D)).to(io).to(dev)
+                        for x in (kr, vr)))
     Lq = B * T
     out = torch.empty((Lq, H, D), dtype=io, device=dev)
     lse = torch.empty((H, Lq), dtype=torch.float32, device=dev)
@@ -150,7 +155,7 @@ def main():
         step(i)
         i += 1
     torch.cuda.synchronize()
-    n_hist = cache.state()["mem_len"] + cache.state()["win_len"]
+    n_hist = cache.state()["mem_len"] + cache.state()["win_len"] + w.get("ref_frames", 0)
     Lk = (n_hist + B) * T
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -324,6 +329,7 @@ def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv,
     attention of every head for a few query rows over the full key set (history rebuilt
     by the oracle's own compressor from the same frames), extrapolated to the whole step."""
     import oracle as O
+    import synth
     from oracle.stream import OracleCache
     T, H, D = w["tokens"], w["heads"], w["head_dim"]
     io_bf16 = w["q_dtype"] == 1
@@ -333,6 +339,11 @@ def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv,
     # block n uses pool block n mod len(pool)).
     st = cache.state()
     oc = OracleCache(w)
+    if w.get("ref_frames", 0):
+        # the reference segment as the device holds it (converted to the input dtype)
+        io = torch.bfloat16 if io_bf16 else torch.float32
+        kr, vr = (torch.from_numpy(x).to(io).float().numpy() for x in synth.ref_frames(w, args.seed))
+        oc.set_ref(kr, vr)
     np_pool = [[t.float().cpu().numpy().reshape(B, -1) for t in trip] for trip in pool]
     t_setup = time.perf_counter()
     oc.bk.F, oc.bk.G = st["F"], st["G"] - st["mem_len"]

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "liblact.so")
 LACT_F32, LACT_BF16, LACT_FP8_E4M3 = 0, 1, 2
 LACT_MAX_KEY_FRAMES = 256
 LACT_MAX_Q_BLOCKS = 16
-SEG_MEMORY, SEG_WINDOW, SEG_CURRENT = 0, 1, 2
+SEG_MEMORY, SEG_WINDOW, SEG_CURRENT, SEG_REF = 0, 1, 2, 3
 STATUS = {0: "LACT_OK", 1: "LACT_E_INVALID", 2: "LACT_E_SHAPE", 3: "LACT_E_CAPACITY",
           4: "LACT_E_DTYPE", 5: "LACT_E_STATE", 6: "LACT_E_HIP"}
 
@@ -33,7 +33,7 @@ class lact_cfg(ctypes.Structure):
                 ("ratio", ctypes.c_int32), ("max_block_frames", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("rope_mode", ctypes.c_int32), ("rope_split", ctypes.c_int32 * 3),
-                ("rope_theta", ctypes.c_float)]
+                ("rope_theta", ctypes.c_float), ("ref_frames", ctypes.c_int32)]
 
 
 class lact_key_frame(ctypes.Structure):
@@ -47,12 +47,13 @@ class lact_state(ctypes.Structure):
                 ("win_len", ctypes.c_int32), ("mem_len", ctypes.c_int32),
                 ("pending", ctypes.c_int32), ("ring_slots", ctypes.c_int32),
                 ("version", ctypes.c_uint64), ("staged_frames", ctypes.c_int32),
-                ("staged_valid", ctypes.c_int32)]
+                ("staged_valid", ctypes.c_int32), ("ref_valid", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
-_LAYOUT_FIELDS = ["total", "ring_k", "ring_v", "mem_k", "mem_v", "krot", "qrot", "vcur", "vhist",
-                  "ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale", "rope_table",
-                  "attn_flags", "frame_bytes"]
+_LAYOUT_FIELDS = ["total", "ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v", "krot", "qrot",
+                  "vcur", "vhist", "ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale",
+                  "ref_k_scale", "ref_v_scale", "rope_table", "attn_flags", "frame_bytes"]
 
 
 class lact_layout(ctypes.Structure):
@@ -67,7 +68,7 @@ class LactError(RuntimeError):
 
 
 EXPORTS = ["lact_cache_footprint", "lact_cache_layout", "lact_cache_init", "lact_cache_destroy",
-           "lact_rope_reset_apply", "lact_block_attention", "lact_kv_ring_append",
+           "lact_ref_set", "lact_rope_reset_apply", "lact_block_attention", "lact_kv_ring_append",
            "lact_convkv_compress", "lact_cache_state", "lact_cache_keys", "lact_plan_create",
            "lact_plan_destroy", "lact_plan_append", "lact_plan_compress", "lact_plan_state",
            "lact_plan_keys", "lact_last_error"]
@@ -90,6 +91,7 @@ def lib():
         "lact_cache_layout": [P(lact_cfg), P(lact_layout)],
         "lact_cache_init": [P(lact_cfg), vp, ctypes.c_size_t, P(vp)],
         "lact_cache_destroy": [vp],
+        "lact_ref_set": [vp, vp, vp, i32, vp],
         "lact_rope_reset_apply": [vp, vp, vp, vp, i32, vp],
         "lact_block_attention": [vp, P(i32), i32, vp, vp, vp],
         "lact_kv_ring_append": [vp, vp, vp, i32, vp],
@@ -119,7 +121,8 @@ def _check(status):
 
 
 def make_cfg(heads, head_dim, grid_h, grid_w, window_frames, mem_slots, ratio, max_block_frames,
-             kv_dtype, q_dtype, rope_mode, rope_split, rope_theta=10000.0, **_ignored):
+             kv_dtype, q_dtype, rope_mode, rope_split, rope_theta=10000.0, ref_frames=0,
+             **_ignored):
     c = lact_cfg()
     c.heads, c.head_dim, c.grid_h, c.grid_w = heads, head_dim, grid_h, grid_w
     c.window_frames, c.mem_slots, c.ratio = window_frames, mem_slots, ratio
@@ -128,6 +131,7 @@ def make_cfg(heads, head_dim, grid_h, grid_w, window_frames, mem_slots, ratio, m
     sp = list(rope_split) + [0] * (3 - len(rope_split))
     c.rope_split = (ctypes.c_int32 * 3)(*sp)
     c.rope_theta = rope_theta
+    c.ref_frames = ref_frames
     return c
 
 
@@ -186,6 +190,11 @@ def lact_block_attention(h, q_block_frames, out, lse=None, stream=None):
         arr = (ctypes.c_int32 * n)(*q_block_frames)
     lse_p = _ptr(lse, torch.float32, "lse") if lse is not None else None
     _check(lib().lact_block_attention(h, arr, n, _ptr(out, name="out"), lse_p, _stream(stream)))
+
+
+def lact_ref_set(h, k_ref, v_ref, n_frames, stream=None):
+    _check(lib().lact_ref_set(h, _ptr(k_ref, name="k_ref"), _ptr(v_ref, name="v_ref"), n_frames,
+                              _stream(stream)))
 
 
 def lact_kv_ring_append(h, k_new, v_new, n_frames, stream=None):
@@ -296,6 +305,9 @@ class Cache:
             out = torch.empty((Lq, self.H, self.D), dtype=self.io_dtype, device=self.buf.device)
         lact_block_attention(self.h, q_block_frames, out, lse, stream)
         return out
+
+    def ref_set(self, k_ref, v_ref, stream=None):
+        lact_ref_set(self.h, k_ref, v_ref, k_ref.shape[0] // self.T, stream)
 
     def kv_ring_append(self, k_new, v_new, stream=None):
         lact_kv_ring_append(self.h, k_new, v_new, k_new.shape[0] // self.T, stream)

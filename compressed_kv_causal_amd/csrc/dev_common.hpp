@@ -170,16 +170,25 @@ __device__ __forceinline__ float store8_kv(void* base, int32_t dtype, int64_t of
   return rq.scale;
 }
 
-// Frame base element offset of history frame fi in memory or in the raw ring.
-__device__ __forceinline__ bool hist_is_mem(const HistMap& m, int32_t fi) { return fi < m.mem_len; }
-__device__ __forceinline__ int32_t hist_slot(const HistMap& m, int32_t fi) {
+// Sources of a key frame's rows.
+enum : int32_t { SRC_RING = 0, SRC_MEM = 1, SRC_CUR = 2, SRC_REF = 3 };
+
+// Storage of history key frame fi: SRC_REF, SRC_MEM or SRC_RING, and its slot there.
+__device__ __forceinline__ int32_t hist_src(const HistMap& m, int32_t fi, int32_t* slot) {
+  if (fi < m.ref_len) {
+    *slot = fi;
+    return SRC_REF;
+  }
+  fi -= m.ref_len;
   int32_t s;
   if (fi < m.mem_len) {
     s = m.mem_slot0 + fi;
-    return s >= m.M ? s - m.M : s;
+    *slot = s >= m.M ? s - m.M : s;
+    return SRC_MEM;
   }
   s = m.ring_slot0 + (fi - m.mem_len);
-  return s >= m.R ? s - m.R : s;
+  *slot = s >= m.R ? s - m.R : s;
+  return SRC_RING;
 }
 
 }  // namespace lact

@@ -34,28 +34,29 @@ __device__ __forceinline__ int32_t block_of_row(const AttnArgs& a, int32_t row) 
   return b;
 }
 
-// Element offset of V row (key j, head h).  Key frame fi = j / T of [memory | window |
-// current]: memory and window frames are read where they are stored (raw ring or memory
-// slot), the block's frames from the staged copy.
+// Element offset of V row (key j, head h).  Key frame fi = j / T of [reference | memory |
+// window | current]: history frames are read where they are stored (reference slot,
+// memory slot or raw ring), the block's frames from the staged copy.
 __device__ __forceinline__ int64_t v_row_off(const AttnArgs& a, int32_t j, int32_t h,
                                              int32_t* which) {
   const int32_t fi = j / a.T;
   const int32_t u = j - fi * a.T;
-  const int32_t nh = a.hist.mem_len + a.hist.win_len;
+  const int32_t nh = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   int32_t slot;
   if (fi < nh) {
-    slot = hist_slot(a.hist, fi);
-    *which = fi < a.hist.mem_len ? 1 : 0;
+    *which = hist_src(a.hist, fi, &slot);
   } else {
     slot = fi - nh;
-    *which = 2;
+    *which = SRC_CUR;
   }
   return (((int64_t)slot * a.T + u) * a.H + h) * a.D;
 }
 
 template <typename T>
 __device__ __forceinline__ const T* v_base(const AttnArgs& a, int32_t which) {
-  return static_cast<const T*>(which == 1 ? a.v_mem : (which == 0 ? a.v_ring : a.v_cur));
+  return static_cast<const T*>(which == SRC_MEM ? a.v_mem
+                               : which == SRC_RING ? a.v_ring
+                               : which == SRC_REF ? a.v_ref : a.v_cur);
 }
 
 // Row m of a 32-key block holds actual key perm32(m): bits 2 and 3 swapped.  With this
@@ -286,22 +287,25 @@ struct Geo {
   const char* v_mem;
   const char* v_ring;
   const char* v_cur;
+  const char* v_ref;
   int64_t frame_bytes;  // one V frame, T * H * D * 2
-  int T, Lk, nf, mem_len, nh, M, R, mem_slot0, ring_slot0;
+  int T, Lk, nf, ref_len, mem_end, nh, M, R, mem_slot0, ring_slot0;
 };
 
-// V base address of key frame f of [memory | window | block] (frames past the end repeat
-// the last one, so copies issued past the end read finite data inside the buffers).
+// V base address of key frame f of [reference | memory | window | block] (frames past
+// the end repeat the last one, so copies issued past the end read finite data inside the
+// buffers).
 __device__ __forceinline__ const char* frame_base(const Geo& g, int f) {
   f = f < g.nf ? f : g.nf - 1;
-  int ms = g.mem_slot0 + f;
+  int ms = g.mem_slot0 + (f - g.ref_len);
   ms = ms >= g.M ? ms - g.M : ms;
-  int rs = g.ring_slot0 + (f - g.mem_len);
+  int rs = g.ring_slot0 + (f - g.mem_end);
   rs = rs >= g.R ? rs - g.R : rs;
+  const char* fb = g.v_ref + f * g.frame_bytes;
   const char* mb = g.v_mem + ms * g.frame_bytes;
   const char* rb = g.v_ring + rs * g.frame_bytes;
   const char* cb = g.v_cur + (f - g.nh) * g.frame_bytes;
-  return f < g.mem_len ? mb : (f < g.nh ? rb : cb);
+  return f < g.ref_len ? fb : (f < g.mem_end ? mb : (f < g.nh ? rb : cb));
 }
 
 struct Ctx {
@@ -542,12 +546,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   c.g.v_mem = static_cast<const char*>(a.v_mem);
   c.g.v_ring = static_cast<const char*>(a.v_ring);
   c.g.v_cur = static_cast<const char*>(a.v_cur);
+  c.g.v_ref = static_cast<const char*>(a.v_ref);
   c.g.frame_bytes = (int64_t)a.T * a.H * ROW_BYTES;
   c.g.T = a.T;
   c.g.Lk = a.Lk;
   c.g.nf = a.Lk / a.T;
-  c.g.mem_len = a.hist.mem_len;
-  c.g.nh = a.hist.mem_len + a.hist.win_len;
+  c.g.ref_len = a.hist.ref_len;
+  c.g.mem_end = a.hist.ref_len + a.hist.mem_len;
+  c.g.nh = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   c.g.M = a.hist.M;
   c.g.R = a.hist.R;
   c.g.mem_slot0 = a.hist.mem_slot0;

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
   const int32_t row = e / LPR, li = e % LPR;              // row = u * H + h inside the frame
   if (row >= rows) return;
   const int32_t u = row / a.H, h = row - u * a.H;
-  const int32_t n_hist = a.hist.mem_len + a.hist.win_len;
+  const int32_t n_hist = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   const int32_t fi = blockIdx.y + (a.hist_rows ? 0 : n_hist);
   const int64_t KFT = (int64_t)a.key_frames_max * a.T;
   const int64_t QT = (int64_t)a.block_frames_max * a.T;
@@ -245,16 +245,20 @@ __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
   const bool fp8 = a.kv_dtype == DT_FP8;
   float x[8];
   if (fi < n_hist) {
-    const bool mem = hist_is_mem(a.hist, fi);
-    const int64_t srow = (int64_t)hist_slot(a.hist, fi) * rows + row;
-    const float sc = fp8 ? (mem ? a.mem_k_scale : a.ring_k_scale)[srow] : 1.0f;
-    load8_kv(mem ? a.mem_k : a.ring_k, a.kv_dtype, srow * D + li * 8, sc, x);
+    int32_t slot;
+    const int32_t src = hist_src(a.hist, fi, &slot);
+    const int64_t srow = (int64_t)slot * rows + row;
+    const void* ksrc = src == SRC_REF ? a.ref_k : (src == SRC_MEM ? a.mem_k : a.ring_k);
+    const float* kscale = src == SRC_REF ? a.ref_k_scale : (src == SRC_MEM ? a.mem_k_scale : a.ring_k_scale);
+    const float sc = fp8 ? kscale[srow] : 1.0f;
+    load8_kv(ksrc, a.kv_dtype, srow * D + li * 8, sc, x);
     rope_rotate8(a, fi, u, li, x);
     const int64_t drow = h * KFT + (int64_t)fi * a.T + u;
     store8_op(a.krot, a.in_dtype, drow * D + li * 8, x);
     if (fp8) {
-      const float sv = (mem ? a.mem_v_scale : a.ring_v_scale)[srow];
-      load8_kv(mem ? a.mem_v : a.ring_v, DT_FP8, srow * D + li * 8, sv, x);
+      const void* vsrc = src == SRC_REF ? a.ref_v : (src == SRC_MEM ? a.mem_v : a.ring_v);
+      const float* vscale = src == SRC_REF ? a.ref_v_scale : (src == SRC_MEM ? a.mem_v_scale : a.ring_v_scale);
+      load8_kv(vsrc, DT_FP8, srow * D + li * 8, vscale[srow], x);
       store8_op(a.vhist, a.in_dtype, ((int64_t)fi * rows + row) * D + li * 8, x);
     }
     return;
@@ -326,7 +330,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
-  const int32_t n_hist = a.hist.mem_len + a.hist.win_len;
+  const int32_t n_hist = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   const int32_t frames = (a.hist_rows ? n_hist : 0) + a.n_cur;
   if (frames <= 0) return hipSuccess;
   const int lpr = a.D / 8;

@@ -14,11 +14,12 @@ enum : int32_t { DT_F32 = LACT_F32, DT_BF16 = LACT_BF16, DT_FP8 = LACT_FP8_E4M3 
 
 constexpr int kMaxGroupsPerLaunch = 16;
 
-// Where history key frame fi (attention order) lives: memory rank j < mem_len is in memory
-// slot (mem_slot0 + j) mod M (group G - mem_len + j); window rank k is in raw slot
+// Where history key frame fi (attention order [reference | memory | window]) lives:
+// reference frame i < ref_len is reference slot i; memory rank j is in memory slot
+// (mem_slot0 + j) mod M (group G - mem_len + j); window rank k is in raw slot
 // (ring_slot0 + k) mod R (frame E + k).  mem_slot0 = (G - mem_len) mod M, ring_slot0 = E mod R.
 struct HistMap {
-  int32_t mem_len, win_len, M, R, mem_slot0, ring_slot0;
+  int32_t ref_len, mem_len, win_len, M, R, mem_slot0, ring_slot0;
 };
 
 // Append: frame F + i goes to raw slot (slot0 + i) mod R, slot0 = F mod R.
@@ -54,16 +55,20 @@ struct RopeArgs {
   const void* v_cur;       // [n*T][H][D] in in_dtype
   const void* ring_k;
   const void* mem_k;
+  const void* ref_k;
   const void* ring_v;
   const void* mem_v;
+  const void* ref_v;
   const float* ring_k_scale;
   const float* mem_k_scale;
+  const float* ref_k_scale;
   const float* ring_v_scale;
   const float* mem_v_scale;
+  const float* ref_v_scale;
   void* krot;              // [H][KF*T][D] operand dtype
   void* qrot;              // [H][B_max*T][D]
   void* vcur;              // [B_max][T][H][D]
-  void* vhist;             // FP8 only: [M+W][T][H][D] dequantised V of [memory | window]
+  void* vhist;             // FP8 only: [ref+M+W][T][H][D] dequantised V of the history
   const float2* table;
   HistMap hist;
   int32_t hist_rows;       // 1: rebuild history keys (and, FP8, history values)
@@ -88,6 +93,7 @@ struct AttnArgs {
   const void* k;           // krot
   const void* v_ring;      // V rows of window frames (raw ring slots)
   const void* v_mem;       // V rows of memory frames (memory slots)
+  const void* v_ref;       // V rows of reference frames (reference slots)
   const void* v_cur;       // V rows of the block's frames
   void* out;               // [Lq][H][D] q dtype
   float* lse;              // [H][Lq] or null

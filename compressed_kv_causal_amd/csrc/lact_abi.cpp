@@ -38,9 +38,10 @@ lact_status check_cfg(const lact_cfg* c) {
     return fail(LACT_E_SHAPE, "window_frames and mem_slots must be >= 0");
   if (c->ratio < 1 || c->ratio > 16) return fail(LACT_E_SHAPE, "ratio must be in 1..16");
   if (c->max_block_frames < 1) return fail(LACT_E_SHAPE, "max_block_frames must be >= 1");
-  const int64_t kf = (int64_t)c->mem_slots + c->window_frames + c->max_block_frames;
+  if (c->ref_frames < 0) return fail(LACT_E_SHAPE, "ref_frames must be >= 0");
+  const int64_t kf = (int64_t)c->ref_frames + c->mem_slots + c->window_frames + c->max_block_frames;
   if (kf > LACT_MAX_KEY_FRAMES)
-    return fail(LACT_E_CAPACITY, "mem_slots + window_frames + max_block_frames exceeds " +
+    return fail(LACT_E_CAPACITY, "ref_frames + mem_slots + window_frames + max_block_frames exceeds " +
                                      std::to_string(LACT_MAX_KEY_FRAMES));
   const int64_t T = (int64_t)c->grid_h * c->grid_w;
   if (T * c->heads * c->head_dim > (int64_t(1) << 28) || kf * T > (int64_t(1) << 24))
@@ -65,7 +66,7 @@ lact_status check_cfg(const lact_cfg* c) {
 }
 
 int64_t rope_table_entries(const lact_cfg& c) {
-  const int64_t kf = (int64_t)c.mem_slots + c.window_frames + c.max_block_frames;
+  const int64_t kf = (int64_t)c.ref_frames + c.mem_slots + c.window_frames + c.max_block_frames;
   const int64_t T = (int64_t)c.grid_h * c.grid_w;
   if (c.rope_mode == 1) return kf * T * (c.head_dim / 2);
   return kf * (c.rope_split[0] / 2) + (int64_t)c.grid_h * (c.rope_split[1] / 2) +
@@ -78,7 +79,7 @@ void compute_layout(const lact_cfg& c, lact_layout* L) {
   const int64_t fe = T * c.heads * c.head_dim;  // elements per frame
   const size_t kvb = elem_bytes(c.kv_dtype);
   const int32_t R = c.window_frames + c.max_block_frames + c.ratio - 1;
-  const int32_t KF = c.mem_slots + c.window_frames + c.max_block_frames;
+  const int32_t KF = c.ref_frames + c.mem_slots + c.window_frames + c.max_block_frames;
   const int32_t B = c.max_block_frames, M = c.mem_slots;
   const bool fp8 = c.kv_dtype == LACT_FP8_E4M3;
   const size_t fb = (size_t)fe * kvb;
@@ -94,15 +95,19 @@ void compute_layout(const lact_cfg& c, lact_layout* L) {
   L->ring_v = take(fb * R);
   L->mem_k = take(fb * M);
   L->mem_v = take(fb * M);
+  L->ref_k = take(fb * (size_t)c.ref_frames);
+  L->ref_v = take(fb * (size_t)c.ref_frames);
   L->krot = take(ob * KF);
   L->qrot = take(ob * B);
   L->vcur = take(ob * B);
-  L->vhist = take(fp8 ? ob * (size_t)(M + c.window_frames) : 0);
+  L->vhist = take(fp8 ? ob * (size_t)(c.ref_frames + M + c.window_frames) : 0);
   if (fp8) {
     L->ring_k_scale = take(sb * R);
     L->ring_v_scale = take(sb * R);
     L->mem_k_scale = take(sb * M);
     L->mem_v_scale = take(sb * M);
+    L->ref_k_scale = take(sb * (size_t)c.ref_frames);
+    L->ref_v_scale = take(sb * (size_t)c.ref_frames);
   }
   L->rope_table = take(sizeof(float) * 2 * (size_t)rope_table_entries(c));
   L->attn_flags = take(sizeof(int32_t) * (size_t)c.heads * (size_t)((B * T + 255) / 256));
@@ -125,6 +130,7 @@ struct lact_cache {
   int32_t staged_frames = 0;
   bool hist_built = false;
   uint64_t hist_version = 0;
+  bool ref_valid = false;     // lact_ref_set has stored the reference segment
   lact_cache(const lact_cfg& c, const lact_layout& l, void* b)
       : cfg(c), lay(l), plan(c), buf(static_cast<char*>(b)) {}
 
@@ -135,6 +141,7 @@ struct lact_cache {
   }
   lact::HistMap hist() const {
     lact::HistMap m;
+    m.ref_len = cfg.ref_frames;
     m.mem_len = plan.mem_len();
     m.win_len = plan.win_len();
     m.M = cfg.mem_slots;
@@ -206,6 +213,8 @@ lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cu
   if (n_frames < 1 || n_frames > c->cfg.max_block_frames)
     return fail(LACT_E_CAPACITY, "n_frames " + std::to_string(n_frames) + " outside 1.." +
                                      std::to_string(c->cfg.max_block_frames));
+  if (c->cfg.ref_frames > 0 && !c->ref_valid)
+    return fail(LACT_E_STATE, "the reference segment has not been set (lact_ref_set)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lact_cfg& g = c->cfg;
   if (!c->table_ready) {
@@ -234,10 +243,14 @@ lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cu
   a.mem_k = c->at(c->lay.mem_k);
   a.ring_v = c->at(c->lay.ring_v);
   a.mem_v = c->at(c->lay.mem_v);
+  a.ref_k = c->at(c->lay.ref_k);
+  a.ref_v = c->at(c->lay.ref_v);
   a.ring_k_scale = c->fat(c->lay.ring_k_scale);
   a.mem_k_scale = c->fat(c->lay.mem_k_scale);
   a.ring_v_scale = c->fat(c->lay.ring_v_scale);
   a.mem_v_scale = c->fat(c->lay.mem_v_scale);
+  a.ref_k_scale = c->fat(c->lay.ref_k_scale);
+  a.ref_v_scale = c->fat(c->lay.ref_v_scale);
   a.krot = c->at(c->lay.krot);
   a.qrot = c->at(c->lay.qrot);
   a.vcur = c->at(c->lay.vcur);
@@ -309,11 +322,12 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
   a.k_head_stride = (int64_t)c->lay.key_frames_max * T * g.head_dim;
   a.hist = c->hist();
   if (g.kv_dtype == LACT_FP8_E4M3) {
-    // history V was dequantised into vhist in attention order: memory ranks from its
-    // start, window ranks after them
+    // history V was dequantised into vhist in attention order: reference frames from its
+    // start, then memory ranks, then window ranks
     const size_t ob = (size_t)T * g.heads * g.head_dim * elem_bytes(g.q_dtype);
-    a.v_mem = c->at(c->lay.vhist);
-    a.v_ring = c->at(c->lay.vhist + ob * (size_t)a.hist.mem_len);
+    a.v_ref = c->at(c->lay.vhist);
+    a.v_mem = c->at(c->lay.vhist + ob * (size_t)a.hist.ref_len);
+    a.v_ring = c->at(c->lay.vhist + ob * (size_t)(a.hist.ref_len + a.hist.mem_len));
     a.hist.mem_slot0 = 0;
     a.hist.ring_slot0 = 0;
     a.hist.M = a.hist.mem_len > 0 ? a.hist.mem_len : 1;
@@ -321,6 +335,7 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
   } else {
     a.v_ring = c->at(c->lay.ring_v);
     a.v_mem = c->at(c->lay.mem_v);
+    a.v_ref = c->at(c->lay.ref_v);
   }
   a.T = T;
   a.H = g.heads;
@@ -330,6 +345,39 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
   a.Lk = a.Lhist + a.Lq;
   hipError_t e = lact::launch_attention(a, g.q_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return LACT_OK;
+}
+
+lact_status lact_ref_set(lact_cache* c, const void* k_ref, const void* v_ref, int32_t n_frames,
+                         void* stream) {
+  if (!c) return fail(LACT_E_INVALID, "cache is NULL");
+  if (!k_ref || !v_ref || !aligned(k_ref, 16) || !aligned(v_ref, 16))
+    return fail(LACT_E_INVALID, "k_ref and v_ref must be non-NULL and 16-byte aligned");
+  const lact_cfg& g = c->cfg;
+  if (g.ref_frames < 1) return fail(LACT_E_STATE, "this cache has no reference segment (ref_frames = 0)");
+  if (n_frames != g.ref_frames)
+    return fail(LACT_E_SHAPE, "n_frames " + std::to_string(n_frames) + " != ref_frames " +
+                                  std::to_string(g.ref_frames));
+  lact::RingWriteArgs a;
+  a.src[0] = k_ref;
+  a.src[1] = v_ref;
+  a.ring[0] = c->at(c->lay.ref_k);
+  a.ring[1] = c->at(c->lay.ref_v);
+  a.ring_scale[0] = c->fat(c->lay.ref_k_scale);
+  a.ring_scale[1] = c->fat(c->lay.ref_v_scale);
+  a.slot0 = 0;
+  a.n_frames = n_frames;
+  a.R = n_frames;
+  a.T = c->T();
+  a.H = g.heads;
+  a.D = g.head_dim;
+  a.in_dtype = g.q_dtype;
+  a.kv_dtype = g.kv_dtype;
+  hipError_t e = lact::launch_ring_write(a, (int64_t)n_frames * a.T * a.H, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reference write launch");
+  c->ref_valid = true;
+  c->hist_built = false;  // the rotated reference keys (and FP8 values) are restaged
+  c->staged = false;
   return LACT_OK;
 }
 
@@ -417,6 +465,7 @@ lact_status lact_cache_state(const lact_cache* c, lact_state* out) {
   c->plan.state(out);
   out->staged_frames = c->staged ? c->staged_frames : 0;
   out->staged_valid = (c->staged && c->staged_version == c->plan.version()) ? 1 : 0;
+  out->ref_valid = c->ref_valid ? 1 : 0;
   return LACT_OK;
 }
 

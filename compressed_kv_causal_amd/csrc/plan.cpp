@@ -23,6 +23,7 @@ int32_t Planner::key_frames(int32_t n_cur, lact_key_frame* out, int32_t cap) con
     }
     ++rank;
   };
+  for (int32_t i = 0; i < ref_; ++i) put(LACT_SEG_REF, i, i);
   for (int64_t g = first_mem_group(); g < G_; ++g) put(LACT_SEG_MEMORY, mem_slot(g), g);
   for (int64_t f = evicted(); f < F_; ++f) put(LACT_SEG_WINDOW, raw_slot(f), f);
   for (int32_t i = 0; i < n_cur; ++i) put(LACT_SEG_CURRENT, i, F_ + i);
@@ -40,6 +41,8 @@ void Planner::state(lact_state* st) const {
   st->version = version_;
   st->staged_frames = 0;
   st->staged_valid = 0;
+  st->ref_valid = 0;
+  st->reserved = 0;
 }
 
 }  // namespace lact

@@ -9,6 +9,9 @@
 // cached KV and compression once between blocks (walkthrough "SoulX-LiveAct", sections
 // "ConvKV Memory" and "Streaming Pipeline").
 //
+// Key frames in attention order: [reference (fixed, ref_frames frames) | memory | window |
+// current]; the temporal position of a key frame is its rank.
+//
 // Counters: F frames appended, G groups compressed, E = max(0, F - W) evicted.  Group g =
 // frames [r*g, r*g + r) -> memory slot g mod M.  Up to r-1 evicted frames wait (pending)
 // for their group and are not attended.  Raw slot of frame f = f mod R, R = W + B_max + r - 1,
@@ -25,7 +28,8 @@ namespace lact {
 class Planner {
  public:
   explicit Planner(const lact_cfg& cfg)
-      : W_(cfg.window_frames), M_(cfg.mem_slots), r_(cfg.ratio), B_(cfg.max_block_frames) {
+      : ref_(cfg.ref_frames), W_(cfg.window_frames), M_(cfg.mem_slots), r_(cfg.ratio),
+        B_(cfg.max_block_frames) {
     R_ = W_ + B_ + r_ - 1;
   }
 
@@ -41,7 +45,9 @@ class Planner {
   uint64_t version() const { return version_; }
   // oldest group present in memory and oldest frame of the window
   int64_t first_mem_group() const { return G_ - mem_len(); }
-  int32_t history_frames() const { return mem_len() + win_len(); }
+  int32_t ref_frames() const { return ref_; }
+  // key frames before the current block: [reference | memory | window]
+  int32_t history_frames() const { return ref_ + mem_len() + win_len(); }
 
   int32_t raw_slot(int64_t frame) const { return static_cast<int32_t>(frame % R_); }
   int32_t mem_slot(int64_t group) const { return M_ > 0 ? static_cast<int32_t>(group % M_) : -1; }
@@ -69,7 +75,7 @@ class Planner {
   void state(lact_state* st) const;
 
  private:
-  int32_t W_, M_, r_, B_, R_;
+  int32_t ref_, W_, M_, r_, B_, R_;
   int64_t F_ = 0, G_ = 0;
   uint64_t version_ = 0;
 };

@@ -67,21 +67,26 @@ typedef struct {
                             3: 3D, (t, h, w) over the channel split rope_split            */
   int32_t rope_split[3]; /* 3D: d_t, d_h, d_w, each even, sum = head_dim                  */
   float rope_theta;      /* RoPE base, e.g. 10000                                         */
+  int32_t ref_frames;    /* reference segment: frames of a fixed KV prefix (the reference
+                            image's part of the context) attended before the memory by
+                            every step; 0 = none.  Set once with lact_ref_set.           */
 } lact_cfg;
 
 /* Supported: head_dim 64 or 128; heads >= 1; T >= 1; W >= 0; M >= 0; 1 <= r <= 16;
- * 1 <= B_max; M + W + B_max <= LACT_MAX_KEY_FRAMES. */
+ * 1 <= B_max; ref_frames >= 0; ref_frames + M + W + B_max <= LACT_MAX_KEY_FRAMES. */
 #define LACT_MAX_KEY_FRAMES 256
 #define LACT_MAX_Q_BLOCKS 16
 
 /* Segment of a key frame in attention order. */
-enum { LACT_SEG_MEMORY = 0, LACT_SEG_WINDOW = 1, LACT_SEG_CURRENT = 2 };
+enum { LACT_SEG_MEMORY = 0, LACT_SEG_WINDOW = 1, LACT_SEG_CURRENT = 2, LACT_SEG_REF = 3 };
 
-/* One key frame in attention order [memory oldest..newest | window oldest..newest | current]. */
+/* One key frame in attention order
+ * [reference | memory oldest..newest | window oldest..newest | current]. */
 typedef struct {
   int32_t segment;       /* LACT_SEG_*                                                    */
-  int32_t physical_slot; /* memory: g mod M; window: f mod R; current: index in the block  */
-  int64_t absolute_id;   /* memory: group g; window and current: absolute frame f         */
+  int32_t physical_slot; /* reference: index i; memory: g mod M; window: f mod R;
+                            current: index in the block                                   */
+  int64_t absolute_id;   /* reference: i; memory: group g; window and current: frame f     */
   int32_t t_pos;         /* reset temporal position: the rank in attention order          */
   int32_t reserved;
 } lact_key_frame;
@@ -97,6 +102,8 @@ typedef struct {
   uint64_t version;      /* +1 on every append and on every compress that consumed groups */
   int32_t staged_frames; /* current frames staged by the last lact_rope_reset_apply       */
   int32_t staged_valid;  /* 1 if that staging was done at the present version             */
+  int32_t ref_valid;     /* 1 once lact_ref_set has stored the reference segment           */
+  int32_t reserved;
 } lact_state;
 
 /* Offsets (bytes, 256-aligned) of the regions inside the single cache buffer, so a caller
@@ -104,23 +111,25 @@ typedef struct {
  * FP8_E4M3.
  *   ring_k/ring_v  [R][T][H][D] kv dtype            raw ring (pre-RoPE K, V)
  *   mem_k/mem_v    [M][T][H][D] kv dtype            compressed memory slots
- *   krot           [H][(M+W+B_max)*T][D] operand    rotated keys in attention order
+ *   ref_k/ref_v    [ref_frames][T][H][D] kv dtype   reference segment (pre-RoPE K, V)
+ *   krot           [H][(ref+M+W+B_max)*T][D] operand  rotated keys in attention order
  *   qrot           [H][B_max*T][D] operand          rotated queries of the block, times
  *                                                   log2(e)/sqrt(D) (the softmax scale
  *                                                   and the change to base 2)
  *   vcur           [B_max][T][H][D] operand         current V staged for attention
- *   vhist          [M+W][T][H][D] operand           FP8: memory + window V dequantised
- *   *_scale        f32 per (token, head): ring/mem [slots][T][H]
+ *   vhist          [ref+M+W][T][H][D] operand       FP8: reference + memory + window V
+ *                                                   dequantised, in attention order
+ *   *_scale        f32 per (token, head): ring/mem/ref [slots][T][H]
  *   rope_table     float2 (cos, sin) table
  *   attn_flags     int32 per (head, 256-row query tile): attention work queue of the exact
  *                  fallback pass (rows whose fast pass could not be trusted)
- * The persistent state is ring_* and mem_* (and their scales); the rest is rewritten by
+ * The persistent state is ring_*, mem_* and ref_* (and their scales); the rest is rewritten by
  * every step.  operand dtype = q_dtype: an FP8 cache is dequantised (code * scale) when the
  * RoPE pass stages a step, and attention runs on bf16 operands. */
 typedef struct {
   size_t total;
-  size_t ring_k, ring_v, mem_k, mem_v, krot, qrot, vcur, vhist;
-  size_t ring_k_scale, ring_v_scale, mem_k_scale, mem_v_scale;
+  size_t ring_k, ring_v, mem_k, mem_v, ref_k, ref_v, krot, qrot, vcur, vhist;
+  size_t ring_k_scale, ring_v_scale, mem_k_scale, mem_v_scale, ref_k_scale, ref_v_scale;
   size_t rope_table, attn_flags;
   size_t frame_bytes;    /* T*H*D * kv element size                                       */
   int32_t ring_slots, key_frames_max;
@@ -146,12 +155,26 @@ lact_status lact_cache_init(const lact_cfg* cfg, void* device_buf, size_t bytes,
 /* Frees the host handle only; the device buffer stays the caller's. NULL is a no-op. */
 lact_status lact_cache_destroy(lact_cache* cache);
 
+/* ---- the reference segment ------------------------------------------------------------- */
+
+/* Stores the reference segment: the KV of ref_frames frames (the reference image's part of
+ * the context; walkthrough, "ConvKV Memory": reference image, long-term memory, short-term
+ * window, current block) that every later step attends first, at the fixed temporal
+ * positions 0 .. ref_frames-1 (memory, window and block ranks follow them).  Stored like a
+ * ring frame: as given, bf16, or FP8_E4M3 quantised per (token, head).  May be called again
+ * to replace it.  Until it has been called, a cache with ref_frames > 0 refuses
+ * lact_rope_reset_apply with LACT_E_STATE.
+ *   k_ref, v_ref: [n_frames*T][H][D] in q_dtype (pre-RoPE K).  n_frames == ref_frames. */
+lact_status lact_ref_set(lact_cache* cache, const void* k_ref, const void* v_ref, int32_t n_frames,
+                         void* stream);
+
 /* ---- the four hot-path calls ----------------------------------------------------------- */
 
 /* RoPE reset + apply (fused).  Positions are reset from the present state (press release,
  * technical-principle paragraph: RoPE Reset; news summary, ConvKV Memory bullet):
- * memory rank j -> t = j; window rank k -> t = mem_len + k; current frame i ->
- * t = mem_len + win_len + i; (h, w) = the token's grid cell.  Rotation of interleaved
+ * reference frame i -> t = i; memory rank j -> t = ref + j; window rank k ->
+ * t = ref + mem_len + k; current frame i -> t = ref + mem_len + win_len + i (ref =
+ * ref_frames); (h, w) = the token's grid cell.  Rotation of interleaved
  * channel pairs (2i, 2i+1) of each part by pos * theta^(-2i/d_part).
  * Writes krot (memory + window + current keys), qrot and vcur in the operand dtype
  * (q_dtype).  The stored history is read as stored (FP8_E4M3: code * per-(token, head)

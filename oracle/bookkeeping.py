@@ -13,7 +13,10 @@ Follows the pages' statement of the memory:
 Readings (the pages are silent on them): the memory is a FIFO of groups, each group built
 once from r consecutive evicted frames; up to r-1 evicted frames wait as "pending" until
 their group is complete and are not attended; reset temporal positions are the ranks in
-[memory oldest..newest | window oldest..newest | current].
+[reference | memory oldest..newest | window oldest..newest | current].  The reference
+segment (walkthrough, "ConvKV Memory": the reference-image part of the context) is a
+fixed set of ref_frames frames that every step attends first, so its positions are
+always 0..ref_frames-1.
 """
 
 
@@ -25,11 +28,12 @@ class OracleCapacityError(Exception):
     pass
 
 
-SEG_MEMORY, SEG_WINDOW, SEG_CURRENT = 0, 1, 2
+SEG_MEMORY, SEG_WINDOW, SEG_CURRENT, SEG_REF = 0, 1, 2, 3
 
 
 class Bookkeeping:
-    def __init__(self, window_frames, mem_slots, ratio, max_block_frames):
+    def __init__(self, window_frames, mem_slots, ratio, max_block_frames, ref_frames=0):
+        self.ref = ref_frames
         self.W = window_frames
         self.M = mem_slots
         self.r = ratio
@@ -84,7 +88,7 @@ class Bookkeeping:
 
     def keys(self, n_cur):
         """Key frames in attention order: dicts with segment, slot, id, t_pos."""
-        out = []
+        out = [dict(segment=SEG_REF, slot=i, id=i) for i in range(self.ref)]
         if self.M > 0:
             for g in range(max(0, self.G - self.M), self.G):
                 out.append(dict(segment=SEG_MEMORY, slot=g % self.M, id=g))

@@ -15,7 +15,7 @@ The attention sees the exact stored values; the current block's q, k, v are used
 import numpy as np
 
 import oracle as O
-from oracle.bookkeeping import Bookkeeping, SEG_MEMORY
+from oracle.bookkeeping import Bookkeeping, SEG_MEMORY, SEG_REF
 
 F32, BF16, FP8 = 0, 1, 2
 
@@ -28,9 +28,10 @@ class OracleCache:
         self.C = self.H * self.D
         self.kv = cfg["kv_dtype"]
         self.bk = Bookkeeping(cfg["window_frames"], cfg["mem_slots"], cfg["ratio"],
-                              cfg["max_block_frames"])
+                              cfg["max_block_frames"], cfg.get("ref_frames", 0))
         self.raw = {}   # absolute frame -> (k, v) stored
         self.mem = {}   # memory slot -> (group, k, v) stored
+        self.ref = {}   # reference frame index -> (k, v) stored
 
     # ---- storage ---------------------------------------------------------------------
     def _store(self, x):
@@ -74,6 +75,12 @@ class OracleCache:
         assert bk_.G == G
         return oc
 
+    def set_ref(self, k_ref, v_ref):
+        """Reference segment: [ref_frames][T*C] float32 input values, stored like any frame."""
+        assert k_ref.shape[0] == self.bk.ref
+        for i in range(self.bk.ref):
+            self.ref[i] = (self._store(k_ref[i]), self._store(v_ref[i]))
+
     # ---- the four operations ---------------------------------------------------------
     def append(self, k_new, v_new):
         """k_new, v_new: [n][T*C] float32 input values."""
@@ -109,6 +116,8 @@ class OracleCache:
             if kf["segment"] == SEG_MEMORY:
                 g, sk, sv = self.mem[kf["slot"]]
                 assert g == kf["id"]
+            elif kf["segment"] == SEG_REF:
+                sk, sv = self.ref[kf["slot"]]
             else:
                 sk, sv = self.raw[kf["id"]]
             kv_, ksc = self.stored_value(sk)

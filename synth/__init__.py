@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 # Stream ids: one counter stream per (seed, tensor, frame).
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_WK, TENSOR_WV = 1, 2, 3, 4, 5
+TENSOR_REF_K, TENSOR_REF_V = 6, 7   # the reference segment's K and V
 TENSOR_SAMPLE = 8            # uniform stream used to pick sampled query rows
 OUTLIER_BASE = 16            # outlier mask of tensor t uses stream OUTLIER_BASE + t
 
@@ -120,6 +121,10 @@ WORKLOADS = {
                        train_blocks=(6, 8, 8, 8, 8, 8)),
 }
 
+# With the reference segment (the reference image's part of the context): 2 frames.
+WORKLOADS["tiny_ref"] = dict(WORKLOADS["tiny_f32"], ref_frames=2)
+WORKLOADS["s512_ref2"] = dict(WORKLOADS["s512_bf16"], ref_frames=2)
+
 # The memory-block / current-block grid of the model card's ablation table (Table 5):
 # window ("memory block") W and block B in frames, 512x512 shapes, memory 16 slots at 5:1.
 for _w, _b in ((6, 6), (8, 8), (6, 8)):
@@ -127,7 +132,8 @@ for _w, _b in ((6, 6), (8, 8), (6, 8)):
                                           max_block_frames=_b, first_block=_b, block=_b)
 
 CFG_KEYS = ("heads", "head_dim", "grid_h", "grid_w", "window_frames", "mem_slots", "ratio",
-            "max_block_frames", "kv_dtype", "q_dtype", "rope_mode", "rope_split", "rope_theta")
+            "max_block_frames", "kv_dtype", "q_dtype", "rope_mode", "rope_split", "rope_theta",
+            "ref_frames")
 
 
 def workload(name, **overrides):
@@ -160,6 +166,22 @@ def frames(w, seed, tensor, frame_ids):
         if w.get("outliers"):
             apply_outliers(out[i], seed, tensor, sf)
     return out
+
+
+def ref_frames(w, seed):
+    """The reference segment's K and V: [ref_frames][T*C] float32 each, N(0, 1) (x8 outliers
+    where the workload has them), from their own streams."""
+    ids = list(range(w.get("ref_frames", 0)))
+    n = w["tokens"] * w["channels"]
+    out = []
+    for tensor in (TENSOR_REF_K, TENSOR_REF_V):
+        x = np.empty((len(ids), n), dtype=np.float32)
+        for i in ids:
+            x[i] = normal(seed, tensor, i, n)
+            if w.get("outliers"):
+                apply_outliers(x[i], seed, tensor, i)
+        out.append(x)
+    return out[0], out[1]
 
 
 def conv_weights(w, seed, tensor):

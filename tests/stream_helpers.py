@@ -37,6 +37,19 @@ class Runner:
         self.d_wk, self.d_bk, self.d_wv, self.d_bv = map(dev, (self.wk, self.bk, self.wv, self.bv))
         self.f = 0
         self.step_index = 0
+        if w.get("ref_frames", 0):
+            self.set_ref()
+
+    def set_ref(self):
+        """The reference segment from its own seeded streams, on the device cache and the
+        oracle (the oracle gets the values as converted to the input dtype)."""
+        kr, vr = synth.ref_frames(self.w, self.seed)
+        n = kr.shape[0]
+        tk, tv = (torch.from_numpy(x.reshape(n * self.T, self.H, self.D)).to(io_dtype(self.w))
+                  for x in (kr, vr))
+        self.cache.ref_set(tk.cuda(), tv.cuda())
+        if self.oc is not None:
+            self.oc.set_ref(tk.float().numpy().reshape(n, -1), tv.float().numpy().reshape(n, -1))
 
     def inputs(self, n, tag=False):
         """(device tensor, host float32 values) for Q, K, V of frames f .. f+n-1."""
@@ -90,11 +103,13 @@ class Runner:
 
     def _hist_kmax(self):
         """Per head, the largest norm of a stored history key at the present state."""
-        from oracle.bookkeeping import SEG_MEMORY
+        from oracle.bookkeeping import SEG_MEMORY, SEG_REF
         kmax = np.zeros(self.H)
         for kf in self.oc.keys(0):
             if kf["segment"] == SEG_MEMORY:
                 sk = self.oc.mem[kf["slot"]][1]
+            elif kf["segment"] == SEG_REF:
+                sk = self.oc.ref[kf["slot"]][0]
             else:
                 sk = self.oc.raw[kf["id"]][0]
             vals, scales = self.oc.stored_value(sk)
@@ -125,6 +140,12 @@ class Runner:
         lay = self.cache.layout
         fb = lay.frame_bytes
         off = (lay.mem_k if tensor == 0 else lay.mem_v) + slot * fb
+        return self.cache.buf[off: off + fb].cpu().numpy()
+
+    def ref_slot_bytes(self, tensor, i):
+        lay = self.cache.layout
+        fb = lay.frame_bytes
+        off = (lay.ref_k if tensor == 0 else lay.ref_v) + i * fb
         return self.cache.buf[off: off + fb].cpu().numpy()
 
     def ring_slot_bytes(self, tensor, slot):

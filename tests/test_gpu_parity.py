@@ -80,6 +80,41 @@ def test_tiny_f32_stream_full_parity():
     say(f"tiny f32: worst rel L2 {worst:.2e} over 47 steps")
 
 
+def test_tiny_reference_stream_full_parity():
+    """Tiny f32 with a 2-frame reference segment: 27 history blocks then 20 AR steps, every
+    output row against the oracle, key table every step (reference first, positions 0, 1);
+    the reference, ring and memory contents bit-exact; the reference replaced halfway."""
+    w = synth.workload("tiny_ref")
+    run = Runner(w)
+    worst = 0.0
+    for s in range(w["history_blocks"] + w["steps"]):
+        if s == 30:
+            run.seed += 1          # a new reference segment: the next steps must see it
+            run.set_ref()
+            run.seed -= 1
+        assert_keys_match(run, 2)
+        res = run.step(2)
+        err, dl = run.compare_attention(res)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[F32] and dl <= LSE_TOL[F32], (s, err, dl)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    assert_ref_bitexact(run)
+    say(f"tiny reference stream: worst rel L2 {worst:.2e} over 47 steps")
+
+
+def test_s512_reference_step_parity():
+    """512x512-shaped bf16 with a 2-frame reference segment (Lk = 34 frames)."""
+    _big_step_parity("s512_ref2", 11, 8)
+
+
+def test_fp8_reference_step_parity():
+    """FP8 KV cache with a 2-frame reference segment (stored e4m3, dequantised by the RoPE
+    pass like the rest of the history)."""
+    _big_step_parity("fp8_kv", 11, 8, ref_frames=2)
+
+
 @pytest.mark.parametrize("blocks", [[1, 2, 3], [2, 2, 2], [3, 3], [6]])
 def test_tiny_multiblock_mask_vs_bruteforce(blocks):
     """Several query blocks in one call: the GPU's block-causal prefix against the oracle's
@@ -142,8 +177,18 @@ def assert_lse(run, res, kv):
         assert run.compare_attention(res)[1] <= LSE_TOL[kv]
 
 
-def _big_step_parity(name, warm, n_last, per_head=6, first_check=False):
-    w = synth.workload(name)
+def assert_ref_bitexact(run):
+    for i, (sk, sv) in sorted(run.oc.ref.items()):
+        for tensor, stored in ((0, sk), (1, sv)):
+            want, scales = run.oracle_stored_bytes(stored)
+            assert np.array_equal(run.ref_slot_bytes(tensor, i), want), f"reference frame {i}"
+            if scales is not None:
+                name = "ref_k_scale" if tensor == 0 else "ref_v_scale"
+                assert np.array_equal(run.scale_slot(name, i), scales), f"scales of reference {i}"
+
+
+def _big_step_parity(name, warm, n_last, per_head=6, first_check=False, **overrides):
+    w = synth.workload(name, **overrides)
     run = Runner(w)
     kv = w["kv_dtype"]
     sizes = synth.block_sizes(w, warm + 1)
@@ -162,6 +207,7 @@ def _big_step_parity(name, warm, n_last, per_head=6, first_check=False):
         assert_state_matches(run)
     assert_memory_bitexact(run)
     assert_ring_bitexact(run)
+    assert_ref_bitexact(run)
     assert_keys_match(run, n_last)
     sel = sample_rows(w, n_last, seed=99, per_head=per_head)
     res = run.step(n_last, sel=sel)

@@ -40,10 +40,11 @@ def test_footprint_is_pure_and_matches_layout():
         w = synth.workload(name)
         R = w["window_frames"] + w["max_block_frames"] + w["ratio"] - 1
         assert lay.ring_slots == R
-        assert lay.key_frames_max == w["mem_slots"] + w["window_frames"] + w["max_block_frames"]
+        ref = w.get("ref_frames", 0)
+        assert lay.key_frames_max == ref + w["mem_slots"] + w["window_frames"] + w["max_block_frames"]
         esize = {0: 4, 1: 2, 2: 1}[w["kv_dtype"]]
         assert lay.frame_bytes == w["tokens"] * w["channels"] * esize
-        names = ("ring_k", "ring_v", "mem_k", "mem_v", "krot", "qrot", "vcur", "vhist")
+        names = ("ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v", "krot", "qrot", "vcur", "vhist")
         offs = [getattr(lay, n) for n in names]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         # staged operands are in the q dtype; FP8 adds the dequantised history V
@@ -52,7 +53,7 @@ def test_footprint_is_pure_and_matches_layout():
         assert lay.qrot - lay.krot >= ob * KF and lay.vcur - lay.qrot >= ob * w["max_block_frames"]
         if w["kv_dtype"] == 2:
             assert lay.vhist - lay.vcur >= ob * w["max_block_frames"]
-            assert lay.ring_k_scale - lay.vhist >= ob * (w["mem_slots"] + w["window_frames"])
+            assert lay.ring_k_scale - lay.vhist >= ob * (ref + w["mem_slots"] + w["window_frames"])
         else:
             assert lay.ring_k_scale == 0 and lay.vhist == lay.rope_table
     # 512x512 bf16: 2R + 2M + KF + 2 B_max = 120 frames of 10 MiB, plus the small tables
@@ -66,7 +67,8 @@ def test_footprint_is_pure_and_matches_layout():
     (dict(mem_slots=200, window_frames=50, max_block_frames=8), 3),
     (dict(kv_dtype=0, q_dtype=1), 4), (dict(kv_dtype=2, q_dtype=0), 4),
     (dict(rope_split=(44, 42, 40)), 2), (dict(rope_split=(43, 43, 42)), 2), (dict(rope_mode=2), 2),
-    (dict(rope_theta=0.5), 1),
+    (dict(rope_theta=0.5), 1), (dict(ref_frames=-1), 2),
+    (dict(ref_frames=100, mem_slots=100, window_frames=50, max_block_frames=8), 3),
 ])
 def test_config_validation(kw, status):
     with pytest.raises(L.LactError) as e:
@@ -79,7 +81,8 @@ def _planner_matches_oracle(name, steps):
     w = synth.workload(name)
     cfg = L.make_cfg(**w)
     plan = L.Plan(cfg)
-    bk = Bookkeeping(w["window_frames"], w["mem_slots"], w["ratio"], w["max_block_frames"])
+    bk = Bookkeeping(w["window_frames"], w["mem_slots"], w["ratio"], w["max_block_frames"],
+                     w.get("ref_frames", 0))
     for s in range(steps):
         n = w["first_block"] if s == 0 else w["block"]
         got, want = plan.state(), bk.state()
@@ -203,6 +206,28 @@ def test_cache_init_checks():
                                ctypes.byref(out)) == 3          # too small
     assert lib.lact_cache_init(ctypes.byref(cfg), None, nbytes, ctypes.byref(out)) == 1
     assert lib.lact_cache_destroy(None) == 0
+
+
+def test_reference_segment_checks():
+    """lact_ref_set: refused on a cache without a reference segment and for a wrong frame
+    count; a cache with one refuses the RoPE pass until it is set; the key table starts with
+    the reference frames at positions 0 .. ref_frames-1."""
+    lib = L.lib()
+    dev = ctypes.c_void_p(0x20000000)
+    c = _HostOnlyCache("tiny_f32")
+    assert lib.lact_ref_set(c.h, dev, dev, 2, None) == 5          # no reference segment
+    c.close()
+    c = _HostOnlyCache("tiny_ref")
+    assert lib.lact_ref_set(c.h, dev, dev, 1, None) == 2          # ref_frames is 2
+    assert lib.lact_ref_set(c.h, None, dev, 2, None) == 1
+    assert lib.lact_rope_reset_apply(c.h, dev, dev, dev, 2, None) == 5
+    assert "reference" in lib.lact_last_error().decode()
+    assert L.lact_cache_state(c.h)["ref_valid"] == 0
+    keys = L.lact_cache_keys(c.h, 2)
+    assert [(k["segment"], k["t_pos"], k["slot"]) for k in keys] == \
+        [(L.SEG_REF, 0, 0), (L.SEG_REF, 1, 1), (L.SEG_CURRENT, 2, 0),
+         (L.SEG_CURRENT, 3, 1)]
+    c.close()
 
 
 def test_multiblock_argument_checks():

@@ -610,3 +610,69 @@ def test_stream_at_state_equals_sequential_stream():
                 assert np.array_equal(ff.mem[slot][2][1], seq.mem[slot][2][1])
             for f in range(seq.bk.E, seq.bk.F):
                 assert np.array_equal(ff.raw[f][0][1], seq.raw[f][0][1])
+
+
+# ---- reference segment -------------------------------------------------------------------
+
+def test_reference_keys_hand_table():
+    """Reference segment of 2 frames, window 4, memory 10 at 5:1, blocks of 2: after 27
+    blocks (54 frames appended, 50 evicted, groups 0..9 compressed) the key table of a
+    2-frame block, written out by hand."""
+    bk = Bookkeeping(4, 10, 5, 2, ref_frames=2)
+    for _ in range(27):
+        bk.append(2)
+        bk.compress()
+    got = [(k["segment"], k["slot"], k["id"], k["t_pos"]) for k in bk.keys(2)]
+    want = ([(3, 0, 0, 0), (3, 1, 1, 1)] +
+            [(0, g, g, 2 + g) for g in range(10)] +
+            [(1, 0, 50, 12), (1, 1, 51, 13), (1, 2, 52, 14), (1, 3, 53, 15)] +   # R = 10 slots
+            [(2, 0, 54, 16), (2, 1, 55, 17)])
+    assert got == want
+
+
+def test_reference_positions_fixed_and_bounded():
+    """Over 1000 steps the reference frames keep positions 0 and 1, come first, and every
+    position stays below ref + M + W + B_max."""
+    bk = Bookkeeping(8, 16, 5, 8, ref_frames=2)
+    for _ in range(1000):
+        keys = bk.keys(8)
+        assert [(k["segment"], k["t_pos"]) for k in keys[:2]] == [(3, 0), (3, 1)]
+        assert all(k["segment"] != 3 for k in keys[2:])
+        assert max(k["t_pos"] for k in keys) < 2 + 16 + 8 + 8
+        bk.append(8)
+        bk.compress()
+
+
+def test_reference_zero_query_is_mean_of_visible_values():
+    """Closed form with a reference segment: q = 0 makes every visible score equal, so each
+    row's output is the plain mean of the V rows it sees -- both reference frames, the
+    window and the block frames up to its own -- and its LSE is log(count).  Window-only
+    memory (M = 0) keeps every stored value equal to its input."""
+    w = synth.workload("tiny_f32", ref_frames=2, mem_slots=0, window_frames=3, max_block_frames=3)
+    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    oc = OracleCache(w)
+    rng = np.random.default_rng(5)
+    kr, vr = (rng.standard_normal((2, T * H * D)).astype(np.float32) for _ in range(2))
+    oc.set_ref(kr, vr)
+    frames_v = {}
+    for f0 in (0, 2, 4):                      # 6 frames appended; window = frames 3..5
+        k = rng.standard_normal((2, T * H * D)).astype(np.float32)
+        v = rng.standard_normal((2, T * H * D)).astype(np.float32)
+        for i in range(2):
+            frames_v[f0 + i] = v[i]
+        oc.append(k, v)
+        zw, zb = np.zeros((H * D, 5), np.float32), np.zeros(H * D, np.float32)
+        oc.compress(zw, zb, zw, zb)           # M = 0: evicted groups are dropped
+    q = np.zeros((3 * T, H, D), np.float32)
+    kc = rng.standard_normal((3 * T, H, D)).astype(np.float32)
+    vc = rng.standard_normal((3 * T, H, D)).astype(np.float32)
+    O_, LSE, heads, rows = oc.attention(q, kc, vc, block_frames=[1, 2])
+    hist_v = np.concatenate([vr.reshape(2 * T, H, D)] +
+                            [frames_v[f].reshape(T, H, D) for f in (3, 4, 5)])
+    for blk, n_cur in ((0, 1), (1, 3)):
+        visible = np.concatenate([hist_v, vc[: n_cur * T]]).astype(np.float64)
+        mean = visible.mean(axis=0)                       # [H][D]
+        sel = np.where((rows >= (0 if blk == 0 else T)) & (rows < (T if blk == 0 else 3 * T)))[0]
+        for i in sel:
+            np.testing.assert_allclose(O_[i], mean[heads[i]], rtol=0, atol=1e-12)
+            assert abs(LSE[i] - math.log(visible.shape[0])) < 1e-12
