@@ -82,6 +82,8 @@ def main():
     w = synth.workload(args.workload)
     if w.get("train_blocks"):
         return train_main(args, w)
+    if w.get("members", 1) > 1:
+        return set_main(args, w)
     T, H, D = w["tokens"], w["heads"], w["head_dim"]
     B = w["block"]
     dt = {0: "f32", 1: "bf16", 2: "fp8"}[w["kv_dtype"]]   # storage of the cache
@@ -321,6 +323,129 @@ def train_main(args, w):
             "sample": (f"attention of all {H} heads x {len(rows)} query rows over their visible "
                        f"keys ({secs:.1f} s, double precision), extrapolated by visible key "
                        f"pairs (x{1 / frac:.0f}) to the whole call; RoPE not counted")}
+    print(json.dumps(rec), flush=True)
+
+
+def set_main(args, w):
+    """A set of caches, one per (layer, denoising step), at model scale: per AR block every
+    member runs RoPE + attention over its own history, then one append launch and one
+    compress launch advance all members.  Timed per block."""
+    import torch
+    import compressed_kv_causal_amd as L
+    import synth
+    T, H, D, B = w["tokens"], w["heads"], w["head_dim"], w["block"]
+    nm = w["members"]
+    dt = {0: "f32", 1: "bf16", 2: "fp8"}[w["kv_dtype"]]
+    io = torch.float32 if w["q_dtype"] == 0 else torch.bfloat16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = L.make_cfg(**w)
+    set_bytes = L.lact_set_footprint(cfg, nm)
+    solo_bytes = L.lact_cache_footprint(cfg)
+    cache = L.Cache(cfg, device=dev, members=nm)
+    # inputs resident in HBM: a pool of seeded blocks; member m's block is pool block m mod P,
+    # and the K, V of all members for the batched append are stacked once, before timing
+    pool = []
+    for blk in range(args.pool_blocks):
+        ids = list(range(blk * B, (blk + 1) * B))
+        pool.append([torch.from_numpy(synth.frames(w, args.seed, t, ids).reshape(B * T, H, D))
+                     .to(io).to(dev) for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V)])
+    P = len(pool)
+    k_all = torch.stack([pool[m % P][1] for m in range(nm)]).reshape(nm * B * T, H, D)
+    v_all = torch.stack([pool[m % P][2] for m in range(nm)]).reshape(nm * B * T, H, D)
+    wts = [synth.conv_weights(w, args.seed + m, synth.TENSOR_WK) + synth.conv_weights(w, args.seed + m, synth.TENSOR_WV)
+           for m in range(nm)]
+    d_wk, d_bk, d_wv, d_bv = (torch.from_numpy(np.stack([x[i] for x in wts])).to(dev) for i in range(4))
+    Lq = B * T
+    out = torch.empty((Lq, H, D), dtype=io, device=dev)
+    stream = torch.cuda.current_stream()
+    h = cache.h
+    kview = k_all.view(nm, B * T, H, D)
+    vview = v_all.view(nm, B * T, H, D)
+
+    def advance():
+        L.lact_kv_ring_append(h, k_all, v_all, B, stream)
+        L.lact_convkv_compress(h, d_wk, d_bk, d_wv, d_bv, stream)
+
+    def block(ev=None):
+        for m in range(nm):
+            if ev is not None:
+                ev[0][m].record(stream)
+            L.lact_member_rope_reset_apply(h, m, pool[m % P][0], kview[m], vview[m], B, stream)
+            if ev is not None:
+                ev[1][m].record(stream)
+            L.lact_member_block_attention(h, m, None, out, None, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        L.lact_kv_ring_append(h, k_all, v_all, B, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        L.lact_convkv_compress(h, d_wk, d_bk, d_wv, d_bv, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    # fill the memory with the batched append + compress alone (attention changes no state)
+    while True:
+        st = cache.state()
+        if st["mem_len"] == w["mem_slots"] and st["win_len"] == w["window_frames"]:
+            break
+        advance()
+    for _ in range(args.warmup):
+        block()
+    torch.cuda.synchronize()
+    n_hist = cache.state()["mem_len"] + cache.state()["win_len"]
+    Lk = (n_hist + B) * T
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[[E() for _ in range(nm)], [E() for _ in range(nm)], E(), E(), E()]
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        block(evs[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rope_ms = np.mean([sum(e[0][m].elapsed_time(e[1][m]) for m in range(nm)) for e in evs])
+    attn_ms = np.mean([sum(e[1][m].elapsed_time(e[0][m + 1]) for m in range(nm - 1)) +
+                       e[1][nm - 1].elapsed_time(e[2]) for e in evs])
+    app_ms = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    cmp_ms = np.mean([e[3].elapsed_time(e[4]) for e in evs])
+    ms_block = wall * 1e3 / args.steps
+    fe = T * H * D
+    kvb = {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+    ob = 4 if w["q_dtype"] == 0 else 2
+    sb = T * H * 4 if dt == "fp8" else 0
+    append_bytes = nm * 2 * B * (fe * (ob + kvb) + sb)
+    compress_bytes = nm * (B / w["ratio"]) * 2 * (fe * kvb + sb) * (w["ratio"] + 1)
+    attn_flop = 4.0 * Lq * Lk * D * H * nm
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    peak = PEAK["f32" if w["q_dtype"] == 0 else "bf16"]
+    rec = {
+        "metric": METRIC,
+        "value": round(B / (ms_block * 1e-3), 3),
+        "unit": f"latent frames/s (all {nm} caches of the set: layers x denoising steps, steady state)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_block, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if w["q_dtype"] == 0 else "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, N(0,0.2) conv weights per member)",
+        "config": {"workload": args.workload, "members": nm, "kv_storage": dt, "heads": H,
+                   "head_dim": D, "tokens_per_frame": T, "block_frames": B,
+                   "window_frames": w["window_frames"], "mem_slots": w["mem_slots"],
+                   "ratio": w["ratio"], "Lq": Lq, "Lk": Lk},
+        "footprint_gib": {"set": round(set_bytes / 2 ** 30, 2),
+                          "independent_caches": round(nm * solo_bytes / 2 ** 30, 2)},
+        "attn_tflops": round(attn_tflops, 2),
+        "step_breakdown_ms": {"rope_reset_apply_all_members": round(rope_ms, 3),
+                              "block_attention_all_members": round(attn_ms, 3),
+                              "kv_ring_append_batched": round(app_ms, 3),
+                              "convkv_compress_batched": round(cmp_ms, 3),
+                              "per_member": round(ms_block / nm, 4)},
+        "stream_gbs": {"kv_ring_append_batched": round(append_bytes / (app_ms * 1e-3) / 1e9, 1),
+                       "convkv_compress_batched": round(compress_bytes / (cmp_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "kernel": "k_attn (block attention, all members)",
+                     "algorithmic_per_launch": f"{attn_flop / nm:.4e} flop = 4*Lq*Lk*D*H"},
+        "cpu_baseline": None,
+    }
     print(json.dumps(rec), flush=True)
 
 

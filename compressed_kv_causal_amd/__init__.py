@@ -5,8 +5,9 @@ ABI of ``include/lact.h``; torch provides device memory and streams.  If liblact
 missing, every call raises -- there is no fallback path.
 
 The functions carry the C names: ``lact_rope_reset_apply``, ``lact_block_attention``,
-``lact_kv_ring_append``, ``lact_convkv_compress`` and the sizing, lifetime, inspection
-and planner calls.  ``Cache`` bundles one cache buffer and handle for convenience.
+``lact_kv_ring_append``, ``lact_convkv_compress``, their ``lact_member_*`` forms for cache
+sets, and the sizing, lifetime, inspection and planner calls.  ``Cache`` bundles one cache
+buffer (or a set of ``members`` caches in one buffer) and its handle for convenience.
 """
 import ctypes
 import os
@@ -19,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "liblact.so")
 LACT_F32, LACT_BF16, LACT_FP8_E4M3 = 0, 1, 2
 LACT_MAX_KEY_FRAMES = 256
 LACT_MAX_Q_BLOCKS = 16
+LACT_MAX_MEMBERS = 1024
 SEG_MEMORY, SEG_WINDOW, SEG_CURRENT, SEG_REF = 0, 1, 2, 3
 STATUS = {0: "LACT_OK", 1: "LACT_E_INVALID", 2: "LACT_E_SHAPE", 3: "LACT_E_CAPACITY",
           4: "LACT_E_DTYPE", 5: "LACT_E_STATE", 6: "LACT_E_HIP"}
@@ -48,8 +50,11 @@ class lact_state(ctypes.Structure):
                 ("pending", ctypes.c_int32), ("ring_slots", ctypes.c_int32),
                 ("version", ctypes.c_uint64), ("staged_frames", ctypes.c_int32),
                 ("staged_valid", ctypes.c_int32), ("ref_valid", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("staged_member", ctypes.c_int32)]
 
+
+_PERSISTENT = ("ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v", "ring_k_scale",
+               "ring_v_scale", "mem_k_scale", "mem_v_scale", "ref_k_scale", "ref_v_scale")
 
 _LAYOUT_FIELDS = ["total", "ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v", "krot", "qrot",
                   "vcur", "vhist", "ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale",
@@ -58,7 +63,9 @@ _LAYOUT_FIELDS = ["total", "ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v
 
 class lact_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS] + \
-               [("ring_slots", ctypes.c_int32), ("key_frames_max", ctypes.c_int32)]
+               [("ring_slots", ctypes.c_int32), ("key_frames_max", ctypes.c_int32),
+                ("member_bytes", ctypes.c_size_t), ("members", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class LactError(RuntimeError):
@@ -68,7 +75,10 @@ class LactError(RuntimeError):
 
 
 EXPORTS = ["lact_cache_footprint", "lact_cache_layout", "lact_cache_init", "lact_cache_destroy",
-           "lact_ref_set", "lact_rope_reset_apply", "lact_block_attention", "lact_kv_ring_append",
+           "lact_set_footprint", "lact_set_layout", "lact_set_init",
+           "lact_ref_set", "lact_rope_reset_apply", "lact_block_attention",
+           "lact_member_ref_set", "lact_member_rope_reset_apply", "lact_member_block_attention",
+           "lact_kv_ring_append",
            "lact_convkv_compress", "lact_cache_state", "lact_cache_keys", "lact_plan_create",
            "lact_plan_destroy", "lact_plan_append", "lact_plan_compress", "lact_plan_state",
            "lact_plan_keys", "lact_last_error"]
@@ -91,9 +101,15 @@ def lib():
         "lact_cache_layout": [P(lact_cfg), P(lact_layout)],
         "lact_cache_init": [P(lact_cfg), vp, ctypes.c_size_t, P(vp)],
         "lact_cache_destroy": [vp],
+        "lact_set_footprint": [P(lact_cfg), i32, P(ctypes.c_size_t)],
+        "lact_set_layout": [P(lact_cfg), i32, P(lact_layout)],
+        "lact_set_init": [P(lact_cfg), i32, vp, ctypes.c_size_t, P(vp)],
         "lact_ref_set": [vp, vp, vp, i32, vp],
         "lact_rope_reset_apply": [vp, vp, vp, vp, i32, vp],
         "lact_block_attention": [vp, P(i32), i32, vp, vp, vp],
+        "lact_member_ref_set": [vp, i32, vp, vp, i32, vp],
+        "lact_member_rope_reset_apply": [vp, i32, vp, vp, vp, i32, vp],
+        "lact_member_block_attention": [vp, i32, P(i32), i32, vp, vp, vp],
         "lact_kv_ring_append": [vp, vp, vp, i32, vp],
         "lact_convkv_compress": [vp, vp, vp, vp, vp, vp, P(i32)],
         "lact_cache_state": [vp, P(lact_state)],
@@ -177,17 +193,39 @@ def lact_cache_destroy(h):
     _check(lib().lact_cache_destroy(h))
 
 
+def lact_set_footprint(cfg, n_members):
+    n = ctypes.c_size_t()
+    _check(lib().lact_set_footprint(ctypes.byref(cfg), n_members, ctypes.byref(n)))
+    return n.value
+
+
+def lact_set_layout(cfg, n_members):
+    L = lact_layout()
+    _check(lib().lact_set_layout(ctypes.byref(cfg), n_members, ctypes.byref(L)))
+    return L
+
+
+def lact_set_init(cfg, n_members, device_buf_ptr, nbytes):
+    h = ctypes.c_void_p()
+    _check(lib().lact_set_init(ctypes.byref(cfg), n_members, ctypes.c_void_p(device_buf_ptr),
+                               nbytes, ctypes.byref(h)))
+    return h
+
+
 def lact_rope_reset_apply(h, q, k_cur, v_cur, n_frames, stream=None):
     _check(lib().lact_rope_reset_apply(h, _ptr(q, name="q"), _ptr(k_cur, name="k_cur"),
                                        _ptr(v_cur, name="v_cur"), n_frames, _stream(stream)))
 
 
-def lact_block_attention(h, q_block_frames, out, lse=None, stream=None):
+def _blocks(q_block_frames):
     if q_block_frames is None:
-        arr, n = None, 0
-    else:
-        n = len(q_block_frames)
-        arr = (ctypes.c_int32 * n)(*q_block_frames)
+        return None, 0
+    n = len(q_block_frames)
+    return (ctypes.c_int32 * n)(*q_block_frames), n
+
+
+def lact_block_attention(h, q_block_frames, out, lse=None, stream=None):
+    arr, n = _blocks(q_block_frames)
     lse_p = _ptr(lse, torch.float32, "lse") if lse is not None else None
     _check(lib().lact_block_attention(h, arr, n, _ptr(out, name="out"), lse_p, _stream(stream)))
 
@@ -195,6 +233,24 @@ def lact_block_attention(h, q_block_frames, out, lse=None, stream=None):
 def lact_ref_set(h, k_ref, v_ref, n_frames, stream=None):
     _check(lib().lact_ref_set(h, _ptr(k_ref, name="k_ref"), _ptr(v_ref, name="v_ref"), n_frames,
                               _stream(stream)))
+
+
+def lact_member_rope_reset_apply(h, member, q, k_cur, v_cur, n_frames, stream=None):
+    _check(lib().lact_member_rope_reset_apply(h, member, _ptr(q, name="q"),
+                                              _ptr(k_cur, name="k_cur"), _ptr(v_cur, name="v_cur"),
+                                              n_frames, _stream(stream)))
+
+
+def lact_member_block_attention(h, member, q_block_frames, out, lse=None, stream=None):
+    arr, n = _blocks(q_block_frames)
+    lse_p = _ptr(lse, torch.float32, "lse") if lse is not None else None
+    _check(lib().lact_member_block_attention(h, member, arr, n, _ptr(out, name="out"), lse_p,
+                                             _stream(stream)))
+
+
+def lact_member_ref_set(h, member, k_ref, v_ref, n_frames, stream=None):
+    _check(lib().lact_member_ref_set(h, member, _ptr(k_ref, name="k_ref"),
+                                     _ptr(v_ref, name="v_ref"), n_frames, _stream(stream)))
 
 
 def lact_kv_ring_append(h, k_new, v_new, n_frames, stream=None):
@@ -267,14 +323,24 @@ class Plan:
 
 
 class Cache:
-    """One ConvKV cache: a device buffer of lact_cache_footprint bytes plus its handle."""
+    """One ConvKV cache, or a set of ``members`` caches advanced together (one per layer and
+    diffusion step): a device buffer of lact_set_footprint bytes plus its handle.  With one
+    member the plain calls are used, with several the lact_member_* forms (``member=``)."""
 
-    def __init__(self, cfg, device="cuda"):
+    def __init__(self, cfg, device="cuda", members=1):
         self.cfg = cfg if isinstance(cfg, lact_cfg) else make_cfg(**cfg)
-        self.nbytes = lact_cache_footprint(self.cfg)
-        self.layout = lact_cache_layout(self.cfg)
+        self.members = members
+        if members == 1:
+            self.nbytes = lact_cache_footprint(self.cfg)
+            self.layout = lact_cache_layout(self.cfg)
+        else:
+            self.nbytes = lact_set_footprint(self.cfg, members)
+            self.layout = lact_set_layout(self.cfg, members)
         self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
-        self.h = lact_cache_init(self.cfg, self.buf.data_ptr(), self.nbytes)
+        if members == 1:
+            self.h = lact_cache_init(self.cfg, self.buf.data_ptr(), self.nbytes)
+        else:
+            self.h = lact_set_init(self.cfg, members, self.buf.data_ptr(), self.nbytes)
         c = self.cfg
         self.T = c.grid_h * c.grid_w
         self.H, self.D = c.heads, c.head_dim
@@ -294,23 +360,35 @@ class Cache:
             pass
 
     # the four hot-path calls
-    def rope_reset_apply(self, q, k_cur, v_cur, stream=None):
+    def rope_reset_apply(self, q, k_cur, v_cur, stream=None, member=0):
         n = q.shape[0] // self.T
-        lact_rope_reset_apply(self.h, q, k_cur, v_cur, n, stream)
+        if self.members == 1 and member == 0:
+            lact_rope_reset_apply(self.h, q, k_cur, v_cur, n, stream)
+        else:
+            lact_member_rope_reset_apply(self.h, member, q, k_cur, v_cur, n, stream)
 
-    def block_attention(self, q_block_frames=None, out=None, lse=None, stream=None):
+    def block_attention(self, q_block_frames=None, out=None, lse=None, stream=None, member=0):
         st = self.state()
         Lq = st["staged_frames"] * self.T
         if out is None:
             out = torch.empty((Lq, self.H, self.D), dtype=self.io_dtype, device=self.buf.device)
-        lact_block_attention(self.h, q_block_frames, out, lse, stream)
+        if self.members == 1 and member == 0:
+            lact_block_attention(self.h, q_block_frames, out, lse, stream)
+        else:
+            lact_member_block_attention(self.h, member, q_block_frames, out, lse, stream)
         return out
 
-    def ref_set(self, k_ref, v_ref, stream=None):
-        lact_ref_set(self.h, k_ref, v_ref, k_ref.shape[0] // self.T, stream)
+    def ref_set(self, k_ref, v_ref, stream=None, member=0):
+        n = k_ref.shape[0] // self.T
+        if self.members == 1 and member == 0:
+            lact_ref_set(self.h, k_ref, v_ref, n, stream)
+        else:
+            lact_member_ref_set(self.h, member, k_ref, v_ref, n, stream)
 
     def kv_ring_append(self, k_new, v_new, stream=None):
-        lact_kv_ring_append(self.h, k_new, v_new, k_new.shape[0] // self.T, stream)
+        """k_new, v_new: [members * n * T, H, D] (members stacked) or [n * T, H, D]."""
+        lact_kv_ring_append(self.h, k_new, v_new, k_new.shape[0] // (self.T * self.members),
+                            stream)
 
     def convkv_compress(self, w_k, b_k, w_v, b_v, stream=None):
         return lact_convkv_compress(self.h, w_k, b_k, w_v, b_v, stream)
@@ -322,8 +400,10 @@ class Cache:
         return lact_cache_keys(self.h, n_cur)
 
     # views into the buffer (inspection / tests)
-    def region(self, name, slots, dtype, per_slot_elems):
+    def region(self, name, slots, dtype, per_slot_elems, member=0):
         off = getattr(self.layout, name)
+        if name in _PERSISTENT:
+            off += member * self.layout.member_bytes
         itemsize = torch.empty((), dtype=dtype).element_size()
         n = slots * per_slot_elems
         return self.buf[off: off + n * itemsize].view(dtype).view(slots, per_slot_elems)

@@ -19,21 +19,24 @@ namespace lact {
 // ---------------------------------------------------------------------------------------
 template <int LPR>
 __global__ __launch_bounds__(256) void k_ring_write(const RingWriteArgs a) {
-  // blockIdx.y = frame of the block, blockIdx.z = tensor (K, V); rows of a frame are
-  // (token, head) pairs, LPR lanes each
+  // blockIdx.y = frame of the block, blockIdx.z = (member, tensor K or V); rows of a frame
+  // are (token, head) pairs, LPR lanes each
   const int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
   const int32_t rows = a.T * a.H;
   const int32_t row = e / LPR, li = e % LPR;
   if (row >= rows) return;
-  const int32_t fi = blockIdx.y, tensor = blockIdx.z;
+  const int32_t fi = blockIdx.y, tensor = blockIdx.z & 1, m = blockIdx.z >> 1;
+  const void* src = static_cast<const char*>(a.src[tensor]) + m * a.src_mstride;
+  void* ring = static_cast<char*>(a.ring[tensor]) + m * a.ring_mstride;
   int32_t slot = a.slot0 + fi;
   if (slot >= a.R) slot -= a.R;
   const int64_t srow = (int64_t)fi * rows + row;
   const int64_t drow = (int64_t)slot * rows + row;
   float x[8];
-  load8_in(a.src[tensor], a.in_dtype, srow * a.D + li * 8, x);
-  const float s = store8_kv<LPR>(a.ring[tensor], a.kv_dtype, drow * a.D + li * 8, x);
-  if (a.kv_dtype == DT_FP8 && li == 0) a.ring_scale[tensor][drow] = s;
+  load8_in(src, a.in_dtype, srow * a.D + li * 8, x);
+  const float s = store8_kv<LPR>(ring, a.kv_dtype, drow * a.D + li * 8, x);
+  if (a.kv_dtype == DT_FP8 && li == 0)
+    reinterpret_cast<float*>(reinterpret_cast<char*>(a.ring_scale[tensor]) + m * a.ring_mstride)[drow] = s;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -45,8 +48,38 @@ __global__ __launch_bounds__(256) void k_ring_write(const RingWriteArgs a) {
 // ---------------------------------------------------------------------------------------
 // Work split: a workgroup is one wave; lane = one 8-channel chunk of 64 consecutive chunks
 // (blockIdx.x), so a wave reads and writes 1 KiB contiguous per token and frame (512 B for
-// FP8); blockIdx.y = a run of TOK tokens, blockIdx.z = (group, tensor).  D/8 lanes form one
-// (token, head) row, which is what the FP8 row quantiser reduces over.
+// FP8); blockIdx.y = a run of TOK tokens, blockIdx.z = (member, group, tensor).  D/8 lanes
+// form one (token, head) row, which is what the FP8 row quantiser reduces over.
+struct CompressPtrs {
+  const char* ring;
+  const float* ring_scale;
+  char* mem;
+  float* mem_scale;
+  const float* w;
+  const float* b;
+  int gi;
+};
+
+// blockIdx.z -> the group and this member's tensors
+__device__ __forceinline__ CompressPtrs compress_ptrs(const CompressArgs& a) {
+  const int tensor = blockIdx.z & 1;
+  const int mg = blockIdx.z >> 1;
+  const int m = mg / a.n_groups;
+  CompressPtrs p;
+  p.gi = mg - m * a.n_groups;
+  const int64_t mb = m * a.mstride;
+  p.ring = static_cast<const char*>(a.ring[tensor]) + mb;
+  p.mem = static_cast<char*>(a.mem[tensor]) + mb;
+  p.ring_scale = nullptr;
+  p.mem_scale = nullptr;
+  if (a.kv_dtype == DT_FP8) {
+    p.ring_scale = reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.ring_scale[tensor]) + mb);
+    p.mem_scale = reinterpret_cast<float*>(reinterpret_cast<char*>(a.mem_scale[tensor]) + mb);
+  }
+  p.w = a.w[tensor] + m * a.w_mstride;
+  p.b = a.b[tensor] + m * a.b_mstride;
+  return p;
+}
 //
 // k_compress_r: the ratio is a compile-time R.  The lane keeps its 8 x R weights and 8
 // biases in registers and issues every load of its TOK tokens x R frames before the first
@@ -58,11 +91,12 @@ __global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
   using Raw = typename std::conditional<KV == DT_FP8, uint2, uint4>::type;  // 8 stored elements
   const int32_t C = a.H * a.D;
   const int32_t c0 = (blockIdx.x * 64 + threadIdx.x) * 8;  // first channel of this lane
-  const int gi = blockIdx.z >> 1, tensor = blockIdx.z & 1;
   if (c0 >= C) return;                                     // whole LPR groups leave together
+  const CompressPtrs p = compress_ptrs(a);
+  const int gi = p.gi;
   const int32_t u0 = blockIdx.y * TOK;
   const int32_t rows = a.T * a.H;
-  const char* ring = static_cast<const char*>(a.ring[tensor]);
+  const char* ring = p.ring;
   constexpr int EB = KV == DT_FP8 ? 1 : 2;                 // stored bytes per element
 
   Raw raw[TOK][R];
@@ -81,14 +115,14 @@ __global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
     for (int k = 0; k < R; ++k) {
       const int64_t el = (int64_t)slot[k] * a.T * C + (int64_t)u * C + c0;
       raw[t][k] = *reinterpret_cast<const Raw*>(ring + el * EB);
-      sc[t][k] = KV == DT_FP8 ? a.ring_scale[tensor][(int64_t)slot[k] * rows + hrow] : 1.0f;
+      sc[t][k] = KV == DT_FP8 ? p.ring_scale[(int64_t)slot[k] * rows + hrow] : 1.0f;
     }
   }
   float w[8][R], b[8];
-  const float* wp = a.w[tensor] + (int64_t)c0 * R;
+  const float* wp = p.w + (int64_t)c0 * R;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    b[e] = a.b[tensor][c0 + e];
+    b[e] = p.b[c0 + e];
 #pragma unroll
     for (int k = 0; k < R; ++k) w[e][k] = wp[e * R + k];
   }
@@ -116,9 +150,9 @@ __global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
     }
     if (u >= a.T) continue;        // uniform per LPR group: a row's lanes share u
     const int64_t dst = (int64_t)a.out_slot[gi] * a.T * C + (int64_t)u * C + c0;
-    const float s = store8_kv<LPR>(a.mem[tensor], KV, dst, acc);
+    const float s = store8_kv<LPR>(p.mem, KV, dst, acc);
     if (KV == DT_FP8 && (threadIdx.x % LPR) == 0)
-      a.mem_scale[tensor][(int64_t)a.out_slot[gi] * rows + u * a.H + c0 / a.D] = s;
+      p.mem_scale[(int64_t)a.out_slot[gi] * rows + u * a.H + c0 / a.D] = s;
   }
 }
 
@@ -128,12 +162,13 @@ __global__ __launch_bounds__(64) void k_compress(const CompressArgs a) {
   constexpr int TOK = 16;
   const int32_t C = a.H * a.D;
   const int32_t c0 = (blockIdx.x * 64 + threadIdx.x) * 8;  // first channel of this lane
-  const int gi = blockIdx.z >> 1, tensor = blockIdx.z & 1;
   if (c0 >= C) return;
+  const CompressPtrs p = compress_ptrs(a);
+  const int gi = p.gi;
   const int32_t r = a.r;
   float b[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) b[e] = a.b[tensor][c0 + e];
+  for (int e = 0; e < 8; ++e) b[e] = p.b[c0 + e];
   const int32_t u0 = blockIdx.y * TOK;
   for (int32_t u = u0; u < u0 + TOK && u < a.T; ++u) {
     const int64_t el = (int64_t)u * C + c0;                // element offset inside a frame
@@ -144,16 +179,16 @@ __global__ __launch_bounds__(64) void k_compress(const CompressArgs a) {
     for (int k = 0; k < r; ++k) {
       int32_t slot = a.in_slot0[gi] + k;
       if (slot >= a.R) slot -= a.R;
-      const float sc = a.kv_dtype == DT_FP8 ? a.ring_scale[tensor][(int64_t)slot * a.T * a.H + hrow] : 1.0f;
+      const float sc = a.kv_dtype == DT_FP8 ? p.ring_scale[(int64_t)slot * a.T * a.H + hrow] : 1.0f;
       float x[8];
-      load8_kv(a.ring[tensor], a.kv_dtype, (int64_t)slot * a.T * C + el, sc, x);
+      load8_kv(p.ring, a.kv_dtype, (int64_t)slot * a.T * C + el, sc, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(a.w[tensor][(int64_t)(c0 + e) * r + k], x[e], acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(p.w[(int64_t)(c0 + e) * r + k], x[e], acc[e]);
     }
     const int64_t dst = (int64_t)a.out_slot[gi] * a.T * C + el;
-    const float s = store8_kv<LPR>(a.mem[tensor], a.kv_dtype, dst, acc);
+    const float s = store8_kv<LPR>(p.mem, a.kv_dtype, dst, acc);
     if (a.kv_dtype == DT_FP8 && (threadIdx.x % LPR) == 0)
-      a.mem_scale[tensor][(int64_t)a.out_slot[gi] * a.T * a.H + hrow] = s;
+      p.mem_scale[(int64_t)a.out_slot[gi] * a.T * a.H + hrow] = s;
   }
 }
 
@@ -293,7 +328,7 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
 hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const int lpr = a.D / 8;
-  dim3 grid(blocks_for((int64_t)a.T * a.H * lpr), a.n_frames, 2);
+  dim3 grid(blocks_for((int64_t)a.T * a.H * lpr), a.n_frames, 2 * a.members);
   if (a.D == 128)
     hipLaunchKernelGGL(k_ring_write<16>, grid, dim3(256), 0, s, a);
   else
@@ -306,7 +341,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   const int32_t chunks = a.H * a.D / 8;
   constexpr int TOK = 4;
   if (a.D == 128 && a.r == 5 && a.kv_dtype != DT_F32) {
-    dim3 grid((chunks + 63) / 64, (a.T + TOK - 1) / TOK, 2 * a.n_groups);
+    dim3 grid((chunks + 63) / 64, (a.T + TOK - 1) / TOK, 2 * a.n_groups * a.members);
     if (a.kv_dtype == DT_BF16)
       hipLaunchKernelGGL((k_compress_r<16, 5, TOK, DT_BF16>), grid, dim3(64), 0, s, a);
     else
@@ -314,14 +349,14 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.D == 64 && a.r == 5 && a.kv_dtype != DT_F32) {
-    dim3 grid((chunks + 63) / 64, (a.T + TOK - 1) / TOK, 2 * a.n_groups);
+    dim3 grid((chunks + 63) / 64, (a.T + TOK - 1) / TOK, 2 * a.n_groups * a.members);
     if (a.kv_dtype == DT_BF16)
       hipLaunchKernelGGL((k_compress_r<8, 5, TOK, DT_BF16>), grid, dim3(64), 0, s, a);
     else
       hipLaunchKernelGGL((k_compress_r<8, 5, TOK, DT_FP8>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
   }
-  dim3 grid((chunks + 63) / 64, (a.T + 15) / 16, 2 * a.n_groups);
+  dim3 grid((chunks + 63) / 64, (a.T + 15) / 16, 2 * a.n_groups * a.members);
   if (a.D == 128)
     hipLaunchKernelGGL(k_compress<16>, grid, dim3(64), 0, s, a);
   else

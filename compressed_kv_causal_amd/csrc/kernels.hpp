@@ -22,24 +22,32 @@ struct HistMap {
   int32_t ref_len, mem_len, win_len, M, R, mem_slot0, ring_slot0;
 };
 
-// Append: frame F + i goes to raw slot (slot0 + i) mod R, slot0 = F mod R.
+// Append: frame F + i goes to raw slot (slot0 + i) mod R, slot0 = F mod R.  A set's
+// members follow each other at fixed byte strides, on the input side and in the cache.
 struct RingWriteArgs {
-  const void* src[2];      // K, V: [n*T][H][D] in in_dtype
-  void* ring[2];           // raw ring bases [R][T][H][D]
-  float* ring_scale[2];    // FP8: [R][T][H]
+  const void* src[2];      // K, V: [members][n*T][H][D] in in_dtype
+  void* ring[2];           // member 0's raw ring bases [R][T][H][D]
+  float* ring_scale[2];    // FP8: member 0's [R][T][H]
+  int64_t src_mstride;     // bytes between members' inputs
+  int64_t ring_mstride;    // bytes between members' rings (and scales)
+  int32_t members;
   int32_t slot0, n_frames, R, T, H, D;
   int32_t in_dtype, kv_dtype;
 };
 
 // Compress: group g reads raw slots (r*g + k) mod R = (in_slot0 + k) mod R and writes
 // memory slot out_slot = g mod M.
+// Every member of a set in one launch: member m's ring, memory and scales are at
+// + m * mstride bytes, its weights at + m * w_mstride and biases at + m * b_mstride floats.
 struct CompressArgs {
   const void* ring[2];
   const float* ring_scale[2];
   void* mem[2];
   float* mem_scale[2];
-  const float* w[2];       // [C][r]
-  const float* b[2];       // [C]
+  const float* w[2];       // [members][C][r]
+  const float* b[2];       // [members][C]
+  int64_t mstride, w_mstride, b_mstride;
+  int32_t members;
   int32_t in_slot0[kMaxGroupsPerLaunch];
   int32_t out_slot[kMaxGroupsPerLaunch];
   int32_t n_groups, r, R, T, H, D;

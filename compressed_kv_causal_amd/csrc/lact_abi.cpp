@@ -8,6 +8,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 #include "lact.h"
@@ -73,7 +74,16 @@ int64_t rope_table_entries(const lact_cfg& c) {
          (int64_t)c.grid_w * (c.rope_split[2] / 2);
 }
 
-void compute_layout(const lact_cfg& c, lact_layout* L) {
+lact_status check_members(int32_t n) {
+  if (n < 1 || n > LACT_MAX_MEMBERS)
+    return fail(LACT_E_CAPACITY, "n_members " + std::to_string(n) + " outside 1.." +
+                                     std::to_string(LACT_MAX_MEMBERS));
+  return LACT_OK;
+}
+
+// Persistent regions of member 0 first (member m's at + m * member_bytes), then the
+// staging shared by all members.
+void compute_layout(const lact_cfg& c, int32_t members, lact_layout* L) {
   std::memset(L, 0, sizeof(*L));
   const int64_t T = (int64_t)c.grid_h * c.grid_w;
   const int64_t fe = T * c.heads * c.head_dim;  // elements per frame
@@ -97,10 +107,6 @@ void compute_layout(const lact_cfg& c, lact_layout* L) {
   L->mem_v = take(fb * M);
   L->ref_k = take(fb * (size_t)c.ref_frames);
   L->ref_v = take(fb * (size_t)c.ref_frames);
-  L->krot = take(ob * KF);
-  L->qrot = take(ob * B);
-  L->vcur = take(ob * B);
-  L->vhist = take(fp8 ? ob * (size_t)(c.ref_frames + M + c.window_frames) : 0);
   if (fp8) {
     L->ring_k_scale = take(sb * R);
     L->ring_v_scale = take(sb * R);
@@ -109,6 +115,13 @@ void compute_layout(const lact_cfg& c, lact_layout* L) {
     L->ref_k_scale = take(sb * (size_t)c.ref_frames);
     L->ref_v_scale = take(sb * (size_t)c.ref_frames);
   }
+  L->member_bytes = off;
+  L->members = members;
+  off = L->member_bytes * (size_t)members;
+  L->krot = take(ob * KF);
+  L->qrot = take(ob * B);
+  L->vcur = take(ob * B);
+  L->vhist = take(fp8 ? ob * (size_t)(c.ref_frames + M + c.window_frames) : 0);
   L->rope_table = take(sizeof(float) * 2 * (size_t)rope_table_entries(c));
   L->attn_flags = take(sizeof(int32_t) * (size_t)c.heads * (size_t)((B * T + 255) / 256));
   L->total = off;
@@ -125,19 +138,30 @@ struct lact_cache {
   lact::Planner plan;
   char* buf;
   bool table_ready = false;
-  bool staged = false;
-  uint64_t staged_version = 0;
+  bool staged = false;        // the staging holds staged_member's operands ...
+  uint64_t staged_version = 0;  // ... of this state version
   int32_t staged_frames = 0;
-  bool hist_built = false;
-  uint64_t hist_version = 0;
-  bool ref_valid = false;     // lact_ref_set has stored the reference segment
+  int32_t staged_member = 0;
+  bool hist_built = false;    // the staged history (krot, vhist) is hist_member's ...
+  uint64_t hist_version = 0;  // ... at this version
+  int32_t hist_member = 0;
+  std::vector<uint8_t> ref_valid;  // per member: the reference segment has been stored
   lact_cache(const lact_cfg& c, const lact_layout& l, void* b)
-      : cfg(c), lay(l), plan(c), buf(static_cast<char*>(b)) {}
+      : cfg(c), lay(l), plan(c), buf(static_cast<char*>(b)), ref_valid((size_t)l.members, 0) {}
 
   int32_t T() const { return cfg.grid_h * cfg.grid_w; }
+  int32_t members() const { return lay.members; }
+  // shared staging regions
   void* at(size_t off) const { return buf + off; }
-  float* fat(size_t off) const {
-    return cfg.kv_dtype == LACT_FP8_E4M3 ? reinterpret_cast<float*>(buf + off) : nullptr;
+  // member m's persistent regions
+  void* mat(int32_t m, size_t off) const { return buf + (size_t)m * lay.member_bytes + off; }
+  float* fat(int32_t m, size_t off) const {
+    return cfg.kv_dtype == LACT_FP8_E4M3 ? reinterpret_cast<float*>(mat(m, off)) : nullptr;
+  }
+  bool all_refs() const {
+    for (uint8_t v : ref_valid)
+      if (!v) return false;
+    return true;
   }
   lact::HistMap hist() const {
     lact::HistMap m;
@@ -165,32 +189,44 @@ extern "C" {
 
 const char* lact_last_error(void) { return g_last_error.c_str(); }
 
-lact_status lact_cache_footprint(const lact_cfg* cfg, size_t* device_bytes) {
+lact_status lact_set_footprint(const lact_cfg* cfg, int32_t n_members, size_t* device_bytes) {
   lact_status st = check_cfg(cfg);
+  if (st == LACT_OK) st = check_members(n_members);
   if (st != LACT_OK) return st;
   if (!device_bytes) return fail(LACT_E_INVALID, "device_bytes is NULL");
   lact_layout L;
-  compute_layout(*cfg, &L);
+  compute_layout(*cfg, n_members, &L);
   *device_bytes = L.total;
   return LACT_OK;
 }
 
-lact_status lact_cache_layout(const lact_cfg* cfg, lact_layout* out) {
+lact_status lact_cache_footprint(const lact_cfg* cfg, size_t* device_bytes) {
+  return lact_set_footprint(cfg, 1, device_bytes);
+}
+
+lact_status lact_set_layout(const lact_cfg* cfg, int32_t n_members, lact_layout* out) {
   lact_status st = check_cfg(cfg);
+  if (st == LACT_OK) st = check_members(n_members);
   if (st != LACT_OK) return st;
   if (!out) return fail(LACT_E_INVALID, "out is NULL");
-  compute_layout(*cfg, out);
+  compute_layout(*cfg, n_members, out);
   return LACT_OK;
 }
 
-lact_status lact_cache_init(const lact_cfg* cfg, void* device_buf, size_t bytes, lact_cache** out) {
+lact_status lact_cache_layout(const lact_cfg* cfg, lact_layout* out) {
+  return lact_set_layout(cfg, 1, out);
+}
+
+lact_status lact_set_init(const lact_cfg* cfg, int32_t n_members, void* device_buf, size_t bytes,
+                          lact_cache** out) {
   lact_status st = check_cfg(cfg);
+  if (st == LACT_OK) st = check_members(n_members);
   if (st != LACT_OK) return st;
   if (!out) return fail(LACT_E_INVALID, "out is NULL");
   if (!device_buf || !aligned(device_buf, 256))
     return fail(LACT_E_INVALID, "device_buf must be non-NULL and 256-byte aligned");
   lact_layout L;
-  compute_layout(*cfg, &L);
+  compute_layout(*cfg, n_members, &L);
   if (bytes < L.total)
     return fail(LACT_E_CAPACITY, "device buffer of " + std::to_string(bytes) + " bytes; need " +
                                      std::to_string(L.total));
@@ -200,20 +236,28 @@ lact_status lact_cache_init(const lact_cfg* cfg, void* device_buf, size_t bytes,
   return LACT_OK;
 }
 
+lact_status lact_cache_init(const lact_cfg* cfg, void* device_buf, size_t bytes, lact_cache** out) {
+  return lact_set_init(cfg, 1, device_buf, bytes, out);
+}
+
 lact_status lact_cache_destroy(lact_cache* cache) {
   delete cache;
   return LACT_OK;
 }
 
-lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cur, const void* v_cur,
-                                  int32_t n_frames, void* stream) {
+lact_status lact_member_rope_reset_apply(lact_cache* c, int32_t member, const void* q,
+                                         const void* k_cur, const void* v_cur, int32_t n_frames,
+                                         void* stream) {
   if (!c) return fail(LACT_E_INVALID, "cache is NULL");
+  if (member < 0 || member >= c->members())
+    return fail(LACT_E_INVALID, "member " + std::to_string(member) + " outside 0.." +
+                                    std::to_string(c->members() - 1));
   if (!q || !k_cur || !v_cur || !aligned(q, 16) || !aligned(k_cur, 16) || !aligned(v_cur, 16))
     return fail(LACT_E_INVALID, "q, k_cur, v_cur must be non-NULL and 16-byte aligned");
   if (n_frames < 1 || n_frames > c->cfg.max_block_frames)
     return fail(LACT_E_CAPACITY, "n_frames " + std::to_string(n_frames) + " outside 1.." +
                                      std::to_string(c->cfg.max_block_frames));
-  if (c->cfg.ref_frames > 0 && !c->ref_valid)
+  if (c->cfg.ref_frames > 0 && !c->ref_valid[(size_t)member])
     return fail(LACT_E_STATE, "the reference segment has not been set (lact_ref_set)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lact_cfg& g = c->cfg;
@@ -239,25 +283,27 @@ lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cu
   a.q = q;
   a.k_cur = k_cur;
   a.v_cur = v_cur;
-  a.ring_k = c->at(c->lay.ring_k);
-  a.mem_k = c->at(c->lay.mem_k);
-  a.ring_v = c->at(c->lay.ring_v);
-  a.mem_v = c->at(c->lay.mem_v);
-  a.ref_k = c->at(c->lay.ref_k);
-  a.ref_v = c->at(c->lay.ref_v);
-  a.ring_k_scale = c->fat(c->lay.ring_k_scale);
-  a.mem_k_scale = c->fat(c->lay.mem_k_scale);
-  a.ring_v_scale = c->fat(c->lay.ring_v_scale);
-  a.mem_v_scale = c->fat(c->lay.mem_v_scale);
-  a.ref_k_scale = c->fat(c->lay.ref_k_scale);
-  a.ref_v_scale = c->fat(c->lay.ref_v_scale);
+  const int32_t m = member;
+  a.ring_k = c->mat(m, c->lay.ring_k);
+  a.mem_k = c->mat(m, c->lay.mem_k);
+  a.ring_v = c->mat(m, c->lay.ring_v);
+  a.mem_v = c->mat(m, c->lay.mem_v);
+  a.ref_k = c->mat(m, c->lay.ref_k);
+  a.ref_v = c->mat(m, c->lay.ref_v);
+  a.ring_k_scale = c->fat(m, c->lay.ring_k_scale);
+  a.mem_k_scale = c->fat(m, c->lay.mem_k_scale);
+  a.ring_v_scale = c->fat(m, c->lay.ring_v_scale);
+  a.mem_v_scale = c->fat(m, c->lay.mem_v_scale);
+  a.ref_k_scale = c->fat(m, c->lay.ref_k_scale);
+  a.ref_v_scale = c->fat(m, c->lay.ref_v_scale);
   a.krot = c->at(c->lay.krot);
   a.qrot = c->at(c->lay.qrot);
   a.vcur = c->at(c->lay.vcur);
   a.vhist = g.kv_dtype == LACT_FP8_E4M3 ? c->at(c->lay.vhist) : nullptr;
   a.table = static_cast<const float2*>(c->at(c->lay.rope_table));
   a.hist = c->hist();
-  const bool rebuild = !(c->hist_built && c->hist_version == c->plan.version());
+  const bool rebuild =
+      !(c->hist_built && c->hist_version == c->plan.version() && c->hist_member == member);
   a.hist_rows = rebuild ? 1 : 0;
   a.n_cur = n_frames;
   a.T = c->T();
@@ -278,19 +324,38 @@ lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cu
   if (e != hipSuccess) return hip_fail(e, "rope launch");
   c->hist_built = true;
   c->hist_version = c->plan.version();
+  c->hist_member = member;
   c->staged = true;
   c->staged_version = c->plan.version();
   c->staged_frames = n_frames;
+  c->staged_member = member;
   return LACT_OK;
 }
 
-lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, int32_t n_q_blocks,
-                                 void* out, float* lse, void* stream) {
+static lact_status refuse_set(const lact_cache* c, const char* call) {
+  return fail(LACT_E_INVALID, std::string("the handle is a set of ") + std::to_string(c->members()) +
+                                  " members: name one with lact_member_" + call);
+}
+
+lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cur, const void* v_cur,
+                                  int32_t n_frames, void* stream) {
+  if (c && c->members() > 1) return refuse_set(c, "rope_reset_apply");
+  return lact_member_rope_reset_apply(c, 0, q, k_cur, v_cur, n_frames, stream);
+}
+
+lact_status lact_member_block_attention(lact_cache* c, int32_t member, const int32_t* q_block_frames,
+                                        int32_t n_q_blocks, void* out, float* lse, void* stream) {
   if (!c) return fail(LACT_E_INVALID, "cache is NULL");
+  if (member < 0 || member >= c->members())
+    return fail(LACT_E_INVALID, "member " + std::to_string(member) + " outside 0.." +
+                                    std::to_string(c->members() - 1));
   if (!out || !aligned(out, 16)) return fail(LACT_E_INVALID, "out must be non-NULL and 16-byte aligned");
   if (lse && !aligned(lse, 4)) return fail(LACT_E_INVALID, "lse must be 4-byte aligned");
   if (!c->staged || c->staged_version != c->plan.version())
     return fail(LACT_E_STATE, "lact_rope_reset_apply has not run at the present state");
+  if (c->staged_member != member)
+    return fail(LACT_E_STATE, "the staging holds member " + std::to_string(c->staged_member) +
+                                  ", not member " + std::to_string(member));
   const lact_cfg& g = c->cfg;
   const int32_t T = c->T();
   lact::AttnArgs a;
@@ -333,9 +398,9 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
     a.hist.M = a.hist.mem_len > 0 ? a.hist.mem_len : 1;
     a.hist.R = a.hist.win_len > 0 ? a.hist.win_len : 1;
   } else {
-    a.v_ring = c->at(c->lay.ring_v);
-    a.v_mem = c->at(c->lay.mem_v);
-    a.v_ref = c->at(c->lay.ref_v);
+    a.v_ring = c->mat(member, c->lay.ring_v);
+    a.v_mem = c->mat(member, c->lay.mem_v);
+    a.v_ref = c->mat(member, c->lay.ref_v);
   }
   a.T = T;
   a.H = g.heads;
@@ -348,9 +413,18 @@ lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, i
   return LACT_OK;
 }
 
-lact_status lact_ref_set(lact_cache* c, const void* k_ref, const void* v_ref, int32_t n_frames,
-                         void* stream) {
+lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, int32_t n_q_blocks,
+                                 void* out, float* lse, void* stream) {
+  if (c && c->members() > 1) return refuse_set(c, "block_attention");
+  return lact_member_block_attention(c, 0, q_block_frames, n_q_blocks, out, lse, stream);
+}
+
+lact_status lact_member_ref_set(lact_cache* c, int32_t member, const void* k_ref, const void* v_ref,
+                                int32_t n_frames, void* stream) {
   if (!c) return fail(LACT_E_INVALID, "cache is NULL");
+  if (member < 0 || member >= c->members())
+    return fail(LACT_E_INVALID, "member " + std::to_string(member) + " outside 0.." +
+                                    std::to_string(c->members() - 1));
   if (!k_ref || !v_ref || !aligned(k_ref, 16) || !aligned(v_ref, 16))
     return fail(LACT_E_INVALID, "k_ref and v_ref must be non-NULL and 16-byte aligned");
   const lact_cfg& g = c->cfg;
@@ -361,10 +435,13 @@ lact_status lact_ref_set(lact_cache* c, const void* k_ref, const void* v_ref, in
   lact::RingWriteArgs a;
   a.src[0] = k_ref;
   a.src[1] = v_ref;
-  a.ring[0] = c->at(c->lay.ref_k);
-  a.ring[1] = c->at(c->lay.ref_v);
-  a.ring_scale[0] = c->fat(c->lay.ref_k_scale);
-  a.ring_scale[1] = c->fat(c->lay.ref_v_scale);
+  a.ring[0] = c->mat(member, c->lay.ref_k);
+  a.ring[1] = c->mat(member, c->lay.ref_v);
+  a.ring_scale[0] = c->fat(member, c->lay.ref_k_scale);
+  a.ring_scale[1] = c->fat(member, c->lay.ref_v_scale);
+  a.members = 1;
+  a.src_mstride = 0;
+  a.ring_mstride = 0;
   a.slot0 = 0;
   a.n_frames = n_frames;
   a.R = n_frames;
@@ -375,10 +452,16 @@ lact_status lact_ref_set(lact_cache* c, const void* k_ref, const void* v_ref, in
   a.kv_dtype = g.kv_dtype;
   hipError_t e = lact::launch_ring_write(a, (int64_t)n_frames * a.T * a.H, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "reference write launch");
-  c->ref_valid = true;
-  c->hist_built = false;  // the rotated reference keys (and FP8 values) are restaged
-  c->staged = false;
+  c->ref_valid[(size_t)member] = 1;
+  if (c->hist_member == member) c->hist_built = false;  // its rotated reference keys (and
+  if (c->staged_member == member) c->staged = false;    // FP8 values) are restaged
   return LACT_OK;
+}
+
+lact_status lact_ref_set(lact_cache* c, const void* k_ref, const void* v_ref, int32_t n_frames,
+                         void* stream) {
+  if (c && c->members() > 1) return refuse_set(c, "ref_set");
+  return lact_member_ref_set(c, 0, k_ref, v_ref, n_frames, stream);
 }
 
 lact_status lact_kv_ring_append(lact_cache* c, const void* k_new, const void* v_new, int32_t n_frames,
@@ -393,10 +476,13 @@ lact_status lact_kv_ring_append(lact_cache* c, const void* k_new, const void* v_
   lact::RingWriteArgs a;
   a.src[0] = k_new;
   a.src[1] = v_new;
-  a.ring[0] = c->at(c->lay.ring_k);
-  a.ring[1] = c->at(c->lay.ring_v);
-  a.ring_scale[0] = c->fat(c->lay.ring_k_scale);
-  a.ring_scale[1] = c->fat(c->lay.ring_v_scale);
+  a.ring[0] = c->mat(0, c->lay.ring_k);
+  a.ring[1] = c->mat(0, c->lay.ring_v);
+  a.ring_scale[0] = c->fat(0, c->lay.ring_k_scale);
+  a.ring_scale[1] = c->fat(0, c->lay.ring_v_scale);
+  a.members = c->members();
+  a.src_mstride = (int64_t)n_frames * c->T() * g.heads * g.head_dim * (int64_t)elem_bytes(g.q_dtype);
+  a.ring_mstride = (int64_t)c->lay.member_bytes;
   a.slot0 = c->plan.raw_slot(c->plan.frames_appended());
   a.n_frames = n_frames;
   a.R = c->plan.ring_slots();
@@ -425,14 +511,18 @@ lact_status lact_convkv_compress(lact_cache* c, const float* w_k, const float* b
   const int64_t first = G + ready - written;  // earlier groups would be overwritten at once
   lact::CompressArgs a;
   std::memset(&a, 0, sizeof(a));
-  a.ring[0] = c->at(c->lay.ring_k);
-  a.ring[1] = c->at(c->lay.ring_v);
-  a.ring_scale[0] = c->fat(c->lay.ring_k_scale);
-  a.ring_scale[1] = c->fat(c->lay.ring_v_scale);
-  a.mem[0] = c->at(c->lay.mem_k);
-  a.mem[1] = c->at(c->lay.mem_v);
-  a.mem_scale[0] = c->fat(c->lay.mem_k_scale);
-  a.mem_scale[1] = c->fat(c->lay.mem_v_scale);
+  a.ring[0] = c->mat(0, c->lay.ring_k);
+  a.ring[1] = c->mat(0, c->lay.ring_v);
+  a.ring_scale[0] = c->fat(0, c->lay.ring_k_scale);
+  a.ring_scale[1] = c->fat(0, c->lay.ring_v_scale);
+  a.mem[0] = c->mat(0, c->lay.mem_k);
+  a.mem[1] = c->mat(0, c->lay.mem_v);
+  a.mem_scale[0] = c->fat(0, c->lay.mem_k_scale);
+  a.mem_scale[1] = c->fat(0, c->lay.mem_v_scale);
+  a.members = c->members();
+  a.mstride = (int64_t)c->lay.member_bytes;
+  a.w_mstride = (int64_t)g.heads * g.head_dim * g.ratio;
+  a.b_mstride = (int64_t)g.heads * g.head_dim;
   a.w[0] = w_k;
   a.w[1] = w_v;
   a.b[0] = b_k;
@@ -465,7 +555,8 @@ lact_status lact_cache_state(const lact_cache* c, lact_state* out) {
   c->plan.state(out);
   out->staged_frames = c->staged ? c->staged_frames : 0;
   out->staged_valid = (c->staged && c->staged_version == c->plan.version()) ? 1 : 0;
-  out->ref_valid = c->ref_valid ? 1 : 0;
+  out->ref_valid = c->all_refs() ? 1 : 0;
+  out->staged_member = c->staged_member;
   return LACT_OK;
 }
 

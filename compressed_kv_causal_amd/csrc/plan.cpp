@@ -42,7 +42,7 @@ void Planner::state(lact_state* st) const {
   st->staged_frames = 0;
   st->staged_valid = 0;
   st->ref_valid = 0;
-  st->reserved = 0;
+  st->staged_member = 0;
 }
 
 }  // namespace lact

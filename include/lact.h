@@ -29,6 +29,10 @@
  *   - Every check runs before anything is enqueued. On error the call returns a non-OK
  *     status, the cache state is unchanged and lact_last_error() holds a message.
  *   - A cache handle is not thread-safe; separate handles are independent.
+ *   - A handle holds one cache (lact_cache_init) or a set of n_members caches of one cfg
+ *     (lact_set_init: one per layer and diffusion step) that advance together: they share
+ *     the bookkeeping, the staging area and the RoPE table, and append and compress run for
+ *     all members in one launch each.
  *   - Layouts are token-major: a frame is T = grid_h*grid_w tokens, row-major over the
  *     (h, w) patch grid; per token H heads of D channels; channel c = h*D + d.
  */
@@ -76,6 +80,7 @@ typedef struct {
  * 1 <= B_max; ref_frames >= 0; ref_frames + M + W + B_max <= LACT_MAX_KEY_FRAMES. */
 #define LACT_MAX_KEY_FRAMES 256
 #define LACT_MAX_Q_BLOCKS 16
+#define LACT_MAX_MEMBERS 1024
 
 /* Segment of a key frame in attention order. */
 enum { LACT_SEG_MEMORY = 0, LACT_SEG_WINDOW = 1, LACT_SEG_CURRENT = 2, LACT_SEG_REF = 3 };
@@ -102,13 +107,16 @@ typedef struct {
   uint64_t version;      /* +1 on every append and on every compress that consumed groups */
   int32_t staged_frames; /* current frames staged by the last lact_rope_reset_apply       */
   int32_t staged_valid;  /* 1 if that staging was done at the present version             */
-  int32_t ref_valid;     /* 1 once lact_ref_set has stored the reference segment           */
-  int32_t reserved;
+  int32_t ref_valid;     /* 1 once the reference segment is stored (every member's, in a set) */
+  int32_t staged_member; /* member whose operands the staging holds (0 for a single cache)  */
 } lact_state;
 
-/* Offsets (bytes, 256-aligned) of the regions inside the single cache buffer, so a caller
- * can inspect or snapshot it.  Scale regions and vhist are 0-sized unless kv_dtype is
- * FP8_E4M3.
+/* Offsets (bytes, 256-aligned) of the regions inside the cache buffer, so a caller can
+ * inspect or snapshot it.  Scale regions and vhist are 0-sized unless kv_dtype is
+ * FP8_E4M3.  The persistent regions (ring_*, mem_*, ref_* and their scales) come first and
+ * are per member: member m's copy of a region starts at offset + m * member_bytes.  The
+ * staging regions (krot, qrot, vcur, vhist, rope_table, attn_flags) follow all members
+ * and are shared by them.
  *   ring_k/ring_v  [R][T][H][D] kv dtype            raw ring (pre-RoPE K, V)
  *   mem_k/mem_v    [M][T][H][D] kv dtype            compressed memory slots
  *   ref_k/ref_v    [ref_frames][T][H][D] kv dtype   reference segment (pre-RoPE K, V)
@@ -133,6 +141,9 @@ typedef struct {
   size_t rope_table, attn_flags;
   size_t frame_bytes;    /* T*H*D * kv element size                                       */
   int32_t ring_slots, key_frames_max;
+  size_t member_bytes;   /* stride between members' persistent regions                    */
+  int32_t members;       /* 1 for a single cache                                          */
+  int32_t reserved;
 } lact_layout;
 
 typedef struct lact_cache lact_cache; /* opaque host handle */
@@ -155,6 +166,23 @@ lact_status lact_cache_init(const lact_cfg* cfg, void* device_buf, size_t bytes,
 /* Frees the host handle only; the device buffer stays the caller's. NULL is a no-op. */
 lact_status lact_cache_destroy(lact_cache* cache);
 
+/* ---- cache sets ------------------------------------------------------------------------ */
+
+/* A set of n_members caches of one cfg, one per (layer, diffusion step): the pages' model
+ * keeps a KV cache in every self-attention layer, and under Neighbor Forcing each of the 3
+ * distilled denoising steps of a block reuses the KV built at that same step (walkthrough,
+ * "Neighbor Forcing", "ConvKV Memory" and "3-step distilled inference"), so all of them
+ * append one block and compress once between blocks ("Streaming Pipeline").  The members
+ * share one bookkeeping (they always hold the same frames), one staging area and one RoPE
+ * table; each has its own ring, memory and reference segment.  Per member, the step is
+ * lact_member_rope_reset_apply -> lact_member_block_attention; once per block, for all
+ * members, lact_kv_ring_append -> lact_convkv_compress.  1 <= n_members <= LACT_MAX_MEMBERS.
+ * A set of 1 is a cache: lact_cache_footprint / layout / init are these with n_members = 1. */
+lact_status lact_set_footprint(const lact_cfg* cfg, int32_t n_members, size_t* device_bytes);
+lact_status lact_set_layout(const lact_cfg* cfg, int32_t n_members, lact_layout* out);
+lact_status lact_set_init(const lact_cfg* cfg, int32_t n_members, void* device_buf, size_t bytes,
+                          lact_cache** out);
+
 /* ---- the reference segment ------------------------------------------------------------- */
 
 /* Stores the reference segment: the KV of ref_frames frames (the reference image's part of
@@ -167,6 +195,11 @@ lact_status lact_cache_destroy(lact_cache* cache);
  *   k_ref, v_ref: [n_frames*T][H][D] in q_dtype (pre-RoPE K).  n_frames == ref_frames. */
 lact_status lact_ref_set(lact_cache* cache, const void* k_ref, const void* v_ref, int32_t n_frames,
                          void* stream);
+/* lact_ref_set for member `member` of a set (0 <= member < n_members).  lact_ref_set,
+ * lact_rope_reset_apply and lact_block_attention are these with member 0 and refuse a set
+ * of more than one member (LACT_E_INVALID). */
+lact_status lact_member_ref_set(lact_cache* cache, int32_t member, const void* k_ref,
+                                const void* v_ref, int32_t n_frames, void* stream);
 
 /* ---- the four hot-path calls ----------------------------------------------------------- */
 
@@ -184,6 +217,12 @@ lact_status lact_ref_set(lact_cache* cache, const void* k_ref, const void* v_ref
  *   q, k_cur, v_cur: [n_frames*T][H][D] in q_dtype.  1 <= n_frames <= B_max. */
 lact_status lact_rope_reset_apply(lact_cache* cache, const void* q, const void* k_cur,
                                   const void* v_cur, int32_t n_frames, void* stream);
+/* lact_rope_reset_apply for one member of a set: stages that member's operands in the
+ * shared staging area (the history part is rebuilt unless the staging already holds this
+ * member's history at the present state). */
+lact_status lact_member_rope_reset_apply(lact_cache* cache, int32_t member, const void* q,
+                                         const void* k_cur, const void* v_cur, int32_t n_frames,
+                                         void* stream);
 
 /* Block attention over the staged operands (walkthrough, "Neighbor Forcing": block-wise
  * causal mask of block size m; "ConvKV Memory": the [memory | window | current] context).
@@ -195,12 +234,19 @@ lact_status lact_rope_reset_apply(lact_cache* cache, const void* q, const void* 
  * LACT_E_STATE unless lact_rope_reset_apply ran at the present state version. */
 lact_status lact_block_attention(lact_cache* cache, const int32_t* q_block_frames,
                                  int32_t n_q_blocks, void* out, float* lse, void* stream);
+/* lact_block_attention for one member of a set: LACT_E_STATE unless the last RoPE call
+ * staged this member at the present state version. */
+lact_status lact_member_block_attention(lact_cache* cache, int32_t member,
+                                        const int32_t* q_block_frames, int32_t n_q_blocks,
+                                        void* out, float* lse, void* stream);
 
 /* Append-only ring append (walkthrough, "ConvKV Memory" and "Streaming Pipeline": only the
  * new tokens' KV are added, cached KV stay unchanged).  Frame F + i goes to raw slot
  * (F + i) mod R; F += n_frames.  FP8_E4M3 quantises per (token, head): scale = amax/448
  * (1 if amax = 0), code = e4m3(x * (448/amax)) rounded to nearest even, saturating.
  *   k_new, v_new: [n_frames*T][H][D] in q_dtype (pre-RoPE K).  1 <= n_frames <= B_max.
+ *   For a set: [n_members][n_frames*T][H][D], member after member; one launch appends the
+ *   block to every member.
  * LACT_E_STATE if pending >= r (compress first). */
 lact_status lact_kv_ring_append(lact_cache* cache, const void* k_new, const void* v_new,
                                 int32_t n_frames, void* stream);
@@ -214,6 +260,8 @@ lact_status lact_kv_ring_append(lact_cache* cache, const void* k_new, const void
  * re-quantised per (token, head)).  Groups that a later group of the same call would
  * overwrite (more than M ready at once) are consumed without being written.
  *   w_k, w_v: [C][r] f32; b_k, b_v: [C] f32 (device).  slots_written: host, nullable.
+ *   For a set: [n_members][C][r] and [n_members][C] (each member's own conv weights); one
+ *   launch per 16 groups compresses every member.
  * With M = 0 ready groups are consumed and dropped (window-only context). */
 lact_status lact_convkv_compress(lact_cache* cache, const float* w_k, const float* b_k,
                                  const float* w_v, const float* b_v, void* stream,

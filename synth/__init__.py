@@ -125,6 +125,11 @@ WORKLOADS = {
 WORKLOADS["tiny_ref"] = dict(WORKLOADS["tiny_f32"], ref_frames=2)
 WORKLOADS["s512_ref2"] = dict(WORKLOADS["s512_bf16"], ref_frames=2)
 
+# Model scale: one cache per (layer, denoising step), 40 layers (the 40 x 128-channel heads
+# are those of the 14B Wan2.1 DiT the model is initialised from) x 3 distilled steps.
+WORKLOADS["model_s512"] = dict(WORKLOADS["s512_bf16"], members=120)
+WORKLOADS["model_s512_fp8"] = dict(WORKLOADS["fp8_kv"], members=120)
+
 # The memory-block / current-block grid of the model card's ablation table (Table 5):
 # window ("memory block") W and block B in frames, 512x512 shapes, memory 16 slots at 5:1.
 for _w, _b in ((6, 6), (8, 8), (6, 8)):

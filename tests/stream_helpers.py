@@ -21,12 +21,16 @@ def io_dtype(w):
 
 
 class Runner:
-    def __init__(self, w, seed=0, with_oracle=True, kernel=None):
+    """One cache, or (cache=, member=) one member of a set that a SetRunner advances."""
+
+    def __init__(self, w, seed=0, with_oracle=True, kernel=None, cache=None, member=0):
         self.w = w
         self.seed = seed
         self.T, self.H, self.D = w["tokens"], w["heads"], w["head_dim"]
         self.cfg = L.make_cfg(**w)
-        self.cache = L.Cache(self.cfg)
+        self.cache = cache if cache is not None else L.Cache(self.cfg)
+        self.member = member
+        self.mbase = member * self.cache.layout.member_bytes
         self.oc = OracleCache(w) if with_oracle else None
         if kernel is None:
             self.wk, self.bk = synth.conv_weights(w, seed, synth.TENSOR_WK)
@@ -47,7 +51,7 @@ class Runner:
         n = kr.shape[0]
         tk, tv = (torch.from_numpy(x.reshape(n * self.T, self.H, self.D)).to(io_dtype(self.w))
                   for x in (kr, vr))
-        self.cache.ref_set(tk.cuda(), tv.cuda())
+        self.cache.ref_set(tk.cuda(), tv.cuda(), member=self.member)
         if self.oc is not None:
             self.oc.set_ref(tk.float().numpy().reshape(n, -1), tv.float().numpy().reshape(n, -1))
 
@@ -66,26 +70,35 @@ class Runner:
     def step(self, n, attend=True, blocks=None, sel=None, lse=True, tag=False, form=1):
         """One AR step: rope -> attention -> append -> compress, on the GPU and the oracle.
         Returns dict(out, lse, ref) where ref = (O, LSE, heads, rows) of the oracle or None."""
+        res = self.attend_part(n, attend, blocks, sel, lse, tag, form)
+        self.cache.kv_ring_append(res["dk"], res["dv"])
+        res["slots"] = self.cache.convkv_compress(self.d_wk, self.d_bk, self.d_wv, self.d_bv)
+        self.oracle_advance(res)
+        return res
+
+    def oracle_advance(self, res):
+        n = res["n"]
+        if self.oc is not None:
+            self.oc.append(res["k"].reshape(n, -1), res["v"].reshape(n, -1))
+            res["groups"] = self.oc.compress(self.wk, self.bk, self.wv, self.bv)
+        self.f += n
+        self.step_index += 1
+
+    def attend_part(self, n, attend=True, blocks=None, sel=None, lse=True, tag=False, form=1):
+        """The step's inputs, and (attend) its RoPE + attention on the GPU and the oracle."""
         (q, qh), (k, kh), (v, vh) = self.inputs(n, tag)
-        res = {}
+        res = {"n": n, "dk": k, "dv": v, "k": kh, "v": vh}
         if attend:
-            self.cache.rope_reset_apply(q, k, v)
+            self.cache.rope_reset_apply(q, k, v, member=self.member)
             Lq = n * self.T
             lse_t = torch.empty((self.H, Lq), dtype=torch.float32, device="cuda") if lse else None
-            out = self.cache.block_attention(blocks, lse=lse_t)
+            out = self.cache.block_attention(blocks, lse=lse_t, member=self.member)
             res["out"], res["lse"] = out, lse_t
             if self.oc is not None and sel is not False:
                 res["ref"] = self.oc.attention(qh, kh, vh, block_frames=blocks, sel=sel, form=form)
                 if self.w["kv_dtype"] == FP8:
                     res["hist_kmax"] = self._hist_kmax()
-            res["q"], res["k"], res["v"] = qh, kh, vh
-        self.cache.kv_ring_append(k, v)
-        res["slots"] = self.cache.convkv_compress(self.d_wk, self.d_bk, self.d_wv, self.d_bv)
-        if self.oc is not None:
-            self.oc.append(kh.reshape(n, -1), vh.reshape(n, -1))
-            res["groups"] = self.oc.compress(self.wk, self.bk, self.wv, self.bv)
-        self.f += n
-        self.step_index += 1
+            res["q"] = qh
         return res
 
     # ---- comparisons -------------------------------------------------------------------
@@ -139,25 +152,25 @@ class Runner:
         """Raw bytes of memory slot `slot` of K (0) or V (1) as stored on the device."""
         lay = self.cache.layout
         fb = lay.frame_bytes
-        off = (lay.mem_k if tensor == 0 else lay.mem_v) + slot * fb
+        off = self.mbase + (lay.mem_k if tensor == 0 else lay.mem_v) + slot * fb
         return self.cache.buf[off: off + fb].cpu().numpy()
 
     def ref_slot_bytes(self, tensor, i):
         lay = self.cache.layout
         fb = lay.frame_bytes
-        off = (lay.ref_k if tensor == 0 else lay.ref_v) + i * fb
+        off = self.mbase + (lay.ref_k if tensor == 0 else lay.ref_v) + i * fb
         return self.cache.buf[off: off + fb].cpu().numpy()
 
     def ring_slot_bytes(self, tensor, slot):
         lay = self.cache.layout
         fb = lay.frame_bytes
-        off = (lay.ring_k if tensor == 0 else lay.ring_v) + slot * fb
+        off = self.mbase + (lay.ring_k if tensor == 0 else lay.ring_v) + slot * fb
         return self.cache.buf[off: off + fb].cpu().numpy()
 
     def scale_slot(self, name, slot):
         lay = self.cache.layout
         n = self.T * self.H
-        off = getattr(lay, name) + slot * n * 4
+        off = self.mbase + getattr(lay, name) + slot * n * 4
         return self.cache.buf[off: off + n * 4].cpu().numpy().view(np.float32)
 
     def oracle_stored_bytes(self, stored):
@@ -189,3 +202,29 @@ def sample_rows(w, n_frames, seed, per_head=16, heads=None):
     hh = np.repeat(np.asarray(list(hs), np.int32), len(rows))
     rr = np.tile(np.asarray(rows, np.int64), len(list(hs)))
     return hh, rr
+
+
+class SetRunner:
+    """A set of `members` caches (one per layer and denoising step) in one buffer: member m
+    has its own seeded inputs (seed base + m), conv weights, reference segment and oracle;
+    per step every member runs RoPE + attention, then one append and one compress launch
+    advance all of them."""
+
+    def __init__(self, w, members, seed=0, with_oracle=True):
+        self.w = w
+        self.cache = L.Cache(L.make_cfg(**w), members=members)
+        self.runs = [Runner(w, seed=seed + m, with_oracle=with_oracle, cache=self.cache, member=m)
+                     for m in range(members)]
+        stack = lambda name: torch.stack([getattr(r, name) for r in self.runs]).contiguous()
+        self.d_wk, self.d_bk, self.d_wv, self.d_bv = (stack(n) for n in ("d_wk", "d_bk", "d_wv", "d_bv"))
+
+    def step(self, n, attend=True, **kw):
+        res = [r.attend_part(n, attend, **kw) for r in self.runs]
+        k = torch.cat([x["dk"] for x in res]).contiguous()
+        v = torch.cat([x["dv"] for x in res]).contiguous()
+        self.cache.kv_ring_append(k, v)
+        slots = self.cache.convkv_compress(self.d_wk, self.d_bk, self.d_wv, self.d_bv)
+        for r, x in zip(self.runs, res):
+            x["slots"] = slots
+            r.oracle_advance(x)
+        return res

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import synth
-from stream_helpers import BF16, F32, FP8, Runner, rel_l2, sample_rows
+from stream_helpers import BF16, F32, FP8, Runner, SetRunner, rel_l2, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -378,3 +378,82 @@ def test_bf16_d128_overflow_falls_back_to_exact_pass():
     rel_lse = float(np.abs(lse_got - LSE_ref).max() / np.abs(LSE_ref).max())
     say(f"overflow fallback: flags {flags.tolist()}, rel L2 {err:.3e}, rel dLSE {rel_lse:.2e}")
     assert err <= ATTN_TOL[BF16] and rel_lse <= 2e-3
+
+
+# ---- cache sets: one cache per (layer, denoising step), advanced by batched launches ----
+
+def test_tiny_set_stream_full_parity():
+    """Tiny f32 set of 3 members with a 2-frame reference each, every member with its own
+    inputs, conv weights and reference: 27 history blocks then 20 AR steps; every output row
+    of every member against that member's oracle each step; one append and one compress
+    launch per step for all members; each member's ring, memory and reference bit-exact."""
+    w = synth.workload("tiny_ref")
+    sr = SetRunner(w, 3)
+    worst = 0.0
+    for s in range(w["history_blocks"] + w["steps"]):
+        for r in sr.runs:
+            assert_keys_match(r, 2)
+        res = sr.step(2)
+        outs = []
+        for r, x in zip(sr.runs, res):
+            err, dl = r.compare_attention(x)
+            worst = max(worst, err)
+            assert err <= ATTN_TOL[F32] and dl <= LSE_TOL[F32], (s, r.member, err, dl)
+            assert_state_matches(r)
+            outs.append(x["out"].float().cpu().numpy())
+        assert not np.array_equal(outs[0], outs[1])    # the members hold different data
+    st = sr.cache.state()
+    assert st["ref_valid"] == 1 and st["staged_member"] == 2
+    for r in sr.runs:
+        assert_memory_bitexact(r)
+        assert_ring_bitexact(r)
+        assert_ref_bitexact(r)
+    say(f"tiny set of 3: worst rel L2 {worst:.2e} over 47 steps x 3 members")
+
+
+def test_fp8_set_step_parity():
+    """512x512-shaped FP8 set of 2 members with a 2-frame reference: 11 blocks through the
+    batched append (quantising per member) and compress (each member's weights and scales),
+    every member's memory, ring and reference bit-exact; then a full step of each member
+    on sampled rows of all heads against its oracle."""
+    w = synth.workload("fp8_kv", ref_frames=2)
+    sr = SetRunner(w, 2)
+    for n in synth.block_sizes(w, 11):
+        sr.step(n, attend=False)
+    for r in sr.runs:
+        assert_state_matches(r)
+        assert_memory_bitexact(r)
+        assert_ring_bitexact(r)
+        assert_ref_bitexact(r)
+    sel = sample_rows(w, 8, seed=99, per_head=4)
+    res = sr.step(8, sel=sel)
+    for r, x in zip(sr.runs, res):
+        err, _ = r.compare_attention(x)
+        say(f"fp8 set member {r.member}: rel L2 {err:.3e}")
+        assert err <= ATTN_TOL[FP8]
+        assert_lse(r, x, FP8)
+
+
+def test_s512_set_equals_independent_caches():
+    """512x512 bf16: a set of 2 members gives bit-identical outputs, LSE and cache contents
+    to two independent caches fed the same inputs and weights (12 steps, the last 2
+    attended)."""
+    w = synth.workload("s512_bf16")
+    sr = SetRunner(w, 2, with_oracle=False)
+    solo = [Runner(w, seed=m, with_oracle=False) for m in range(2)]
+    sizes = synth.block_sizes(w, 12)
+    for i, n in enumerate(sizes):
+        attend = i >= len(sizes) - 2
+        res = sr.step(n, attend=attend, sel=False)
+        ref = [r.step(n, attend=attend, sel=False) for r in solo]
+        if attend:
+            for m in range(2):
+                assert torch.equal(res[m]["out"], ref[m]["out"]), (i, m)
+                assert torch.equal(res[m]["lse"], ref[m]["lse"]), (i, m)
+    assert sr.cache.state()["version"] == solo[0].cache.state()["version"]
+    lay, one = sr.cache.layout, solo[0].cache.layout
+    for m in range(2):
+        a = sr.cache.buf[m * lay.member_bytes: (m + 1) * lay.member_bytes]
+        b = solo[m].cache.buf[: one.member_bytes]
+        assert torch.equal(a, b), f"persistent state of member {m}"
+    say("s512 set of 2 == 2 independent caches, bit for bit")

@@ -44,21 +44,62 @@ def test_footprint_is_pure_and_matches_layout():
         assert lay.key_frames_max == ref + w["mem_slots"] + w["window_frames"] + w["max_block_frames"]
         esize = {0: 4, 1: 2, 2: 1}[w["kv_dtype"]]
         assert lay.frame_bytes == w["tokens"] * w["channels"] * esize
-        names = ("ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v", "krot", "qrot", "vcur", "vhist")
+        fp8 = w["kv_dtype"] == 2
+        # persistent regions first (one member), then the staging
+        names = ("ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v") + \
+            (("ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale", "ref_k_scale",
+              "ref_v_scale") if fp8 else ()) + ("krot", "qrot", "vcur", "vhist", "rope_table",
+                                                "attn_flags")
         offs = [getattr(lay, n) for n in names]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        assert lay.members == 1 and lay.krot == lay.member_bytes
+        fb, M, W = lay.frame_bytes, w["mem_slots"], w["window_frames"]
+        assert lay.mem_k - lay.ring_v >= fb * R and lay.ref_k - lay.mem_v >= fb * M
         # staged operands are in the q dtype; FP8 adds the dequantised history V
         ob = w["tokens"] * w["channels"] * {0: 4, 1: 2}[w["q_dtype"]]
         KF = lay.key_frames_max
         assert lay.qrot - lay.krot >= ob * KF and lay.vcur - lay.qrot >= ob * w["max_block_frames"]
-        if w["kv_dtype"] == 2:
+        if fp8:
             assert lay.vhist - lay.vcur >= ob * w["max_block_frames"]
-            assert lay.ring_k_scale - lay.vhist >= ob * (ref + w["mem_slots"] + w["window_frames"])
+            assert lay.rope_table - lay.vhist >= ob * (ref + M + W)
+            sb = w["tokens"] * w["heads"] * 4
+            assert lay.member_bytes - lay.ref_v_scale >= sb * ref
         else:
             assert lay.ring_k_scale == 0 and lay.vhist == lay.rope_table
     # 512x512 bf16: 2R + 2M + KF + 2 B_max = 120 frames of 10 MiB, plus the small tables
     mib = L.lact_cache_footprint(_cfg("s512_bf16")) / 2 ** 20
     assert 1200 <= mib < 1201
+
+
+def test_set_layout_and_footprint():
+    """A set of n members: n copies of the persistent regions at a fixed stride, one
+    staging area; a set of 1 is the single cache."""
+    for name in ("s512_bf16", "fp8_kv", "tiny_ref", "s720_bf16"):
+        c = _cfg(name)
+        one = L.lact_cache_layout(c)
+        s1 = L.lact_set_layout(c, 1)
+        assert [getattr(one, f) for f, _ in L.lact_layout._fields_] == \
+            [getattr(s1, f) for f, _ in L.lact_layout._fields_]
+        for n in (2, 3, 120):
+            lay = L.lact_set_layout(c, n)
+            assert lay.members == n and lay.member_bytes == one.member_bytes
+            assert lay.member_bytes % 256 == 0
+            for f in ("ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v", "ring_k_scale",
+                      "mem_v_scale", "frame_bytes", "ring_slots", "key_frames_max"):
+                assert getattr(lay, f) == getattr(one, f), f
+            shift = (n - 1) * one.member_bytes
+            for f in ("krot", "qrot", "vcur", "vhist", "rope_table", "attn_flags", "total"):
+                assert getattr(lay, f) == getattr(one, f) + shift, f
+            assert L.lact_set_footprint(c, n) == lay.total
+    # 40 layers x 3 denoising steps at 512x512 bf16: 120 x 720 MiB persistent + 480 MiB staging
+    c = _cfg("s512_bf16")
+    gib = L.lact_set_footprint(c, 120) / 2 ** 30
+    assert 84.8 < gib < 84.9
+    assert L.lact_set_footprint(c, 120) < 120 * L.lact_cache_footprint(c) * 0.62
+    for n in (0, -1, L.LACT_MAX_MEMBERS + 1):
+        with pytest.raises(L.LactError) as e:
+            L.lact_set_footprint(c, n)
+        assert e.value.status == 3
 
 
 @pytest.mark.parametrize("kw, status", [
@@ -149,10 +190,14 @@ class _HostOnlyCache:
     """A cache handle over a host address of the right alignment: lact_cache_init does no
     device work, and every call below fails its checks before anything is enqueued."""
 
-    def __init__(self, name="tiny_f32", **kw):
+    def __init__(self, name="tiny_f32", members=None, **kw):
         self.cfg = _cfg(name, **kw)
-        self.nbytes = L.lact_cache_footprint(self.cfg)
-        self.h = L.lact_cache_init(self.cfg, 0x10000000, self.nbytes)
+        if members is None:
+            self.nbytes = L.lact_cache_footprint(self.cfg)
+            self.h = L.lact_cache_init(self.cfg, 0x10000000, self.nbytes)
+        else:
+            self.nbytes = L.lact_set_footprint(self.cfg, members)
+            self.h = L.lact_set_init(self.cfg, members, 0x10000000, self.nbytes)
 
     def close(self):
         L.lact_cache_destroy(self.h)
@@ -238,3 +283,35 @@ def test_multiblock_argument_checks():
     # still no RoPE pass: state error comes first
     assert lib.lact_block_attention(c.h, blocks, 2, dev, None, None) == 5
     c.close()
+
+
+def test_set_member_checks():
+    """A set refuses the single-cache forms of the per-member calls and member indexes out
+    of range; attention asks for the member the staging holds; the buffer must hold every
+    member; the reference is tracked per member; one bookkeeping for all members."""
+    lib = L.lib()
+    dev = ctypes.c_void_p(0x20000000)
+    c = _HostOnlyCache("tiny_ref", members=3)
+    assert lib.lact_rope_reset_apply(c.h, dev, dev, dev, 2, None) == 1
+    assert "member" in lib.lact_last_error().decode()
+    assert lib.lact_block_attention(c.h, None, 0, dev, None, None) == 1
+    assert lib.lact_ref_set(c.h, dev, dev, 2, None) == 1
+    for m in (-1, 3):
+        assert lib.lact_member_rope_reset_apply(c.h, m, dev, dev, dev, 2, None) == 1
+        assert lib.lact_member_block_attention(c.h, m, None, 0, dev, None, None) == 1
+        assert lib.lact_member_ref_set(c.h, m, dev, dev, 2, None) == 1
+    # no reference stored yet: the RoPE pass of any member is refused
+    assert lib.lact_member_rope_reset_apply(c.h, 1, dev, dev, dev, 2, None) == 5
+    assert lib.lact_member_block_attention(c.h, 1, None, 0, dev, None, None) == 5
+    st = L.lact_cache_state(c.h)
+    assert st["ref_valid"] == 0 and st["staged_member"] == 0 and st["F"] == 0
+    c.close()
+    # a set's buffer must hold all members
+    cfg = _cfg("tiny_f32")
+    need = L.lact_set_footprint(cfg, 4)
+    with pytest.raises(L.LactError) as e:
+        L.lact_set_init(cfg, 4, 0x10000000, need - 1)
+    assert e.value.status == 3
+    with pytest.raises(L.LactError) as e:
+        L.lact_set_init(cfg, 0, 0x10000000, need)
+    assert e.value.status == 3
