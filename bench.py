@@ -343,16 +343,19 @@ def set_main(args, w):
     set_bytes = L.lact_set_footprint(cfg, nm)
     solo_bytes = L.lact_cache_footprint(cfg)
     cache = L.Cache(cfg, device=dev, members=nm)
-    # inputs resident in HBM: a pool of seeded blocks; member m's block is pool block m mod P,
-    # and the K, V of all members for the batched append are stacked once, before timing
+    # inputs resident in HBM: a pool of P seeded blocks; at AR step i member m takes pool
+    # block (i + m) mod P.  K and V are laid out once, before timing, as nm + P - 1 blocks
+    # (block j = pool block j mod P), so the stacked input of step i is the contiguous run
+    # of nm blocks from block i mod P.
     pool = []
     for blk in range(args.pool_blocks):
         ids = list(range(blk * B, (blk + 1) * B))
         pool.append([torch.from_numpy(synth.frames(w, args.seed, t, ids).reshape(B * T, H, D))
                      .to(io).to(dev) for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V)])
     P = len(pool)
-    k_all = torch.stack([pool[m % P][1] for m in range(nm)]).reshape(nm * B * T, H, D)
-    v_all = torch.stack([pool[m % P][2] for m in range(nm)]).reshape(nm * B * T, H, D)
+    nb = nm + P - 1
+    k_run = torch.stack([pool[j % P][1] for j in range(nb)])
+    v_run = torch.stack([pool[j % P][2] for j in range(nb)])
     wts = [synth.conv_weights(w, args.seed + m, synth.TENSOR_WK) + synth.conv_weights(w, args.seed + m, synth.TENSOR_WV)
            for m in range(nm)]
     d_wk, d_bk, d_wv, d_bv = (torch.from_numpy(np.stack([x[i] for x in wts])).to(dev) for i in range(4))
@@ -360,23 +363,29 @@ def set_main(args, w):
     out = torch.empty((Lq, H, D), dtype=io, device=dev)
     stream = torch.cuda.current_stream()
     h = cache.h
-    kview = k_all.view(nm, B * T, H, D)
-    vview = v_all.view(nm, B * T, H, D)
 
-    def advance():
+    def stacked(i):
+        o = i % P
+        return (k_run[o: o + nm].reshape(nm * B * T, H, D), v_run[o: o + nm].reshape(nm * B * T, H, D))
+
+    def advance(i):
+        k_all, v_all = stacked(i)
         L.lact_kv_ring_append(h, k_all, v_all, B, stream)
         L.lact_convkv_compress(h, d_wk, d_bk, d_wv, d_bv, stream)
 
-    def block(ev=None):
+    def block(i, ev=None):
+        o = i % P
         for m in range(nm):
             if ev is not None:
                 ev[0][m].record(stream)
-            L.lact_member_rope_reset_apply(h, m, pool[m % P][0], kview[m], vview[m], B, stream)
+            L.lact_member_rope_reset_apply(h, m, pool[(o + m) % P][0], k_run[o + m], v_run[o + m],
+                                           B, stream)
             if ev is not None:
                 ev[1][m].record(stream)
             L.lact_member_block_attention(h, m, None, out, None, stream)
         if ev is not None:
             ev[2].record(stream)
+        k_all, v_all = stacked(i)
         L.lact_kv_ring_append(h, k_all, v_all, B, stream)
         if ev is not None:
             ev[3].record(stream)
@@ -385,13 +394,16 @@ def set_main(args, w):
             ev[4].record(stream)
 
     # fill the memory with the batched append + compress alone (attention changes no state)
+    i = 0
     while True:
         st = cache.state()
         if st["mem_len"] == w["mem_slots"] and st["win_len"] == w["window_frames"]:
             break
-        advance()
+        advance(i)
+        i += 1
     for _ in range(args.warmup):
-        block()
+        block(i)
+        i += 1
     torch.cuda.synchronize()
     n_hist = cache.state()["mem_len"] + cache.state()["win_len"]
     Lk = (n_hist + B) * T
@@ -400,9 +412,14 @@ def set_main(args, w):
            for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s_ in range(args.steps):
-        block(evs[s_])
+        block(i, evs[s_])
+        i += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # query tiles the fast attention pass handed to the exact pass (last member's call)
+    n_flags = H * ((Lq + 255) // 256)
+    flags = cache.buf[cache.layout.attn_flags:].view(torch.int32)[:n_flags]
+    exact_tiles = int(flags.sum().item())
     rope_ms = np.mean([sum(e[0][m].elapsed_time(e[1][m]) for m in range(nm)) for e in evs])
     attn_ms = np.mean([sum(e[1][m].elapsed_time(e[0][m + 1]) for m in range(nm - 1)) +
                        e[1][nm - 1].elapsed_time(e[2]) for e in evs])
@@ -433,6 +450,7 @@ def set_main(args, w):
         "footprint_gib": {"set": round(set_bytes / 2 ** 30, 2),
                           "independent_caches": round(nm * solo_bytes / 2 ** 30, 2)},
         "attn_tflops": round(attn_tflops, 2),
+        "attn_exact_pass_tiles_last_member": f"{exact_tiles}/{n_flags}",
         "step_breakdown_ms": {"rope_reset_apply_all_members": round(rope_ms, 3),
                               "block_attention_all_members": round(attn_ms, 3),
                               "kv_ring_append_batched": round(app_ms, 3),

@@ -20,37 +20,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// OCP E4M3FN: bias 7, no infinities, S.1111.111 = NaN, largest finite 448, subnormals
-// m * 2^-9.  Exact decode.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 24;
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 0) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));
-  if (e == 15 && m == 7) return __uint_as_float(0x7FC00000u | s);
-  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+// OCP E4M3FN (bias 7, no infinities, S.1111.111 = NaN, largest finite 448, subnormals
+// m * 2^-9) through gfx950's conversion instructions, which use this format.
+// Decode: exact for every code (NaN codes give NaN).  Encode: round to nearest, ties to
+// even mantissa; the value is clamped to [-448, 448] first, so larger magnitudes saturate
+// to +-448 (a NaN input gives an unspecified code: the row quantiser only sees finite
+// values for finite inputs).  Both agree with the format's definition for every finite
+// f32 input and every code (checked exhaustively on the device).
+
+// the four codes of w -> x[0..3] (byte i -> x[i])
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* x) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  x[0] = lo[0];
+  x[1] = lo[1];
+  x[2] = hi[0];
+  x[3] = hi[1];
 }
 
-// Nearest e4m3 code, ties to even mantissa, |y| >= 448 saturates to +-448, NaN -> 0x7F/0xFF.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
-  uint32_t u = __float_as_uint(y);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;
-  if (a >= 0x43E00000u) return sign | 0x7Eu;           // |y| >= 448
-  if (a < 0x3C800000u) {                                // |y| < 2^-6: multiples of 2^-9
-    float q = rintf(__uint_as_float(a) * 512.0f);       // exact scaling, then round half even
-    return sign | (uint32_t)q;                          // 8 -> 0x08 = 2^-6, also correct
-  }
-  uint32_t e = (a >> 23) - 120u;                        // biased e4m3 exponent 1..15
-  uint32_t m = (a >> 20) & 7u;
-  uint32_t rest = a & 0xFFFFFu;
-  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) {
-    if (++m == 8u) {
-      m = 0;
-      ++e;
-    }
-  }
-  return sign | (e << 3) | m;
+// codes of y[0..3] packed as bytes 0..3
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(const float* y) {
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(y[i], -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  return (uint32_t)w;
 }
 
 // Row quantiser of the FP8 cache, per (token, head): scale = amax / 448, y = x * (448 / amax)
@@ -96,9 +91,10 @@ __device__ __forceinline__ void load8_bf16(const uint16_t* p, float* x) {
 }
 __device__ __forceinline__ void load8_fp8(const uint8_t* p, float scale, float* x) {
   uint2 v = *reinterpret_cast<const uint2*>(p);
-  uint32_t w[2] = {v.x, v.y};
+  e4m3x4_to_f32(v.x, x);
+  e4m3x4_to_f32(v.y, x + 4);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = e4m3_to_f32((w[i / 4] >> (8 * (i % 4))) & 0xFFu) * scale;
+  for (int i = 0; i < 8; ++i) x[i] *= scale;
 }
 
 __device__ __forceinline__ void store8_f32(float* p, const float* x) {
@@ -115,10 +111,10 @@ __device__ __forceinline__ void store8_bf16(uint16_t* p, const float* x) {
 }
 // quantises 8 values with the row's inverse scale and stores 8 codes
 __device__ __forceinline__ void store8_fp8(uint8_t* p, const float* x, float inv) {
-  uint32_t w[2] = {0u, 0u};
+  float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w[i / 4] |= f32_to_e4m3(x[i] * inv) << (8 * (i % 4));
-  *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  for (int i = 0; i < 8; ++i) y[i] = x[i] * inv;
+  *reinterpret_cast<uint2*>(p) = make_uint2(f32x4_to_e4m3(y), f32x4_to_e4m3(y + 4));
 }
 
 // Load 8 input elements (q dtype: F32 or BF16) starting at element offset off.

@@ -136,9 +136,10 @@ __global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
     for (int k = 0; k < R; ++k) {
       float x[8];
       if (KV == DT_FP8) {
-        const uint32_t wd[2] = {raw[t][k].x, raw[t][k].y};
+        e4m3x4_to_f32(raw[t][k].x, x);
+        e4m3x4_to_f32(raw[t][k].y, x + 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = e4m3_to_f32((wd[e / 4] >> (8 * (e % 4))) & 0xFFu) * sc[t][k];
+        for (int e = 0; e < 8; ++e) x[e] *= sc[t][k];
       } else {
         const uint4 v = reinterpret_cast<const uint4&>(raw[t][k]);
         const uint32_t wd[4] = {v.x, v.y, v.z, v.w};

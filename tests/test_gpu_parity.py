@@ -380,6 +380,39 @@ def test_bf16_d128_overflow_falls_back_to_exact_pass():
     assert err <= ATTN_TOL[BF16] and rel_lse <= 2e-3
 
 
+def test_fp8_codes_of_every_bf16_value():
+    """The FP8 append's codes and scales against the oracle's quantiser for every finite
+    bf16 value of magnitude <= 448: K rows carry 448 (scale 1, so the codes are of the
+    values themselves: every rounding case of e4m3, ties and subnormals included); V rows
+    carry 446 (scale 446/448, so the quantiser's f32 products land between bf16 values)."""
+    w = synth.workload("fp8_kv", heads=8, grid_h=8, grid_w=8, window_frames=2, mem_slots=2,
+                       max_block_frames=1, first_block=1, block=1)
+    run = Runner(w)
+    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    bits = np.arange(0, 0x43E1, dtype=np.uint32)                 # +0 .. 448
+    pos = (bits << 16).view(np.float32)
+    vals = np.concatenate([pos, -pos])
+    rows = T * H
+    k = np.zeros((rows, D), np.float32)
+    v = np.zeros((rows, D), np.float32)
+    kv_vals = vals
+    vv_vals = vals[np.abs(vals) <= 446.0]
+    assert len(kv_vals) <= rows * (D - 1)
+    for arr, lead, src in ((k, 448.0, kv_vals), (v, 446.0, vv_vals)):
+        arr[:, 0] = lead
+        flat = arr[:, 1:].reshape(-1)
+        flat[: len(src)] = src
+        arr[:, 1:] = flat.reshape(rows, D - 1)
+    kt = torch.from_numpy(k.reshape(T, H, D)).to(torch.bfloat16)
+    vt = torch.from_numpy(v.reshape(T, H, D)).to(torch.bfloat16)
+    assert np.array_equal(kt.float().numpy().reshape(rows, D), k)   # bf16 values as given
+    assert np.array_equal(vt.float().numpy().reshape(rows, D), v)
+    run.cache.kv_ring_append(kt.cuda(), vt.cuda())
+    run.oc.append(k.reshape(1, -1), v.reshape(1, -1))
+    assert_ring_bitexact(run)
+    say(f"fp8 codes: {len(kv_vals)} + {len(vv_vals)} values bit-exact")
+
+
 # ---- cache sets: one cache per (layer, denoising step), advanced by batched launches ----
 
 def test_tiny_set_stream_full_parity():
