@@ -43,6 +43,10 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per head in the sample")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="run one device copy of MIB MiB first (reference for HBM byte counters)")
+    p.add_argument("--cold", type=int, default=0, metavar="STEPS",
+                   help="after the timed steps, run STEPS more with a 512 MiB write before each "
+                        "RoPE, append and compress call (last-level cache flushed) and report "
+                        "those calls' times as 'cold'")
     return p.parse_args()
 
 
@@ -172,6 +176,7 @@ def main():
                      for s in range(args.steps)])  # ms
     ms = part.mean(axis=0)
     ms_step_events = float(part.sum(axis=1).mean())
+    step_pct = np.percentile(part.sum(axis=1), [10, 50, 90])
     ms_per_step = wall * 1e3 / args.steps
 
     fe = T * H * D                                   # elements per frame
@@ -216,7 +221,8 @@ def main():
                               "block_attention": round(ms[1], 4),
                               "kv_ring_append": round(ms[2], 4),
                               "convkv_compress": round(ms[3], 4),
-                              "sum_of_events": round(ms_step_events, 4)},
+                              "sum_of_events": round(ms_step_events, 4),
+                              "step_p10_p50_p90": [round(float(x), 4) for x in step_pct]},
         "stream_gbs": {"rope_reset_apply": round(rope_bytes / (ms[0] * 1e-3) / 1e9, 1),
                        "kv_ring_append": round(append_bytes / (ms[2] * 1e-3) / 1e9, 1),
                        "convkv_compress": round(compress_bytes / (ms[3] * 1e-3) / 1e9, 1)},
@@ -228,6 +234,41 @@ def main():
         "cpu_baseline": None,
     }
 
+    if args.cold:
+        # the streaming calls with their inputs out of the last-level cache: a 512 MiB write
+        # before each (the attention call between them keeps the step order)
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(args.cold):
+            q, k, v = pool[i % len(pool)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            scratch.fill_(1)
+            e[0].record(stream)
+            L.lact_rope_reset_apply(h, q, k, v, B, stream)
+            e[1].record(stream)
+            L.lact_block_attention(h, None, out, lse, stream)
+            scratch.fill_(2)
+            e[2].record(stream)
+            L.lact_kv_ring_append(h, k, v, B, stream)
+            e[3].record(stream)
+            scratch.fill_(3)
+            e[4].record(stream)
+            L.lact_convkv_compress(h, d_wk, d_bk, d_wv, d_bv, stream)
+            e[5].record(stream)
+            cold.append(e)
+            i += 1
+        torch.cuda.synchronize()
+        # mean over the steps: the compressor's slot count per step cycles (1, 2, 1, 2, 2)
+        cm = np.mean(np.array([[e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3]),
+                                e[4].elapsed_time(e[5])] for e in cold]), axis=0)
+        rec["cold"] = {"steps": args.cold,
+                       "mean_ms": {"rope_reset_apply": round(float(cm[0]), 4),
+                                     "kv_ring_append": round(float(cm[1]), 4),
+                                     "convkv_compress": round(float(cm[2]), 4)},
+                       "gbs": {"rope_reset_apply": round(rope_bytes / (cm[0] * 1e-3) / 1e9, 1),
+                               "kv_ring_append": round(append_bytes / (cm[1] * 1e-3) / 1e9, 1),
+                               "convkv_compress": round(compress_bytes / (cm[2] * 1e-3) / 1e9, 1)}}
+        del scratch
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, i, wk, bk,
                                            wv, bv)

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import compressed_kv_causal_amd as L
 import synth
 from stream_helpers import BF16, F32, FP8, Runner, SetRunner, rel_l2, sample_rows
 
@@ -314,6 +315,51 @@ def test_bf16_d128_multiblock_mask_vs_bruteforce(blocks):
     err, dl = run.compare_attention(res)
     say(f"bf16 d128 blocks {blocks}: rel L2 {err:.3e}, max dLSE {dl:.2e}")
     assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16], (blocks, err, dl)
+
+
+def test_bf16_d128_max_query_blocks():
+    """The largest call the ABI takes in query blocks: 16 blocks of one frame each (T = 64,
+    so every block is one 64-key tile and every tile boundary is a block boundary) over a
+    history, against the explicit mask matrix on every row."""
+    w = synth.workload("s512_bf16", heads=2, grid_h=8, grid_w=8, window_frames=6,
+                       mem_slots=4, max_block_frames=16, first_block=16, block=16)
+    run = Runner(w)
+    for _ in range(3):
+        run.step(16, attend=False)
+    blocks = [1] * 16
+    res = run.step(16, blocks=blocks, form=0)
+    err, dl = run.compare_attention(res)
+    say(f"16 query blocks: rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16]
+
+
+def test_bf16_d128_max_key_frames():
+    """The largest key set the ABI takes: reference 2 + memory 120 + window 118 + block 16 =
+    256 key frames (T = 64: 16384 keys, 256 tiles).  The memory is filled through the
+    stream (605 evicted frames), then a full step is compared with the oracle on sampled
+    rows of both heads; the stored memory, ring and reference stay bit-exact."""
+    w = synth.workload("s512_bf16", heads=2, grid_h=8, grid_w=8, window_frames=118,
+                       mem_slots=120, max_block_frames=16, first_block=16, block=16,
+                       ref_frames=2, pool_blocks=0)
+    cfg_kf = w["ref_frames"] + w["mem_slots"] + w["window_frames"] + w["max_block_frames"]
+    assert cfg_kf == L.LACT_MAX_KEY_FRAMES
+    run = Runner(w)
+    n = 0
+    while run.cache.state()["mem_len"] < w["mem_slots"]:
+        run.step(16, attend=False)
+        n += 1
+    assert n < 60
+    assert_state_matches(run)
+    assert len(run.cache.keys(16)) == cfg_kf
+    assert_keys_match(run, 16)
+    sel = sample_rows(w, 16, seed=5, per_head=64)
+    res = run.step(16, sel=sel)
+    err, dl = run.compare_attention(res)
+    say(f"256 key frames (Lk {cfg_kf * w['tokens']}): rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16]
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    assert_ref_bitexact(run)
 
 
 def test_bf16_d128_reference_raise_in_kernel():
