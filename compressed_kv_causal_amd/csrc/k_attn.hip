@@ -1,4 +1,4 @@
-// k_attn.hip -- block attention over [memory | window | current] on gfx950.
+// k_attn.hip -- block attention over [reference | memory | window | current] on gfx950.
 //
 // O = softmax(Q K^T / sqrt(D) + mask) V per head (walkthrough "SoulX-LiveAct", section
 // "ConvKV Memory": context = long-term memory, short-term window, current block; section

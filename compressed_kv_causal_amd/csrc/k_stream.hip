@@ -259,7 +259,7 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32
   }
 }
 
-// blockIdx.y = key frame: frames [0, n_hist) are history frames of [memory | window],
+// blockIdx.y = key frame: frames [0, n_hist) are history frames of [reference | memory | window],
 // rotated at t = fi into krot[h][fi*T + u] (only when the history is rebuilt, else the grid
 // starts at the block's frames); frames after are the block's frames i = fi - n_hist at
 // t = fi: q -> qrot (times q_scale = log2(e)/sqrt(D), so that q . k is the base-2 exponent

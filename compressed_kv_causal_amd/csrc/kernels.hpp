@@ -93,7 +93,7 @@ struct RopeTableArgs {
   int64_t entries;
 };
 
-// Attention of the staged block over [memory | window | current] (operand dtype).  The
+// Attention of the staged block over [reference | memory | window | current] (operand dtype).  The
 // staged queries carry the softmax scale and the change to base 2: q . k is already the
 // exponent of 2 that softmax(q k / sqrt(D)) takes.
 struct AttnArgs {

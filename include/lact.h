@@ -13,8 +13,9 @@
  *     listing 2603.11746, Figure 3 caption);
  *   - RoPE positions are reset so they stay bounded (press release, technical-principle
  *     paragraph; news summary, ConvKV Memory bullet);
- *   - the current block's queries attend over [memory | window | current] under the
- *     block-wise causal mask of block size m (walkthrough, section "Neighbor Forcing");
+ *   - the current block's queries attend over [reference | memory | window | current]
+ *     under the block-wise causal mask of block size m (walkthrough, section "Neighbor
+ *     Forcing"; the reference image's KV is the first of the context's partitions);
  *   - the footprint is constant for any video length (walkthrough, "Streaming Pipeline").
  *
  * Step order per AR step and per cache (one cache per layer and diffusion step):
@@ -207,13 +208,14 @@ lact_status lact_member_ref_set(lact_cache* cache, int32_t member, const void* k
  * technical-principle paragraph: RoPE Reset; news summary, ConvKV Memory bullet):
  * reference frame i -> t = i; memory rank j -> t = ref + j; window rank k ->
  * t = ref + mem_len + k; current frame i -> t = ref + mem_len + win_len + i (ref =
- * ref_frames); (h, w) = the token's grid cell.  Rotation of interleaved
- * channel pairs (2i, 2i+1) of each part by pos * theta^(-2i/d_part).
- * Writes krot (memory + window + current keys), qrot and vcur in the operand dtype
- * (q_dtype).  The stored history is read as stored (FP8_E4M3: code * per-(token, head)
- * scale; the model card's FP8 KV cache option keeps K/V in FP8 and widens them for the
- * attention), and an FP8 cache also gets its memory + window V dequantised into vhist.  The history part
- * is rebuilt only when the state changed since the last call.
+ * ref_frames); (h, w) = the token's grid cell.  Rotation of interleaved channel pairs
+ * (2i, 2i+1) of each part by pos * theta^(-2i/d_part).
+ * Writes krot (reference + memory + window + current keys), qrot and vcur in the operand
+ * dtype (q_dtype).  The stored history is read as stored (FP8_E4M3: code * per-(token,
+ * head) scale; the model card's FP8 KV cache option keeps K/V in FP8 and widens them for
+ * the attention), and an FP8 cache also gets its reference + memory + window V dequantised
+ * into vhist.  The history part is rebuilt only when the state changed since the last
+ * call.
  *   q, k_cur, v_cur: [n_frames*T][H][D] in q_dtype.  1 <= n_frames <= B_max. */
 lact_status lact_rope_reset_apply(lact_cache* cache, const void* q, const void* k_cur,
                                   const void* v_cur, int32_t n_frames, void* stream);
@@ -225,9 +227,9 @@ lact_status lact_member_rope_reset_apply(lact_cache* cache, int32_t member, cons
                                          void* stream);
 
 /* Block attention over the staged operands (walkthrough, "Neighbor Forcing": block-wise
- * causal mask of block size m; "ConvKV Memory": the [memory | window | current] context).
- * O = softmax(Q K^T / sqrt(D) + mask) V per head; every memory and window key is visible;
- * current key j is visible to query i iff block(j) <= block(i).
+ * causal mask of block size m; "ConvKV Memory": the [reference | memory | window | current]
+ * context).  O = softmax(Q K^T / sqrt(D) + mask) V per head; every reference, memory and
+ * window key is visible; current key j is visible to query i iff block(j) <= block(i).
  *   q_block_frames: HOST array of n_q_blocks block sizes in frames, summing to the staged
  *                   frame count; NULL means one block of all staged frames.
  *   out: [n*T][H][D] in q_dtype.  lse: [H][n*T] f32 natural-log log-sum-exp, or NULL.

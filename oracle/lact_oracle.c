@@ -20,15 +20,16 @@
  *        (hf.xjtesla.cn/Soul-AILab/LiveAct), section "Command Line Arguments":
  *        --fp8_kv_cache stores the KV cache in FP8 and dequantises on use.
  *
- * Readings where the pages are silent (each is listed with its reason in the design notes):
+ * Readings where the pages are silent (the plainest ones the rest of the pages support):
  *   conv: depthwise over time per (token, channel), kernel = stride = r, bias, no padding,
  *   tap k on frame r*g + k; RoPE: interleaved pairs, angle pos * theta^(-2i/d_part),
- *   3D split (t, h, w); positions reset to ranks [memory | window | current];
+ *   3D split (t, h, w); positions reset to ranks [reference | memory | window | current];
  *   e4m3 = OCP E4M3FN, one f32 scale per (token, head) = amax / 448.
  *
  * Parity pins: every function here is pinned by tests/test_oracle_pins.py against closed
- * forms, brute force or special cases; nothing is "parity unpinned" except the value of
- * FP8 attention beyond its error bar (see the design notes).
+ * forms, brute force or special cases.  The FP8 attention is the oracle's attention over
+ * the stored (quantised) values; what a kernel's own extra rounding adds is held to the
+ * FP8 bar, not pinned to a value.
  */
 #include <math.h>
 #include <pthread.h>

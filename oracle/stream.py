@@ -2,7 +2,7 @@
 attention of one AR step over it (test infrastructure).
 
 Per AR step and per cache the pages' order is: attend with the current block over
-[memory | window | current], append the block's KV (append-only), compress once between
+[reference | memory | window | current], append the block's KV (append-only), compress once between
 blocks (walkthrough "SoulX-LiveAct", sections "ConvKV Memory" and "Streaming Pipeline").
 
 Stored values: F32 and BF16 caches keep the input values (BF16 inputs are bf16-exact);
@@ -109,7 +109,7 @@ class OracleCache:
         return self.bk.keys(n_cur)
 
     def history(self):
-        """Stored K, V of [memory | window] in attention order, with positions.
+        """Stored K, V of [reference | memory | window] in attention order, with positions.
         Returns (k_vals, k_scales, v_vals, v_scales, t, u) with [L][H][D] values."""
         ks, kss, vs, vss, ts = [], [], [], [], []
         for kf in self.keys(0):
