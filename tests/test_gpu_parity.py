@@ -112,8 +112,9 @@ def test_s512_reference_step_parity():
 
 def test_fp8_reference_step_parity():
     """FP8 KV cache with a 2-frame reference segment (stored e4m3, dequantised by the RoPE
-    pass like the rest of the history)."""
-    _big_step_parity("fp8_kv", 11, 8, ref_frames=2)
+    pass like the rest of the history); 512x512 frames with 8 heads (the FP8 oracle's
+    cost grows with the channel count; the kernels' paths do not)."""
+    _big_step_parity("fp8_kv", 11, 8, ref_frames=2, heads=8)
 
 
 @pytest.mark.parametrize("blocks", [[1, 2, 3], [2, 2, 2], [3, 3], [6]])
@@ -300,6 +301,57 @@ def test_fp8_d64_small_stream():
     assert_memory_bitexact(run)
     assert_ring_bitexact(run)
     say(f"fp8 d64 stream: worst rel L2 {worst:.3e}")
+
+
+def test_f32_d128_small_stream():
+    """f32 cache and operands at D = 128 (the one-lane-per-row f32 kernel at its larger
+    width), T = 16, 3D RoPE split (44, 42, 42): 20 steps of the tiny schedule, every row
+    against the oracle, state and stored contents bit-exact."""
+    w = synth.workload("tiny_f32", head_dim=128, rope_mode=3, rope_split=(44, 42, 42))
+    run = Runner(w)
+    worst = 0.0
+    for s in range(20):
+        res = run.step(2)
+        err, dl = run.compare_attention(res)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[F32] and dl <= LSE_TOL[F32], (s, err, dl)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    say(f"f32 d128 stream: worst rel L2 {worst:.3e}")
+
+
+def test_bf16_d128_short_frames_stream():
+    """bf16 at D = 128 with T = 16 < 64 (a key tile would span several frames, so the
+    exact online-softmax kernel serves these shapes): 20 steps, every row against the
+    oracle, multi-block calls included."""
+    w = synth.workload("tiny_f32", head_dim=128, kv_dtype=BF16, q_dtype=BF16, max_block_frames=4)
+    run = Runner(w)
+    worst = 0.0
+    for s in range(20):
+        blocks = [1, 1] if s % 3 == 2 else None
+        res = run.step(2, blocks=blocks, form=0 if blocks else 1)
+        err, dl = run.compare_attention(res)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16], (s, err, dl)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    say(f"bf16 d128 T=16 stream: worst rel L2 {worst:.3e}")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_s512_bf16_step_parity_other_seeds(seed):
+    """The 512x512 bf16 step on two more input seeds (sampled rows of all heads)."""
+    w = synth.workload("s512_bf16")
+    run = Runner(w, seed=seed)
+    for n in synth.block_sizes(w, 11):
+        run.step(n, attend=False)
+    assert_memory_bitexact(run)
+    sel = sample_rows(w, 8, seed=seed, per_head=4)
+    res = run.step(8, sel=sel)
+    err, dl = run.compare_attention(res)
+    say(f"s512 seed {seed}: rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16]
 
 
 @pytest.mark.parametrize("blocks", [[1, 2, 3], [3, 3], [6], [2, 1, 1, 2]])
@@ -491,11 +543,11 @@ def test_tiny_set_stream_full_parity():
 
 
 def test_fp8_set_step_parity():
-    """512x512-shaped FP8 set of 2 members with a 2-frame reference: 11 blocks through the
-    batched append (quantising per member) and compress (each member's weights and scales),
-    every member's memory, ring and reference bit-exact; then a full step of each member
-    on sampled rows of all heads against its oracle."""
-    w = synth.workload("fp8_kv", ref_frames=2)
+    """FP8 set of 2 members with a 2-frame reference, 512x512 frames with 8 heads: 11
+    blocks through the batched append (quantising per member) and compress (each member's
+    weights and scales), every member's memory, ring and reference bit-exact; then a full
+    step of each member on sampled rows of all heads against its oracle."""
+    w = synth.workload("fp8_kv", ref_frames=2, heads=8)
     sr = SetRunner(w, 2)
     for n in synth.block_sizes(w, 11):
         sr.step(n, attend=False)
