@@ -174,6 +174,27 @@ def main():
     wall = time.perf_counter() - t0
     part = np.array([[evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(4)]
                      for s in range(args.steps)])  # ms
+
+    # the first block (no history) of a second, fresh cache, timed on its own
+    first = L.Cache(L.make_cfg(**w), device=dev)
+    if w.get("ref_frames", 0):
+        first.ref_set(*(torch.from_numpy(x.reshape(n_ref * T, H, D)).to(io).to(dev)
+                        for x in (kr, vr)))
+    fq, fk, fv = (t[: first_block * T] for t in pool[0])
+    fev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    fev[0].record(stream)
+    L.lact_rope_reset_apply(first.h, fq, fk, fv, first_block, stream)
+    fev[1].record(stream)
+    L.lact_block_attention(first.h, None, out[: first_block * T], None, stream)
+    fev[2].record(stream)
+    L.lact_kv_ring_append(first.h, fk, fv, first_block, stream)
+    fev[3].record(stream)
+    L.lact_convkv_compress(first.h, d_wk, d_bk, d_wv, d_bv, stream)
+    fev[4].record(stream)
+    torch.cuda.synchronize()
+    first_ms = [fev[j].elapsed_time(fev[j + 1]) for j in range(4)]
+    first.close()
+    del first
     ms = part.mean(axis=0)
     ms_step_events = float(part.sum(axis=1).mean())
     step_pct = np.percentile(part.sum(axis=1), [10, 50, 90])
@@ -217,6 +238,12 @@ def main():
                    "mem_slots": w["mem_slots"], "ratio": w["ratio"], "Lq": Lq, "Lk": Lk},
         "attn_tflops": round(attn_tflops, 2),
         "attn_exact_pass_tiles": f"{exact_tiles}/{n_flags}",
+        "first_block": {"frames": first_block, "Lq": first_block * T,
+                        "Lk": (first_block + w.get("ref_frames", 0)) * T,
+                        "ms": {"rope_reset_apply": round(first_ms[0], 4),
+                               "block_attention": round(first_ms[1], 4),
+                               "kv_ring_append": round(first_ms[2], 4),
+                               "convkv_compress": round(first_ms[3], 4)}},
         "step_breakdown_ms": {"rope_reset_apply": round(ms[0], 4),
                               "block_attention": round(ms[1], 4),
                               "kv_ring_append": round(ms[2], 4),
@@ -508,6 +535,17 @@ def set_main(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv, bv):
     """The oracle, as it stands, on a bounded sample of the same steady-state step: the
     attention of every head for a few query rows over the full key set (history rebuilt
@@ -563,8 +601,15 @@ def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv,
     secs = time.perf_counter() - t0
     frac = len(rr) / float(H * Lq)
     full = secs / frac
+    # one thread on a sixteenth of the sample (the same rows of every 16th head)
+    few = np.arange(0, len(rr), 16)
+    t1 = time.perf_counter()
+    oc.attention(q, k, v, sel=(heads[few], rr[few]), threads=1)
+    secs1 = time.perf_counter() - t1
+    full1 = secs1 / (len(few) / float(H * Lq))
     return {"value": round(B / full, 6), "unit": "latent frames/s (one layer, one diffusion step)",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": _cpu_model(),
+            "value_1_thread": round(B / full1, 6),
             "sample": (f"attention of all {H} heads x {len(rows)} query rows over Lk={Lk} keys "
                        f"({secs:.1f} s, double precision), extrapolated x{1 / frac:.0f} to the "
                        f"full step; history built by the oracle's compressor in {setup_s:.1f} s "
