@@ -230,8 +230,12 @@ lact_status lact_set_init(const lact_cfg* cfg, int32_t n_members, void* device_b
   if (bytes < L.total)
     return fail(LACT_E_CAPACITY, "device buffer of " + std::to_string(bytes) + " bytes; need " +
                                      std::to_string(L.total));
-  lact_cache* c = new (std::nothrow) lact_cache(*cfg, L, device_buf);
-  if (!c) return fail(LACT_E_CAPACITY, "host allocation of the handle failed");
+  lact_cache* c = nullptr;
+  try {  // the handle's per-member table allocates too; no exception crosses the C ABI
+    c = new lact_cache(*cfg, L, device_buf);
+  } catch (const std::bad_alloc&) {
+    return fail(LACT_E_CAPACITY, "host allocation of the handle failed");
+  }
   *out = c;
   return LACT_OK;
 }
