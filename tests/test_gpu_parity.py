@@ -142,6 +142,21 @@ def test_tiny_window_only_and_no_memory():
         assert_state_matches(run)
 
 
+def test_tiny_no_window_memory_only():
+    """W = 0 (every frame leaves the window at once): the context is [memory | current]
+    with up to r - 1 pending frames unseen; 15 steps of 2 frames, every row against the
+    oracle, state and memory bit-exact."""
+    w = synth.workload("tiny_f32", window_frames=0, mem_slots=4)
+    run = Runner(w)
+    for s in range(15):
+        assert_keys_match(run, 2)
+        res = run.step(2)
+        err, dl = run.compare_attention(res)
+        assert err <= ATTN_TOL[F32] and dl <= LSE_TOL[F32], (s, err, dl)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+
+
 @pytest.mark.parametrize("tap", [None, 0, 3])
 def test_frame_id_tag_on_device(tap):
     """No oracle: K element 0 of every frame holds the frame's absolute id.  With the
