@@ -8,7 +8,7 @@ import torch
 
 import compressed_kv_causal_amd as L
 import synth
-from stream_helpers import BF16, F32, FP8, Runner, SetRunner, rel_l2, sample_rows
+from stream_helpers import BF16, F32, FP8, Runner, SetRunner, sample_rows
 
 pytestmark = pytest.mark.gpu
 
