@@ -91,10 +91,18 @@ double lacto_e4m3_value(uint8_t code) {
   return s ? -mag : mag;
 }
 
+/* The magnitudes of codes 0x00..0x7E, lacto_e4m3_value of each, computed once. */
+static double e4m3_mag[127];
+static pthread_once_t e4m3_mag_once = PTHREAD_ONCE_INIT;
+static void e4m3_mag_init(void) {
+  for (int c = 0; c < 127; ++c) e4m3_mag[c] = lacto_e4m3_value((uint8_t)c);
+}
+
 /* Nearest finite e4m3 value to x (sign kept, so -0 -> 0x80); a tie goes to the code with
  * an even mantissa; |x| >= 448 saturates to +-448; NaN -> 0x7F / 0xFF.  The magnitudes of
  * codes 0x00..0x7E increase with the code, so a bisection finds the two neighbours. */
 uint8_t lacto_e4m3_encode(float x) {
+  pthread_once(&e4m3_mag_once, e4m3_mag_init);
   if (isnan(x)) return signbit(x) ? 0xFF : 0x7F;
   uint8_t sign = signbit(x) ? 0x80 : 0x00;
   double a = fabs((double)x);
@@ -102,14 +110,14 @@ uint8_t lacto_e4m3_encode(float x) {
   int lo = 0, hi = 126; /* largest code c with value(c) <= a */
   while (lo < hi) {
     int mid = (lo + hi + 1) / 2;
-    if (lacto_e4m3_value((uint8_t)mid) <= a)
+    if (e4m3_mag[mid] <= a)
       lo = mid;
     else
       hi = mid - 1;
   }
   int c = lo;
-  double d0 = a - lacto_e4m3_value((uint8_t)c);
-  double d1 = lacto_e4m3_value((uint8_t)(c + 1)) - a;
+  double d0 = a - e4m3_mag[c];
+  double d1 = e4m3_mag[c + 1] - a;
   if (d0 < d1) return (uint8_t)(sign | c);
   if (d1 < d0) return (uint8_t)(sign | (c + 1));
   return (uint8_t)(sign | ((c & 1) ? c + 1 : c));
