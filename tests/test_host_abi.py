@@ -315,3 +315,23 @@ def test_set_member_checks():
     with pytest.raises(L.LactError) as e:
         L.lact_set_init(cfg, 0, 0x10000000, need)
     assert e.value.status == 3
+
+
+def test_header_is_plain_c99():
+    """include/lact.h compiles as strict C99 (no C++ or compiler extensions) with every
+    warning an error; nothing is written (syntax check of a translation unit on stdin)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = ('#include "lact.h"\n'
+           "int main(void) {\n"
+           "  lact_cfg c; lact_layout l; lact_state s; lact_key_frame k;\n"
+           "  (void)c; (void)l; (void)s; (void)k;\n"
+           "  return LACT_MAX_KEY_FRAMES > 0 && LACT_MAX_MEMBERS > 0 ? 0 : 1;\n"
+           "}\n")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-I", inc, "-x", "c", "-"], input=src, text=True, capture_output=True)
+    assert r.returncode == 0, r.stderr
