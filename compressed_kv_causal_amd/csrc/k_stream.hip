@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
 #pragma unroll
   for (int t = 0; t < TOK; ++t) {
     const int32_t u = u0 + t < a.T ? u0 + t : a.T - 1;     // tail tokens repeat the last one
-    const int32_t hrow = u * a.H + c0 / a.D;
+    const int32_t hrow = u * a.H + c0 / (8 * LPR);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int64_t el = (int64_t)slot[k] * a.T * C + (int64_t)u * C + c0;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
     const int64_t dst = (int64_t)a.out_slot[gi] * a.T * C + (int64_t)u * C + c0;
     const float s = store8_kv<LPR>(p.mem, KV, dst, acc);
     if (KV == DT_FP8 && (threadIdx.x % LPR) == 0)
-      p.mem_scale[(int64_t)a.out_slot[gi] * rows + u * a.H + c0 / a.D] = s;
+      p.mem_scale[(int64_t)a.out_slot[gi] * rows + u * a.H + c0 / (8 * LPR)] = s;
   }
 }
 
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(64) void k_compress(const CompressArgs a) {
   const int32_t u0 = blockIdx.y * TOK;
   for (int32_t u = u0; u < u0 + TOK && u < a.T; ++u) {
     const int64_t el = (int64_t)u * C + c0;                // element offset inside a frame
-    const int32_t hrow = u * a.H + c0 / a.D;               // (token, head) row inside a frame
+    const int32_t hrow = u * a.H + c0 / (8 * LPR);         // (token, head) row inside a frame
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = b[e];
@@ -234,25 +234,24 @@ __global__ __launch_bounds__(256) void k_rope_table(const RopeTableArgs a) {
 }
 
 // Rotates the 4 pairs of one lane (channels 8*li .. 8*li+7) at temporal position t.
+// The table offsets of the temporal, row and column parts are computed once, before the
+// per-pair (per-lane) selection; with the token u uniform per block they are scalar work.
 __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32_t u, int li,
                                              float* x) {
+  const int32_t ht = a.split_t / 2, hh = a.split_h / 2, hw = a.split_w / 2;
+  const int32_t urow = u / a.grid_w, ucol = u - urow * a.grid_w;
+  const int64_t base1 = ((int64_t)t * a.T + u) * (a.D / 2);            // 1D
+  const int32_t base_t = t * ht;                                        // 3D, temporal part
+  const int32_t base_h = a.key_frames_max * ht + urow * hh - ht;        // row part, - ht
+  const int32_t base_w = a.key_frames_max * ht + a.grid_h * hh + ucol * hw - ht - hh;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int32_t pair = li * 4 + p;
     float2 cs;
-    if (a.rope_mode == 1) {
-      cs = a.table[((int64_t)t * a.T + u) * (a.D / 2) + pair];
-    } else {
-      const int32_t ht = a.split_t / 2, hh = a.split_h / 2, hw = a.split_w / 2;
-      if (pair < ht) {
-        cs = a.table[t * ht + pair];
-      } else if (pair < ht + hh) {
-        cs = a.table[a.key_frames_max * ht + (u / a.grid_w) * hh + (pair - ht)];
-      } else {
-        cs = a.table[a.key_frames_max * ht + a.grid_h * hh + (u % a.grid_w) * hw +
-                     (pair - ht - hh)];
-      }
-    }
+    if (a.rope_mode == 1)
+      cs = a.table[base1 + pair];
+    else
+      cs = a.table[(pair < ht ? base_t : (pair < ht + hh ? base_h : base_w)) + pair];
     const float x0 = x[2 * p], x1 = x[2 * p + 1];
     x[2 * p] = x0 * cs.x - x1 * cs.y;
     x[2 * p + 1] = x0 * cs.y + x1 * cs.x;
@@ -266,13 +265,18 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32
 // of the softmax), k -> krot[h][t*T + u], v -> vcur.  Every output is in the operand
 // dtype (in_dtype).  An FP8 cache is dequantised on the way (code * row scale), and its
 // history V rows are dequantised into vhist in attention order as well.
+// Work split: a block covers the heads of one token (blockIdx.x = token * hb + part,
+// hb = blocks per token), D/8 lanes per (token, head) row, so the token index is uniform
+// per block and no lane divides.
 template <int LPR>
-__global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
-  const int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+__global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
+  const int32_t hb = (a.H * LPR + (int32_t)blockDim.x - 1) / (int32_t)blockDim.x;
+  const int32_t u = (int32_t)blockIdx.x / hb;
+  const int32_t e = ((int32_t)blockIdx.x - u * hb) * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+  const int32_t h = e / LPR, li = e % LPR;
+  if (h >= a.H) return;
   const int32_t rows = a.T * a.H;
-  const int32_t row = e / LPR, li = e % LPR;              // row = u * H + h inside the frame
-  if (row >= rows) return;
-  const int32_t u = row / a.H, h = row - u * a.H;
+  const int32_t row = u * a.H + h;                         // row inside the frame
   const int32_t n_hist = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   const int32_t fi = blockIdx.y + (a.hist_rows ? 0 : n_hist);
   const int64_t KFT = (int64_t)a.key_frames_max * a.T;
@@ -370,11 +374,14 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
   const int32_t frames = (a.hist_rows ? n_hist : 0) + a.n_cur;
   if (frames <= 0) return hipSuccess;
   const int lpr = a.D / 8;
-  dim3 grid(blocks_for((int64_t)a.T * a.H * lpr), frames);
+  const int per_token = a.H * lpr;                          // lanes of one token's heads
+  const int threads = per_token >= 1024 ? 1024 : ((per_token + 63) / 64) * 64;
+  const int hb = (per_token + threads - 1) / threads;       // blocks per token
+  dim3 grid((unsigned)(a.T * hb), frames);
   if (a.D == 128)
-    hipLaunchKernelGGL(k_rope<16>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rope<16>, grid, dim3(threads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_rope<8>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rope<8>, grid, dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
