@@ -318,6 +318,30 @@ def test_fp8_d64_small_stream():
     say(f"fp8 d64 stream: worst rel L2 {worst:.3e}")
 
 
+@pytest.mark.parametrize("kv", [BF16, FP8], ids=["bf16", "fp8"])
+def test_many_heads_stream(kv):
+    """72 heads x 128 on an 8x8 grid with a reference frame: one token's rows take 1152
+    RoPE lanes, more than one workgroup, so the pass splits each token over two; 10 steps
+    with history rebuilt from reference, memory and window, every row against the oracle,
+    state and memory bit-exact."""
+    w = synth.workload("tiny_ref", heads=72, head_dim=128, grid_h=8, grid_w=8, kv_dtype=kv,
+                       q_dtype=BF16, rope_mode=3, rope_split=(44, 42, 42),
+                       outliers=(kv == FP8))
+    run = Runner(w)
+    worst = 0.0
+    for s in range(10):
+        res = run.step(2)
+        err, dl = run.compare_attention(res)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[kv], (s, err, dl)
+        assert_lse(run, res, kv)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    assert_ref_bitexact(run)
+    say(f"72-head {'fp8' if kv == FP8 else 'bf16'} stream: worst rel L2 {worst:.3e}")
+
+
 def test_f32_d128_small_stream():
     """f32 cache and operands at D = 128 (the one-lane-per-row f32 kernel at its larger
     width), T = 16, 3D RoPE split (44, 42, 42): 20 steps of the tiny schedule, every row
