@@ -21,6 +21,7 @@ LACT_F32, LACT_BF16, LACT_FP8_E4M3 = 0, 1, 2
 LACT_MAX_KEY_FRAMES = 256
 LACT_MAX_Q_BLOCKS = 16
 LACT_MAX_MEMBERS = 1024
+LACT_MAX_TOKENS = 262144
 SEG_MEMORY, SEG_WINDOW, SEG_CURRENT, SEG_REF = 0, 1, 2, 3
 STATUS = {0: "LACT_OK", 1: "LACT_E_INVALID", 2: "LACT_E_SHAPE", 3: "LACT_E_CAPACITY",
           4: "LACT_E_DTYPE", 5: "LACT_E_STATE", 6: "LACT_E_HIP"}

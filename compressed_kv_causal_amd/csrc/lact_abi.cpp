@@ -45,6 +45,8 @@ lact_status check_cfg(const lact_cfg* c) {
     return fail(LACT_E_CAPACITY, "ref_frames + mem_slots + window_frames + max_block_frames exceeds " +
                                      std::to_string(LACT_MAX_KEY_FRAMES));
   const int64_t T = (int64_t)c->grid_h * c->grid_w;
+  if (T > LACT_MAX_TOKENS)
+    return fail(LACT_E_CAPACITY, "grid_h * grid_w exceeds " + std::to_string(LACT_MAX_TOKENS));
   if (T * c->heads * c->head_dim > (int64_t(1) << 28) || kf * T > (int64_t(1) << 24))
     return fail(LACT_E_CAPACITY, "frame or key length too large");
   const bool ok_dt = (c->q_dtype == LACT_F32 && c->kv_dtype == LACT_F32) ||

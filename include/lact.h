@@ -77,8 +77,12 @@ typedef struct {
                             every step; 0 = none.  Set once with lact_ref_set.           */
 } lact_cfg;
 
-/* Supported: head_dim 64 or 128; heads >= 1; T >= 1; W >= 0; M >= 0; 1 <= r <= 16;
- * 1 <= B_max; ref_frames >= 0; ref_frames + M + W + B_max <= LACT_MAX_KEY_FRAMES. */
+/* Supported: head_dim 64 or 128; heads >= 1; 1 <= T <= LACT_MAX_TOKENS; W >= 0; M >= 0;
+ * 1 <= r <= 16; 1 <= B_max; ref_frames >= 0; ref_frames + M + W + B_max <=
+ * LACT_MAX_KEY_FRAMES; T * heads * head_dim <= 2^28 and (ref_frames + M + W + B_max) * T
+ * <= 2^24 (LACT_E_CAPACITY otherwise).  LACT_MAX_TOKENS keeps every launch grid within
+ * the device's per-dimension limits. */
+#define LACT_MAX_TOKENS 262144
 #define LACT_MAX_KEY_FRAMES 256
 #define LACT_MAX_Q_BLOCKS 16
 #define LACT_MAX_MEMBERS 1024

@@ -110,6 +110,7 @@ def test_set_layout_and_footprint():
     (dict(rope_split=(44, 42, 40)), 2), (dict(rope_split=(43, 43, 42)), 2), (dict(rope_mode=2), 2),
     (dict(rope_theta=0.5), 1), (dict(ref_frames=-1), 2),
     (dict(ref_frames=100, mem_slots=100, window_frames=50, max_block_frames=8), 3),
+    (dict(grid_h=1024, grid_w=512), 3),
 ])
 def test_config_validation(kw, status):
     with pytest.raises(L.LactError) as e:
