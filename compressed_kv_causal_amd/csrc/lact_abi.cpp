@@ -267,7 +267,13 @@ lact_status lact_member_rope_reset_apply(lact_cache* c, int32_t member, const vo
     return fail(LACT_E_STATE, "the reference segment has not been set (lact_ref_set)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lact_cfg& g = c->cfg;
-  if (!c->table_ready) {
+  // Under stream capture the launches run only when the graph does: the table and the
+  // history are then recorded into the graph every time (each replay is self-contained),
+  // and neither is marked as present for later eager calls.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) cap = hipStreamCaptureStatusNone;
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+  if (!c->table_ready || capturing) {
     lact::RopeTableArgs t;
     t.table = static_cast<float2*>(c->at(c->lay.rope_table));
     t.rope_mode = g.rope_mode;
@@ -283,7 +289,7 @@ lact_status lact_member_rope_reset_apply(lact_cache* c, int32_t member, const vo
     t.entries = rope_table_entries(g);
     hipError_t e = lact::launch_rope_table(t, s);
     if (e != hipSuccess) return hip_fail(e, "rope table launch");
-    c->table_ready = true;
+    if (!capturing) c->table_ready = true;
   }
   lact::RopeArgs a;
   a.q = q;
@@ -308,8 +314,8 @@ lact_status lact_member_rope_reset_apply(lact_cache* c, int32_t member, const vo
   a.vhist = g.kv_dtype == LACT_FP8_E4M3 ? c->at(c->lay.vhist) : nullptr;
   a.table = static_cast<const float2*>(c->at(c->lay.rope_table));
   a.hist = c->hist();
-  const bool rebuild =
-      !(c->hist_built && c->hist_version == c->plan.version() && c->hist_member == member);
+  const bool rebuild = capturing || !(c->hist_built && c->hist_version == c->plan.version() &&
+                                       c->hist_member == member);
   a.hist_rows = rebuild ? 1 : 0;
   a.n_cur = n_frames;
   a.T = c->T();
@@ -328,7 +334,7 @@ lact_status lact_member_rope_reset_apply(lact_cache* c, int32_t member, const vo
   a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
   hipError_t e = lact::launch_rope(a, s);
   if (e != hipSuccess) return hip_fail(e, "rope launch");
-  c->hist_built = true;
+  c->hist_built = !capturing;
   c->hist_version = c->plan.version();
   c->hist_member = member;
   c->staged = true;

@@ -219,7 +219,9 @@ lact_status lact_member_ref_set(lact_cache* cache, int32_t member, const void* k
  * head) scale; the model card's FP8 KV cache option keeps K/V in FP8 and widens them for
  * the attention), and an FP8 cache also gets its reference + memory + window V dequantised
  * into vhist.  The history part is rebuilt only when the state changed since the last
- * call.
+ * call.  A call made while `stream` is being captured into a HIP graph records the
+ * history rebuild (and the cache's one-time cos/sin table) every time, so each replay
+ * stages everything itself, and leaves both marked absent for the next eager call.
  *   q, k_cur, v_cur: [n_frames*T][H][D] in q_dtype.  1 <= n_frames <= B_max. */
 lact_status lact_rope_reset_apply(lact_cache* cache, const void* q, const void* k_cur,
                                   const void* v_cur, int32_t n_frames, void* stream);

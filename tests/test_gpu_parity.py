@@ -584,6 +584,44 @@ def test_rope_attention_graph_replay():
     say("rope + attention graph: 3 replays bit-identical to the eager call")
 
 
+def test_first_rope_call_captured():
+    """A fresh cache whose first RoPE + attention call is captured into a HIP graph: an
+    eager call made before the graph has ever run still computes the cos/sin table and the
+    history itself, and each replay stages everything on its own; both give the bits of a
+    second cache that ran eagerly throughout."""
+    w = synth.workload("s512_bf16", heads=2, grid_h=8, grid_w=8, window_frames=4,
+                       mem_slots=4, max_block_frames=2)
+    a, b = Runner(w, with_oracle=False), Runner(w, with_oracle=False)
+    for _ in range(8):
+        a.step(2, attend=False)
+        b.step(2, attend=False)
+    (q, _), (k, _), (v, _) = a.inputs(2)
+    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    new = lambda: (torch.empty((2 * T, H, D), dtype=torch.bfloat16, device="cuda"),
+                   torch.empty((H, 2 * T), dtype=torch.float32, device="cuda"))
+    (want_o, want_l), (out_g, lse_g), (out_e, lse_e) = new(), new(), new()
+    b.cache.rope_reset_apply(q, k, v)
+    b.cache.block_attention(out=want_o, lse=want_l)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        a.cache.rope_reset_apply(q, k, v)
+        a.cache.block_attention(out=out_g, lse=lse_g)
+    a.cache.rope_reset_apply(q, k, v)                 # eager, before any replay
+    a.cache.block_attention(out=out_e, lse=lse_e)
+    torch.cuda.synchronize()
+    assert torch.equal(out_e, want_o) and torch.equal(lse_e, want_l)
+    for rep in range(2):
+        out_g.zero_()
+        lse_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, want_o) and torch.equal(lse_g, want_l), rep
+        b.cache.rope_reset_apply(q, k, v)             # other eager work between replays
+        torch.cuda.synchronize()
+    say("first call captured: eager call and 2 replays bit-identical to an eager cache")
+
+
 # ---- cache sets: one cache per (layer, denoising step), advanced by batched launches ----
 
 def test_tiny_set_stream_full_parity():
