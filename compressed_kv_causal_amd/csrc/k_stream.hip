@@ -234,24 +234,25 @@ __global__ __launch_bounds__(256) void k_rope_table(const RopeTableArgs a) {
 }
 
 // Rotates the 4 pairs of one lane (channels 8*li .. 8*li+7) at temporal position t.
-// The table offsets of the temporal, row and column parts are computed once, before the
-// per-pair (per-lane) selection; with the token u uniform per block they are scalar work.
 __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32_t u, int li,
                                              float* x) {
-  const int32_t ht = a.split_t / 2, hh = a.split_h / 2, hw = a.split_w / 2;
-  const int32_t urow = u / a.grid_w, ucol = u - urow * a.grid_w;
-  const int64_t base1 = ((int64_t)t * a.T + u) * (a.D / 2);            // 1D
-  const int32_t base_t = t * ht;                                        // 3D, temporal part
-  const int32_t base_h = a.key_frames_max * ht + urow * hh - ht;        // row part, - ht
-  const int32_t base_w = a.key_frames_max * ht + a.grid_h * hh + ucol * hw - ht - hh;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int32_t pair = li * 4 + p;
     float2 cs;
-    if (a.rope_mode == 1)
-      cs = a.table[base1 + pair];
-    else
-      cs = a.table[(pair < ht ? base_t : (pair < ht + hh ? base_h : base_w)) + pair];
+    if (a.rope_mode == 1) {
+      cs = a.table[((int64_t)t * a.T + u) * (a.D / 2) + pair];
+    } else {
+      const int32_t ht = a.split_t / 2, hh = a.split_h / 2, hw = a.split_w / 2;
+      if (pair < ht) {
+        cs = a.table[t * ht + pair];
+      } else if (pair < ht + hh) {
+        cs = a.table[a.key_frames_max * ht + (u / a.grid_w) * hh + (pair - ht)];
+      } else {
+        cs = a.table[a.key_frames_max * ht + a.grid_h * hh + (u % a.grid_w) * hw +
+                     (pair - ht - hh)];
+      }
+    }
     const float x0 = x[2 * p], x1 = x[2 * p + 1];
     x[2 * p] = x0 * cs.x - x1 * cs.y;
     x[2 * p + 1] = x0 * cs.y + x1 * cs.x;
@@ -265,18 +266,13 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32
 // of the softmax), k -> krot[h][t*T + u], v -> vcur.  Every output is in the operand
 // dtype (in_dtype).  An FP8 cache is dequantised on the way (code * row scale), and its
 // history V rows are dequantised into vhist in attention order as well.
-// Work split: a block covers the heads of one token (blockIdx.x = token * hb + part,
-// hb = blocks per token), D/8 lanes per (token, head) row, so the token index is uniform
-// per block and no lane divides.
 template <int LPR>
-__global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
-  const int32_t hb = (a.H * LPR + (int32_t)blockDim.x - 1) / (int32_t)blockDim.x;
-  const int32_t u = (int32_t)blockIdx.x / hb;
-  const int32_t e = ((int32_t)blockIdx.x - u * hb) * (int32_t)blockDim.x + (int32_t)threadIdx.x;
-  const int32_t h = e / LPR, li = e % LPR;
-  if (h >= a.H) return;
+__global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
+  const int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
   const int32_t rows = a.T * a.H;
-  const int32_t row = u * a.H + h;                         // row inside the frame
+  const int32_t row = e / LPR, li = e % LPR;              // row = u * H + h inside the frame
+  if (row >= rows) return;
+  const int32_t u = row / a.H, h = row - u * a.H;
   const int32_t n_hist = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   const int32_t fi = blockIdx.y + (a.hist_rows ? 0 : n_hist);
   const int64_t KFT = (int64_t)a.key_frames_max * a.T;
@@ -374,14 +370,11 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
   const int32_t frames = (a.hist_rows ? n_hist : 0) + a.n_cur;
   if (frames <= 0) return hipSuccess;
   const int lpr = a.D / 8;
-  const int per_token = a.H * lpr;                          // lanes of one token's heads
-  const int threads = per_token >= 1024 ? 1024 : ((per_token + 63) / 64) * 64;
-  const int hb = (per_token + threads - 1) / threads;       // blocks per token
-  dim3 grid((unsigned)(a.T * hb), frames);
+  dim3 grid(blocks_for((int64_t)a.T * a.H * lpr), frames);
   if (a.D == 128)
-    hipLaunchKernelGGL(k_rope<16>, grid, dim3(threads), 0, s, a);
+    hipLaunchKernelGGL(k_rope<16>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_rope<8>, grid, dim3(threads), 0, s, a);
+    hipLaunchKernelGGL(k_rope<8>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
