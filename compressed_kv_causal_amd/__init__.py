@@ -164,6 +164,28 @@ def _ptr(t, dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, shape, dtype, device, name):
+    """Checks a tensor handed to a kernel: exact shape, dtype and device (the C calls take
+    bare pointers and trust these, so a mismatch must stop here)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the cache on {device}")
+
+
+def _frames(t, T, name):
+    """Frames in a [n * T, ...] tensor (n >= 1 whole frames)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() < 1 or t.shape[0] == 0 or t.shape[0] % T:
+        raise ValueError(f"{name} has {tuple(t.shape)[:1]} rows, not a whole number of {T}-token frames")
+    return t.shape[0] // T
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -360,9 +382,15 @@ class Cache:
         except Exception:
             pass
 
-    # the four hot-path calls
+    # the four hot-path calls (every tensor is checked for shape, dtype and device first;
+    # the lact_* functions above take the caller's sizes on trust)
+    def _io(self, t, rows, name):
+        _expect(t, (rows, self.H, self.D), self.io_dtype, self.buf.device, name)
+
     def rope_reset_apply(self, q, k_cur, v_cur, stream=None, member=0):
-        n = q.shape[0] // self.T
+        n = _frames(q, self.T, "q")
+        for t, name in ((q, "q"), (k_cur, "k_cur"), (v_cur, "v_cur")):
+            self._io(t, n * self.T, name)
         if self.members == 1 and member == 0:
             lact_rope_reset_apply(self.h, q, k_cur, v_cur, n, stream)
         else:
@@ -373,6 +401,9 @@ class Cache:
         Lq = st["staged_frames"] * self.T
         if out is None:
             out = torch.empty((Lq, self.H, self.D), dtype=self.io_dtype, device=self.buf.device)
+        self._io(out, Lq, "out")
+        if lse is not None:
+            _expect(lse, (self.H, Lq), torch.float32, self.buf.device, "lse")
         if self.members == 1 and member == 0:
             lact_block_attention(self.h, q_block_frames, out, lse, stream)
         else:
@@ -380,7 +411,9 @@ class Cache:
         return out
 
     def ref_set(self, k_ref, v_ref, stream=None, member=0):
-        n = k_ref.shape[0] // self.T
+        n = _frames(k_ref, self.T, "k_ref")
+        self._io(k_ref, n * self.T, "k_ref")
+        self._io(v_ref, n * self.T, "v_ref")
         if self.members == 1 and member == 0:
             lact_ref_set(self.h, k_ref, v_ref, n, stream)
         else:
@@ -388,10 +421,18 @@ class Cache:
 
     def kv_ring_append(self, k_new, v_new, stream=None):
         """k_new, v_new: [members * n * T, H, D] (members stacked) or [n * T, H, D]."""
-        lact_kv_ring_append(self.h, k_new, v_new, k_new.shape[0] // (self.T * self.members),
-                            stream)
+        n = _frames(k_new, self.T * self.members, "k_new")
+        self._io(k_new, self.members * n * self.T, "k_new")
+        self._io(v_new, self.members * n * self.T, "v_new")
+        lact_kv_ring_append(self.h, k_new, v_new, n, stream)
 
     def convkv_compress(self, w_k, b_k, w_v, b_v, stream=None):
+        """w_k, w_v: [C, r] f32 ([members, C, r] for a set); b_k, b_v: [C] ([members, C])."""
+        C, r = self.H * self.D, self.cfg.ratio
+        lead = () if self.members == 1 else (self.members,)
+        for t, shape, name in ((w_k, lead + (C, r), "w_k"), (w_v, lead + (C, r), "w_v"),
+                               (b_k, lead + (C,), "b_k"), (b_v, lead + (C,), "b_v")):
+            _expect(t, shape, torch.float32, self.buf.device, name)
         return lact_convkv_compress(self.h, w_k, b_k, w_v, b_v, stream)
 
     def state(self):

@@ -342,6 +342,40 @@ def test_many_heads_stream(kv):
     say(f"72-head {'fp8' if kv == FP8 else 'bf16'} stream: worst rel L2 {worst:.3e}")
 
 
+def test_binding_rejects_mismatched_tensors():
+    """Tensors of the wrong shape, dtype or device (or not whole frames) are refused by the
+    binding before anything is launched, and the bookkeeping is left as it was."""
+    w = synth.workload("tiny_f32")
+    run = Runner(w, with_oracle=False)
+    for _ in range(3):
+        run.step(2, attend=False)
+    c = run.cache
+    T, H, D, C = w["tokens"], w["heads"], w["head_dim"], w["channels"]
+    before = {k: c.state()[k] for k in ("F", "E", "G", "version")}
+    good = torch.zeros((2 * T, H, D), dtype=torch.float32, device="cuda")
+    bad = [torch.zeros((2 * T + 1, H, D), device="cuda"), torch.zeros((2 * T, H + 1, D), device="cuda"),
+           torch.zeros((2 * T, H, D), dtype=torch.bfloat16, device="cuda"), torch.zeros((2 * T, H, D))]
+    for x in bad:
+        for args in ((x, good, good), (good, x, good), (good, good, x)):
+            with pytest.raises(ValueError):
+                c.rope_reset_apply(*args)
+        with pytest.raises(ValueError):
+            c.kv_ring_append(good, x)
+    c.rope_reset_apply(good, good, good)
+    with pytest.raises(ValueError):
+        c.block_attention(out=torch.zeros((T, H, D), device="cuda"))
+    with pytest.raises(ValueError):
+        c.block_attention(lse=torch.zeros((H, T), device="cuda"))
+    wk = torch.zeros((C, 5), device="cuda")
+    bk = torch.zeros((C,), device="cuda")
+    for args in ((wk[:, :4].contiguous(), bk, wk, bk), (wk, bk[:-1].contiguous(), wk, bk),
+                 (wk, bk, wk.double(), bk)):
+        with pytest.raises(ValueError):
+            c.convkv_compress(*args)
+    torch.cuda.synchronize()
+    assert {k: c.state()[k] for k in before} == before
+
+
 def test_f32_d128_small_stream():
     """f32 cache and operands at D = 128 (the one-lane-per-row f32 kernel at its larger
     width), T = 16, 3D RoPE split (44, 42, 42): 20 steps of the tiny schedule, every row

@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import compressed_kv_causal_amd as L
 import synth
@@ -336,3 +337,21 @@ def test_header_is_plain_c99():
     r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
                         "-I", inc, "-x", "c", "-"], input=src, text=True, capture_output=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_binding_tensor_checks():
+    """The binding's checks on tensors handed to kernels: exact shape, dtype and device,
+    and whole frames; the C calls take bare pointers and trust them."""
+    cpu = torch.device("cpu")
+    t = torch.zeros((32, 2, 64), dtype=torch.bfloat16)
+    L._expect(t, (32, 2, 64), torch.bfloat16, cpu, "q")
+    for shape, dtype, dev in (((16, 2, 64), torch.bfloat16, cpu), ((32, 2, 64), torch.float32, cpu),
+                              ((32, 2, 64), torch.bfloat16, torch.device("cuda", 0))):
+        with pytest.raises(ValueError):
+            L._expect(t, shape, dtype, dev, "q")
+    with pytest.raises(TypeError):
+        L._expect([0.0], (1,), torch.float32, cpu, "q")
+    assert L._frames(t, 16, "q") == 2
+    for bad, T in ((t, 24), (torch.zeros((0, 2, 64)), 16)):
+        with pytest.raises(ValueError):
+            L._frames(bad, T, "q")
