@@ -8,8 +8,9 @@ workload's shapes, generated before timing and resident in HBM (a pool of 7 bloc
 through, so consecutive steps read different data).
 
 Prints one JSON line: whole-step latent frames/s as `value`, the attention kernel's
-achieved TFLOP/s against the bf16 MFMA peak in `roofline`, and the CPU oracle timed on a
-bounded sample of the same step in `cpu_baseline`.
+achieved TFLOP/s against the bf16 MFMA peak in `roofline`, the CPU oracle timed on a
+bounded sample of the same step in `cpu_baseline`, and in `parity` the device's output for
+that sample (computed after the timed region) against the oracle's.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload s512_bf16]
 """
@@ -297,8 +298,8 @@ def main():
                                "convkv_compress": round(compress_bytes / (cm[2] * 1e-3) / 1e9, 1)}}
         del scratch
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, i, wk, bk,
-                                           wv, bv)
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool,
+                                                          i, wk, bk, wv, bv)
     print(json.dumps(rec), flush=True)
 
 
@@ -597,7 +598,7 @@ def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv,
     rr = np.tile(rows, H)
     threads = min(16, os.cpu_count() or 1)
     t0 = time.perf_counter()
-    oc.attention(q, k, v, sel=(heads, rr), threads=threads)
+    O_ref = oc.attention(q, k, v, sel=(heads, rr), threads=threads)[0]
     secs = time.perf_counter() - t0
     frac = len(rr) / float(H * Lq)
     full = secs / frac
@@ -607,13 +608,24 @@ def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv,
     oc.attention(q, k, v, sel=(heads[few], rr[few]), threads=1)
     secs1 = time.perf_counter() - t1
     full1 = secs1 / (len(few) / float(H * Lq))
+    # The timed configuration's own output for that step (RoPE + attention on the device,
+    # after the timed region) on the same rows, against the oracle's.
+    cache.rope_reset_apply(*pool[next_step % len(pool)])
+    got = cache.block_attention()
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy()[rr, heads, :].astype(np.float64)
+    err = float(np.linalg.norm(got - O_ref) / np.linalg.norm(O_ref))
+    bar = {0: 1e-5, 1: 1e-2, 2: 5e-2}[w["kv_dtype"]]
+    parity = {"rel_l2": float(f"{err:.3e}"), "bar": bar, "ok": err <= bar,
+              "rows": f"all {H} heads x {len(rows)} query rows of the next steady-state step, "
+                      "attention output against the oracle"}
     return {"value": round(B / full, 6), "unit": "latent frames/s (one layer, one diffusion step)",
             "cores": threads, "kind": "oracle", "cpu_model": _cpu_model(),
             "value_1_thread": round(B / full1, 6),
             "sample": (f"attention of all {H} heads x {len(rows)} query rows over Lk={Lk} keys "
                        f"({secs:.1f} s, double precision), extrapolated x{1 / frac:.0f} to the "
                        f"full step; history built by the oracle's compressor in {setup_s:.1f} s "
-                       "(not counted); rope/append/compress not counted")}
+                       "(not counted); rope/append/compress not counted")}, parity
 
 
 if __name__ == "__main__":
