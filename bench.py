@@ -76,8 +76,9 @@ def load_traffic(kernel_file, launches_key):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the ConvKV step is built and measured for a "
-              "single MI355X (no sharding or collectives in this build).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the ConvKV step is measured on a single MI355X "
+              "(the library has no sharding or collectives); run it with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
