@@ -246,10 +246,13 @@ def test_s720_bf16_step_parity():
     _big_step_parity("s720_bf16", 11, 8, first_check=True)
 
 
-def test_grid_w6_b8_step_parity():
-    """The model card's chosen memory-block / current-block pair (6 / 8): window 6, blocks
-    of 8, memory 16 -- ring R = 17, memory and ring bit-exact, step attention vs oracle."""
-    _big_step_parity("grid_w6_b8", 11, 8)
+@pytest.mark.parametrize("wb", [(6, 8), (6, 6), (8, 8)], ids=["w6_b8", "w6_b6", "w8_b8"])
+def test_grid_step_parity(wb):
+    """The model card's memory-block / current-block pairs (window W, blocks of B, memory
+    16; 6 / 8 is the chosen one): ring R = W + B + 4, memory and ring bit-exact after the
+    warm-up, then a step's attention against the oracle on sampled rows."""
+    W, B = wb
+    _big_step_parity(f"grid_w{W}_b{B}", 11, B)
 
 
 def test_train_form_long_sequence():
