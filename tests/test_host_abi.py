@@ -355,3 +355,30 @@ def test_binding_tensor_checks():
     for bad, T in ((t, 24), (torch.zeros((0, 2, 64)), 16)):
         with pytest.raises(ValueError):
             L._frames(bad, T, "q")
+
+
+def test_c_client_against_the_header():
+    """A plain C program (tests/c_client/plan_client.c) built with gcc against
+    include/lact.h and linked to liblact.so: the structs and calls as a C compiler sees
+    them, on the host-only calls (sizing, layout, errors, 1000 planner steps against the
+    schedule's closed form)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(L.LIB_PATH)
+    out_dir = os.path.join(root, "_build", "c_client")       # git-ignored build folder
+    os.makedirs(out_dir, exist_ok=True)
+    exe = os.path.join(out_dir, "plan_client")
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                        "-I", os.path.join(root, "include"),
+                        os.path.join(root, "tests", "c_client", "plan_client.c"),
+                        "-L", libdir, "-llact", f"-Wl,-rpath,{libdir}", f"-Wl,-rpath,{rocm_lib}",
+                        "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "1000 planner steps hold" in r.stdout
