@@ -303,22 +303,30 @@ def test_fp8_d128_multiblock_mask_vs_bruteforce(blocks):
     assert_lse(run, res, FP8)
 
 
-def test_fp8_d64_small_stream():
-    """FP8 KV at D = 64, T = 16 (the generic kernel): 20 steps of the tiny schedule with
-    bf16 inputs, every step's attention against the oracle, state and memory bit-exact."""
-    w = synth.workload("tiny_f32", kv_dtype=FP8, q_dtype=BF16, outliers=True)
+@pytest.mark.parametrize("D", [64, 128], ids=["d64", "d128"])
+def test_fp8_small_stream_memory_wraps(D):
+    """FP8 KV, 60 steps of the tiny schedule with bf16 inputs (23 groups into 10 memory
+    slots, so slots and their scales are overwritten twice): D = 64 on a 4x4 grid (the
+    generic kernels) and D = 128 on an 8x8 grid (the production compressor and attention
+    kernels); every step's attention against the oracle, state bit-exact every step and
+    memory every 10 steps."""
+    grid = dict(grid_h=4, grid_w=4) if D == 64 else dict(grid_h=8, grid_w=8, rope_mode=3,
+                                                        rope_split=(44, 42, 42))
+    w = synth.workload("tiny_f32", head_dim=D, kv_dtype=FP8, q_dtype=BF16, outliers=True, **grid)
     run = Runner(w)
     worst = 0.0
-    for s in range(20):
+    for s in range(60):
         res = run.step(2)
         err, dl = run.compare_attention(res)
         worst = max(worst, err)
         assert err <= ATTN_TOL[FP8], (s, err, dl)
         assert_lse(run, res, FP8)
         assert_state_matches(run)
-    assert_memory_bitexact(run)
+        if s % 10 == 9:
+            assert_memory_bitexact(run)
+    assert run.oc.bk.G > 2 * w["mem_slots"]
     assert_ring_bitexact(run)
-    say(f"fp8 d64 stream: worst rel L2 {worst:.3e}")
+    say(f"fp8 d{D} stream: worst rel L2 {worst:.3e}, {run.oc.bk.G} groups")
 
 
 @pytest.mark.parametrize("kv", [BF16, FP8], ids=["bf16", "fp8"])
