@@ -438,12 +438,14 @@ def test_s512_bf16_step_parity_other_seeds(seed):
     assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16]
 
 
+@pytest.mark.parametrize("ref", [0, 2], ids=["noref", "ref2"])
 @pytest.mark.parametrize("blocks", [[1, 2, 3], [3, 3], [6], [2, 1, 1, 2]])
-def test_bf16_d128_multiblock_mask_vs_bruteforce(blocks):
+def test_bf16_d128_multiblock_mask_vs_bruteforce(blocks, ref):
     """D = 128 bf16 kernel with several query blocks per call and T = 96 (tiles of 32 keys
-    and 256 query rows straddle frames and blocks): against the explicit mask matrix."""
+    and 256 query rows straddle frames and blocks), without and with a 2-frame reference
+    segment at the head of the history: against the explicit mask matrix."""
     w = synth.workload("s512_bf16", heads=4, grid_h=8, grid_w=12, window_frames=4,
-                       mem_slots=6, max_block_frames=6)
+                       mem_slots=6, max_block_frames=6, ref_frames=ref)
     run = Runner(w)
     for _ in range(9):
         run.step(2, attend=False)
