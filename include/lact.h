@@ -23,13 +23,17 @@
  * Compression runs once between blocks (walkthrough, "Streaming Pipeline").
  *
  * Conventions for every call below:
- *   - Tensor pointers are HIP device pointers owned by the caller, 16-byte aligned.
+ *   - Tensor pointers are HIP device pointers owned by the caller, 16-byte aligned, each
+ *     holding at least the extent its call states (the library cannot see buffer sizes and
+ *     reads or writes exactly those extents).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All device work is
  *     enqueued asynchronously on it; no call synchronises with the device and no call
  *     allocates device memory.
  *   - Every check runs before anything is enqueued. On error the call returns a non-OK
  *     status, the cache state is unchanged and lact_last_error() holds a message.
- *   - A cache handle is not thread-safe; separate handles are independent.
+ *   - A cache handle is not thread-safe; separate handles are independent.  Successive
+ *     calls on one handle depend on each other's device work (the staging, the ring and
+ *     the memory): issue them on one stream, or order the streams with events.
  *   - A handle holds one cache (lact_cache_init) or a set of n_members caches of one cfg
  *     (lact_set_init: one per layer and diffusion step) that advance together: they share
  *     the bookkeeping, the staging area and the RoPE table, and append and compress run for
