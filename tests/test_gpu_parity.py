@@ -270,6 +270,14 @@ def test_train_form_long_sequence():
     assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16]
 
 
+def test_fp8_s720_step_parity():
+    """FP8 KV cache on the 720x416 grid (T = 1170, not a multiple of 64: key tiles straddle
+    frames while V comes from the dequantised FP8 history), first block of 6 frames then 8,
+    8 heads: stored codes and scales bit-exact after the warm-up, step attention against
+    the oracle on sampled rows."""
+    _big_step_parity("s720_bf16", 11, 8, first_check=True, kv_dtype=FP8, heads=8, outliers=True)
+
+
 def test_fp8_append_compress_bitexact():
     """FP8 KV: ring codes and scales and the re-quantised memory slots bit-exact."""
     w = synth.workload("fp8_kv")
