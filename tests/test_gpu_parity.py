@@ -395,13 +395,15 @@ def test_binding_rejects_mismatched_tensors():
     assert {k: c.state()[k] for k in before} == before
 
 
-def test_bf16_d64_stream_t96():
-    """bf16 at D = 64 (served by the generic MFMA kernel at any T) on an 8x12 grid, T = 96:
-    64-key tiles straddle frames and 128-row query tiles end mid-frame; 30 steps with
-    multi-block calls every third step, every row against the oracle, state bit-exact,
-    memory overwritten (13 groups into 6 slots) and bit-exact."""
-    w = synth.workload("tiny_f32", heads=3, head_dim=64, grid_h=8, grid_w=12, kv_dtype=BF16,
-                       q_dtype=BF16, mem_slots=6, max_block_frames=4)
+@pytest.mark.parametrize("D, dt", [(64, BF16), (128, F32)], ids=["bf16_d64", "f32_d128"])
+def test_stream_t96(D, dt):
+    """bf16 at D = 64 (the generic MFMA kernel) and f32 at D = 128 (the f32 kernel) on an
+    8x12 grid, T = 96: key tiles straddle frames and query tiles end mid-frame; 30 steps
+    with multi-block calls every third step, every row against the oracle, state
+    bit-exact, memory overwritten (13 groups into 6 slots) and bit-exact."""
+    rope = {} if D == 64 else dict(rope_mode=3, rope_split=(44, 42, 42))
+    w = synth.workload("tiny_f32", heads=3, head_dim=D, grid_h=8, grid_w=12, kv_dtype=dt,
+                       q_dtype=dt, mem_slots=6, max_block_frames=4, **rope)
     run = Runner(w)
     worst = 0.0
     for s in range(30):
@@ -409,12 +411,12 @@ def test_bf16_d64_stream_t96():
         res = run.step(2, blocks=blocks, form=0 if blocks else 1)
         err, dl = run.compare_attention(res)
         worst = max(worst, err)
-        assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16], (s, err, dl)
+        assert err <= ATTN_TOL[dt] and dl <= LSE_TOL[dt], (s, err, dl)
         assert_state_matches(run)
     assert run.oc.bk.G > w["mem_slots"]
     assert_memory_bitexact(run)
     assert_ring_bitexact(run)
-    say(f"bf16 d64 T=96 stream: worst rel L2 {worst:.3e}")
+    say(f"D={D} T=96 stream: worst rel L2 {worst:.3e}")
 
 
 def test_f32_d128_small_stream():
