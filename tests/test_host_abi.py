@@ -382,3 +382,17 @@ def test_c_client_against_the_header():
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "1000 planner steps hold" in r.stdout
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for several (flag or a launcher's WORLD_SIZE) it
+    exits non-zero with a message before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    bench = os.path.join(root, "bench.py")
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, bench] + args, capture_output=True, text=True,
+                           timeout=120, env=dict(os.environ, **env))
+        assert r.returncode == 2, (args, env, r.stderr)
+        assert "one GPU" in r.stderr and r.stdout == ""
