@@ -396,3 +396,13 @@ def test_bench_refuses_more_than_one_gpu():
                            timeout=120, env=dict(os.environ, **env))
         assert r.returncode == 2, (args, env, r.stderr)
         assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without liblact.so every entry of the binding raises (there is no CPU path)."""
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", os.path.join(os.path.dirname(L.LIB_PATH), "absent.so"))
+    cfg = _cfg("tiny_f32")
+    for call in (L.lib, lambda: L.lact_cache_footprint(cfg), lambda: L.Plan(cfg)):
+        with pytest.raises(RuntimeError, match="missing"):
+            call()
