@@ -22,6 +22,7 @@ LACT_MAX_KEY_FRAMES = 256
 LACT_MAX_Q_BLOCKS = 16
 LACT_MAX_MEMBERS = 1024
 LACT_MAX_TOKENS = 262144
+LACT_STATIC_QUEUE_MAX = 16384
 SEG_MEMORY, SEG_WINDOW, SEG_CURRENT, SEG_REF = 0, 1, 2, 3
 STATUS = {0: "LACT_OK", 1: "LACT_E_INVALID", 2: "LACT_E_SHAPE", 3: "LACT_E_CAPACITY",
           4: "LACT_E_DTYPE", 5: "LACT_E_STATE", 6: "LACT_E_HIP"}
@@ -79,7 +80,7 @@ EXPORTS = ["lact_cache_footprint", "lact_cache_layout", "lact_cache_init", "lact
            "lact_set_footprint", "lact_set_layout", "lact_set_init",
            "lact_ref_set", "lact_rope_reset_apply", "lact_block_attention",
            "lact_member_ref_set", "lact_member_rope_reset_apply", "lact_member_block_attention",
-           "lact_kv_ring_append",
+           "lact_member_block_attention_static", "lact_kv_ring_append",
            "lact_convkv_compress", "lact_cache_state", "lact_cache_keys", "lact_plan_create",
            "lact_plan_destroy", "lact_plan_append", "lact_plan_compress", "lact_plan_state",
            "lact_plan_keys", "lact_last_error"]
@@ -111,6 +112,7 @@ def lib():
         "lact_member_ref_set": [vp, i32, vp, vp, i32, vp],
         "lact_member_rope_reset_apply": [vp, i32, vp, vp, vp, i32, vp],
         "lact_member_block_attention": [vp, i32, P(i32), i32, vp, vp, vp],
+        "lact_member_block_attention_static": [vp, i32, P(i32), i32, vp, vp, vp],
         "lact_kv_ring_append": [vp, vp, vp, i32, vp],
         "lact_convkv_compress": [vp, vp, vp, vp, vp, vp, P(i32)],
         "lact_cache_state": [vp, P(lact_state)],
@@ -271,6 +273,15 @@ def lact_member_block_attention(h, member, q_block_frames, out, lse=None, stream
                                              _stream(stream)))
 
 
+def lact_member_block_attention_static(h, member, q_block_frames, out, lse=None, stream=None):
+    """lact_member_block_attention with the exact pass's work queue in the library's static
+    device array (no workspace of the cache buffer is used)."""
+    arr, n = _blocks(q_block_frames)
+    lse_p = _ptr(lse, torch.float32, "lse") if lse is not None else None
+    _check(lib().lact_member_block_attention_static(h, member, arr, n, _ptr(out, name="out"),
+                                                    lse_p, _stream(stream)))
+
+
 def lact_member_ref_set(h, member, k_ref, v_ref, n_frames, stream=None):
     _check(lib().lact_member_ref_set(h, member, _ptr(k_ref, name="k_ref"),
                                      _ptr(v_ref, name="v_ref"), n_frames, _stream(stream)))
@@ -408,6 +419,19 @@ class Cache:
             lact_block_attention(self.h, q_block_frames, out, lse, stream)
         else:
             lact_member_block_attention(self.h, member, q_block_frames, out, lse, stream)
+        return out
+
+    def block_attention_static(self, q_block_frames=None, out=None, lse=None, stream=None,
+                               member=0):
+        """block_attention through lact_member_block_attention_static."""
+        st = self.state()
+        Lq = st["staged_frames"] * self.T
+        if out is None:
+            out = torch.empty((Lq, self.H, self.D), dtype=self.io_dtype, device=self.buf.device)
+        self._io(out, Lq, "out")
+        if lse is not None:
+            _expect(lse, (self.H, Lq), torch.float32, self.buf.device, "lse")
+        lact_member_block_attention_static(self.h, member, q_block_frames, out, lse, stream)
         return out
 
     def ref_set(self, k_ref, v_ref, stream=None, member=0):

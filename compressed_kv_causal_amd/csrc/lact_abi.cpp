@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -355,8 +356,57 @@ lact_status lact_rope_reset_apply(lact_cache* c, const void* q, const void* k_cu
   return lact_member_rope_reset_apply(c, 0, q, k_cur, v_cur, n_frames, stream);
 }
 
-lact_status lact_member_block_attention(lact_cache* c, int32_t member, const int32_t* q_block_frames,
-                                        int32_t n_q_blocks, void* out, float* lse, void* stream) {
+}  // extern "C"
+
+// ---- the exact pass's work queue in a library-held array ---------------------------------
+// For lact_member_block_attention_static: one int32 per (head, 256-row query tile), in a
+// file-scope device array instead of the cache buffer's attn_flags region.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device, with that device current, and kept.
+static __device__ __align__(256) int32_t scratch[LACT_STATIC_QUEUE_MAX];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream` (the current device for
+// the null stream).
+lact_status scratch_address(hipStream_t stream, int32_t** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LACT_E_CAPACITY, "device index " + std::to_string(dev) + " outside 0.." +
+                                     std::to_string(kMaxDevices - 1));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return LACT_OK;
+}
+}  // namespace
+
+// Block attention of `member`; `static_queue` takes the exact pass's work queue from
+// `scratch` instead of the cache buffer.
+static lact_status block_attention_impl(lact_cache* c, int32_t member, const int32_t* q_block_frames,
+                                        int32_t n_q_blocks, void* out, float* lse, void* stream,
+                                        bool static_queue) {
   if (!c) return fail(LACT_E_INVALID, "cache is NULL");
   if (member < 0 || member >= c->members())
     return fail(LACT_E_INVALID, "member " + std::to_string(member) + " outside 0.." +
@@ -394,7 +444,17 @@ lact_status lact_member_block_attention(lact_cache* c, int32_t member, const int
   a.v_cur = c->at(c->lay.vcur);
   a.out = out;
   a.lse = lse;
-  a.flags = reinterpret_cast<int32_t*>(c->at(c->lay.attn_flags));
+  if (static_queue) {
+    const int64_t items = (int64_t)g.heads * ((c->staged_frames * (int64_t)T + 255) / 256);
+    if (items > LACT_STATIC_QUEUE_MAX)
+      return fail(LACT_E_CAPACITY, "heads x 256-row query tiles = " + std::to_string(items) +
+                                       " exceeds LACT_STATIC_QUEUE_MAX (" +
+                                       std::to_string(LACT_STATIC_QUEUE_MAX) + ")");
+    lact_status st = scratch_address(static_cast<hipStream_t>(stream), &a.flags);
+    if (st != LACT_OK) return st;
+  } else {
+    a.flags = reinterpret_cast<int32_t*>(c->at(c->lay.attn_flags));
+  }
   a.q_head_stride = (int64_t)g.max_block_frames * T * g.head_dim;
   a.k_head_stride = (int64_t)c->lay.key_frames_max * T * g.head_dim;
   a.hist = c->hist();
@@ -423,6 +483,19 @@ lact_status lact_member_block_attention(lact_cache* c, int32_t member, const int
   hipError_t e = lact::launch_attention(a, g.q_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return LACT_OK;
+}
+
+extern "C" {
+
+lact_status lact_member_block_attention(lact_cache* c, int32_t member, const int32_t* q_block_frames,
+                                        int32_t n_q_blocks, void* out, float* lse, void* stream) {
+  return block_attention_impl(c, member, q_block_frames, n_q_blocks, out, lse, stream, false);
+}
+
+lact_status lact_member_block_attention_static(lact_cache* c, int32_t member,
+                                               const int32_t* q_block_frames, int32_t n_q_blocks,
+                                               void* out, float* lse, void* stream) {
+  return block_attention_impl(c, member, q_block_frames, n_q_blocks, out, lse, stream, true);
 }
 
 lact_status lact_block_attention(lact_cache* c, const int32_t* q_block_frames, int32_t n_q_blocks,

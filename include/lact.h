@@ -279,6 +279,23 @@ lact_status lact_convkv_compress(lact_cache* cache, const float* w_k, const floa
                                  const float* w_v, const float* b_v, void* stream,
                                  int32_t* slots_written);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation) and so cannot rely on any workspace
+ * beyond the buffers they pass: lact_member_block_attention with the exact pass's work
+ * queue (one int32 per (head, 256-row query tile)) held by the library in a static device
+ * array of LACT_STATIC_QUEUE_MAX entries (64 KiB; each GPU the library runs on holds its
+ * own copy until the process ends) instead of the cache buffer's attn_flags region.
+ * Same arguments, checks, kernels and results as lact_member_block_attention.  It calls
+ * no allocator; its first call on a device looks the array's address up (a host-side
+ * runtime query, nothing is enqueued).  LACT_E_CAPACITY if heads * ceil(staged frames *
+ * T / 256) > LACT_STATIC_QUEUE_MAX.  Every call on one GPU shares that GPU's array, and
+ * each launch writes every entry it reads before reading it: calls that overlap on one GPU
+ * (streams not ordered with each other) race on the array and must not be issued. */
+#define LACT_STATIC_QUEUE_MAX 16384
+lact_status lact_member_block_attention_static(lact_cache* cache, int32_t member,
+                                               const int32_t* q_block_frames, int32_t n_q_blocks,
+                                               void* out, float* lse, void* stream);
+
 /* ---- inspection ------------------------------------------------------------------------ */
 
 lact_status lact_cache_state(const lact_cache* cache, lact_state* out);
