@@ -59,8 +59,8 @@ _PERSISTENT = ("ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v", "ring_k_s
                "ring_v_scale", "mem_k_scale", "mem_v_scale", "ref_k_scale", "ref_v_scale")
 
 _LAYOUT_FIELDS = ["total", "ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v", "krot", "qrot",
-                  "vcur", "vhist", "ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale",
-                  "ref_k_scale", "ref_v_scale", "rope_table", "attn_flags", "frame_bytes"]
+                  "vcur", "vcur_scale", "vscale", "ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale",
+                  "ref_k_scale", "ref_v_scale", "rope_table", "attn_flags", "vmax", "frame_bytes"]
 
 
 class lact_layout(ctypes.Structure):

@@ -8,11 +8,12 @@
 //
 // Kernels:
 //   k_attn_bf16_d128  the D = 128 production kernel (described at its definition).
-//   k_attn_bf16<D>    exact online-softmax flash attention on v_mfma_f32_32x32x16_bf16,
+//   k_attn_bf16<D, F8V>  exact online-softmax flash attention on v_mfma_f32_32x32x16_bf16,
 //                     4 waves x 32 query rows, 64-key tiles staged in LDS (K row-major, V
-//                     transposed by the staging threads), running max with rescaling: the
-//                     kernel for D = 64 and T < 64, and the exact fallback of the D = 128
-//                     kernel for the query tiles it flags.
+//                     transposed by the staging threads, an FP8 cache's V codes widened to
+//                     bf16 there), running max with rescaling: the kernel for D = 64 and
+//                     T < 64, and the exact fallback of the D = 128 kernel for the query
+//                     tiles it flags.
 //   k_attn_f32<D>     plain f32 FMA kernel (one lane per query row) for the f32 cache.
 //
 // bf16 kernel orientation: S^T = K Q^T (K is the MFMA A operand, Q the B operand), so a
@@ -70,7 +71,24 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-template <int D>
+// 8 channels of V row (key j, head h) starting at channel d0, as bf16: from bf16 storage,
+// or (F8V) e4m3 codes times the key's row scale, rounded to bf16.
+template <bool F8V>
+__device__ __forceinline__ uint4 v_chunk_bf16(const AttnArgs& a, int32_t j, int32_t h, int d0) {
+  int32_t which;
+  const int64_t off = v_row_off(a, j, h, &which) + d0;
+  if (!F8V) return *reinterpret_cast<const uint4*>(v_base<uint16_t>(a, which) + off);
+  float x[8];
+  load8_fp8(v_base<uint8_t>(a, which) + off, a.vscale[h * a.vs_head_stride + j], x);
+  uint4 r;
+  r.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+  r.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+  r.z = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
+  r.w = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
+  return r;
+}
+
+template <int D, bool F8V>
 __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KSTR = D + 8;   // LDS row stride of K (bf16); +16 B keeps ds_read_b128 conflict-free
@@ -122,11 +140,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
       for (int t = 0; t < 4; ++t) {
         const int j = k0 + quad * 4 + t;
         vv[t] = make_uint4(0, 0, 0, 0);
-        if (j < a.Lk) {
-          int32_t which;
-          const int64_t off = v_row_off(a, j, h, &which);
-          vv[t] = *reinterpret_cast<const uint4*>(v_base<uint16_t>(a, which) + off + dchunk * 8);
-        }
+        if (j < a.Lk) vv[t] = v_chunk_bf16<F8V>(a, j, h, dchunk * 8);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -264,10 +278,28 @@ constexpr int D = 128, BM = 256, BN = 64, NS = 4, WAVES = 8;
 constexpr int ROW_BYTES = D * 2;
 constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
 constexpr int V_RING = NS * TILE_BYTES;     // V slots follow the K slots in LDS
-constexpr int VMEM_PER_TILE = 4;            // copy instructions per wave per tile (K 2, V 2)
+constexpr int VMEM_PER_TILE = 4;            // copy instructions per wave per tile:
+                                            // K 2, V 2 (bf16) or K 2, V 1, V scales 1 (FP8)
+// FP8 cache: V tiles of e4m3 rows (128 B), then per tile the keys' 1/s_v and log2(s_v)
+// pairs, in groups of 8 keys: [8 x 1/s_v | 8 x (hi, lo)] = 64 B per group
+constexpr int V8_ROW = D;
+constexpr int V8_TILE = BN * V8_ROW;        // 8 KiB
+constexpr int S_RING = V_RING + NS * V8_TILE;
+constexpr int S_TILE = BN * 8;
+constexpr int LDS_BF16 = 2 * NS * TILE_BYTES;
+constexpr int LDS_F8 = S_RING + NS * S_TILE;
+// FP8 probabilities: P~ = 2^(s + log2 s_v - m_ref) = P' s_v, P' = 2^(s - m_ref) the
+// probability, with m_ref = (the first tile's largest s + log2 s_v) - KSHIFT, so that
+// P~ <= 2^KSHIFT there; later tiles keep P~ < 448 through the raise (a lane's sum of P'
+// below 448 * 2^-E_h, 2^E_h the power of two above the head's largest s_v)
+constexpr int KSHIFT = 3;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
@@ -279,6 +311,10 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 __device__ __forceinline__ void copy_to_lds(const void* src, unsigned m0) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
+// The same with 4 B per lane (lane l lands at m0 + 4 l).
+__device__ __forceinline__ void copy_dword_to_lds(const void* src, unsigned m0) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
 
 // The scalars the copies need, as plain values (the kernel's argument block stays in the
 // constant kernarg segment: taking a field by a computed offset would make the compiler
@@ -288,7 +324,7 @@ struct Geo {
   const char* v_ring;
   const char* v_cur;
   const char* v_ref;
-  int64_t frame_bytes;  // one V frame, T * H * D * 2
+  int64_t frame_bytes;  // one V frame, T * H * (bytes of a V row)
   int T, Lk, nf, ref_len, mem_end, nh, M, R, mem_slot0, ring_slot0;
 };
 
@@ -314,7 +350,7 @@ struct Ctx {
   char* lds;
   unsigned lds_u32;   // LDS address of the ring (for M0)
   int h, wave, lane, hi, lr, kvis;
-  int64_t hrow;       // bytes between consecutive tokens of one V frame (H * D * 2)
+  int64_t hrow;       // bytes between consecutive tokens of one V frame (H * V row bytes)
   // copies: the two 4-row groups of a tile this lane copies
   int crow[2];        // row inside the tile
   int koff[2];        // crow * 256 + chunk * 16 (bytes from the tile's first K row)
@@ -322,6 +358,18 @@ struct Ctx {
   // fragment reads: LDS byte offsets from the ring base (slot 0)
   int kread[8];       // K fragment kk of key block 0 (+ 8 KiB for block 1)
   int vread[4][2];    // the two transposed reads of V^T fragment db, chunk 0 (+ 4 KiB per chunk)
+  // FP8 V: the one 8-row group of a tile this lane copies, its V^T fragment reads and the
+  // V scale terms of its keys
+  int vrow8;          // row inside the tile
+  int voff8;          // (vrow8 * H + h) * 128 + chunk * 16
+  int vread8[4];      // first of the four 8-key transposed reads of V^T fragment db
+  int sread;          // 1/s_v of the lane's probabilities' keys (S_RING + hi * 64)
+  int lread[2];       // log2(s_v) pair of the A-operand key row of key block kb
+  const char* vsbase; // the copy source of this lane: 1/s_v (lanes 0-7) or log2 pairs
+                      // (lanes 8-15) of this head, attention order
+  float thr;          // raise threshold 448 * 2^-E_h on a lane's 32-key sum of P'
+  int thr_exp;        // frexp exponent of thr
+  bf16x8_t augb;      // B operand of the log2(s_v) step
 };
 
 // Scalar stream state of the copies: frame and token of the first key of the next tile,
@@ -332,12 +380,15 @@ struct Stream {
   const char* baseB;
 };
 
-// Copy tile t's 64 key rows of K and V into ring slot t % NS, then advance the stream.
+// Copy tile t's 64 key rows of K and V (and, FP8, their V scales) into ring slot t % NS,
+// then advance the stream.
+template <bool F8>
 __device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
   const Geo& a = c.g;
   const unsigned slot = (unsigned)(t % NS);
   const unsigned kdst = c.lds_u32 + slot * TILE_BYTES + (unsigned)c.wave * 8 * ROW_BYTES;
-  const unsigned vdst = kdst + V_RING;
+  const unsigned vdst = F8 ? c.lds_u32 + V_RING + slot * V8_TILE + (unsigned)c.wave * 8 * V8_ROW
+                           : kdst + V_RING;
   if ((t + 1) * BN <= a.Lk) {
     const char* ktile = c.kbase + (int64_t)t * TILE_BYTES;
 #pragma unroll
@@ -351,7 +402,22 @@ __device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
     }
   }
   const char* vA = st.baseA + st.u0 * c.hrow;
-  if (st.u0 + BN <= a.T) {  // the whole tile lies in frame f0
+  if (F8) {
+    if (st.u0 + BN <= a.T) {
+      copy_to_lds(vA + c.voff8, vdst);
+    } else {
+      const char* vB = st.baseB + (st.u0 - a.T) * c.hrow;
+      copy_to_lds((st.u0 + c.vrow8 >= a.T ? vB : vA) + c.voff8, vdst);
+    }
+    // scale terms of keys 8 wave .. 8 wave + 7 of the tile: lanes 0-7 1/s_v, lanes 8-15
+    // the log2 pairs (keys past the end repeat the last one)
+    if (c.lane < 16) {
+      int key = t * BN + c.wave * 8 + (c.lane & 7);
+      key = key < a.Lk ? key : a.Lk - 1;
+      copy_dword_to_lds(c.vsbase + (int64_t)key * 4,
+                        c.lds_u32 + S_RING + slot * S_TILE + (unsigned)c.wave * 64);
+    }
+  } else if (st.u0 + BN <= a.T) {  // the whole tile lies in frame f0
 #pragma unroll
     for (int i = 0; i < 2; ++i) copy_to_lds(vA + c.voff[i], vdst + i * 4 * ROW_BYTES);
   } else {
@@ -393,7 +459,7 @@ __device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0)
 // `init` (the broadcast -m_ref of the lane's row: the chains then produce the exponents
 // of the probabilities directly).  The two key blocks are independent MFMA chains,
 // interleaved; K fragments are read three steps ahead of their MFMAs.
-template <bool MASK, int SLOT>
+template <bool F8, bool MASK, int SLOT>
 __device__ __forceinline__ void qk_tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], const f32x16_t& init,
                                         f32x16_t (&s)[2]) {
   const char* kb = c.lds + slot_of<SLOT>(j) * TILE_BYTES;
@@ -420,6 +486,19 @@ __device__ __forceinline__ void qk_tile(const Ctx& c, int j, const bf16x8_t (&qf
     s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % (AHEAD + 1)][1], qf[kk], s[1], 0, 0, 0);
     step_fence();
   }
+  if (F8) {
+    // one more 16-channel step adds log2(s_v) of each key row: A = (hi, lo, 0, ...) of the
+    // row's key, B = (1, 1, 0, ...) in the lanes of channels 0..7 and 0 in the others
+    // (the constant c.augb)
+    const char* sb = c.lds + slot_of<SLOT>(j) * S_TILE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t pair = *reinterpret_cast<const uint32_t*>(sb + c.lread[kb]);
+      const u32x4_t w = {pair, 0u, 0u, 0u};
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), c.augb, s[kb],
+                                                      0, 0, 0);
+    }
+  }
   mask_block<MASK>(s[0], j * BN, c.hi, c.kvis);
   mask_block<MASK>(s[1], j * BN + 32, c.hi, c.kvis);
 }
@@ -432,6 +511,44 @@ __device__ __forceinline__ bf16x8_t vfrag(const char* vb, const Ctx& c, int ch, 
   __builtin_memcpy(&vf, &lo, 8);
   __builtin_memcpy(reinterpret_cast<char*>(&vf) + 8, &up, 8);
   return vf;
+}
+
+// FP8: P~ = exp2(s - sub) in place; returns this lane's sum of P' = P~ / s_v over its 32
+// keys (the probabilities themselves, for l), in four partial sums.
+template <bool SUB>
+__device__ __forceinline__ float exp_tile_f8(f32x16_t (&s)[2], float sub, const char* sb, const Ctx& c) {
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    const float4 i0 = *reinterpret_cast<const float4*>(sb + c.sread + ch * 128);
+    const float4 i1 = *reinterpret_cast<const float4*>(sb + c.sread + ch * 128 + 16);
+    const float inv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+    const int kb = ch >> 1, b0 = 8 * (ch & 1);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float e = __builtin_amdgcn_exp2f(SUB ? s[kb][b0 + t] - sub : s[kb][b0 + t]);
+      s[kb][b0 + t] = e;
+      part[t & 3] = __builtin_fmaf(e, inv[t], part[t & 3]);
+    }
+  }
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// V^T fragment of FP8 V (channels 32 db .. 32 db + 31, the 32 keys of this lane's half):
+// four transposing 8-bit reads of 8 keys each.  Within each 16-lane group, lanes 2r and
+// 2r + 1 address the two 8-byte halves of key row r's 16-channel chunk, and lane i
+// receives channel i of the 8 rows, i.e. 8 consecutive keys of its channel.  Byte b of
+// the fragment is key 16 (b / 8) + 8 half + (b mod 8) -- the key order of the lane's
+// probabilities, so A and B pair up in the fp8 MFMA.
+__device__ __forceinline__ v8i32 vfrag8(const char* vb, const Ctx& c, int db) {
+  v8i32 f;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const v2i32 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(vb + c.vread8[db] + cc * 16 * V8_ROW));
+    f[2 * cc] = x[0];
+    f[2 * cc + 1] = x[1];
+  }
+  return f;
 }
 
 // p = exp2(s - sub) in place (sub = 0 when s already holds the exponents); returns this
@@ -455,39 +572,108 @@ __device__ __forceinline__ float exp_tile(f32x16_t (&s)[2], float sub) {
 // landed (the copies of tiles j + 2 .. j + NS - 1 stay in flight) and sync.  Tiles past
 // the end are copied too (clamped rows, harmless), so the wait count is a constant.
 //
-// Reference raise: a lane sum of 2^64 or more means a row met scores far above its
-// reference.  The wave then takes each such row's largest probability of the tile, 2^e *
-// [1, 2), and divides that row's probabilities, O and l by 2^e (exact power-of-two scaling)
-// while m_ref moves up by e.  Ordinary data never takes this branch; scores with large
-// outliers take it a few times per row at most.  A probability that is already infinite
-// (a score >= 128 above the reference) cannot be rescaled: l and O become infinite and the
-// workgroup hands its rows to the exact pass.
-template <bool MASK, bool FIRST, int SLOT>
+// O^T += V^T P^T on bf16 V: 16 MFMAs (chunk ch, channel block db) in 4 independent chains,
+// V^T fragments read four MFMAs (128 cycles) ahead
+__device__ __forceinline__ void pv_tile_bf16(const Ctx& c, const char* vb, const f32x16_t (&s)[2],
+                                             f32x16_t (&o)[4]) {
+  bf16x8_t p[4];
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) p[ch][t] = (__bf16)s[ch >> 1][8 * (ch & 1) + t];
+  constexpr int VAHEAD = 4;
+  bf16x8_t vf[VAHEAD + 1];
+#pragma unroll
+  for (int i = 0; i < VAHEAD; ++i) vf[i] = vfrag(vb, c, i >> 2, i & 3);
+  step_fence();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + VAHEAD < 16) vf[(i + VAHEAD) % (VAHEAD + 1)] = vfrag(vb, c, (i + VAHEAD) >> 2, (i + VAHEAD) & 3);
+    o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (VAHEAD + 1)], p[i >> 2], o[i & 3], 0, 0, 0);
+    step_fence();
+  }
+}
+
+// O^T += V^T P~^T on FP8 V: P~ = P' * s_v (P' the probability, s_v the key's V row scale)
+// rounded to e4m3 (the raise keeps it <= 448), against the stored e4m3 codes: 4 MFMAs of
+// 32 channels x 64 keys on v_mfma_f32_32x32x64_f8f6f4 (unit block scales).  The lane's 32
+// values are keys 16 ch + 8 hi + t (ch < 4, t < 8), the B operand's byte 8 ch + t.
+__device__ __forceinline__ void pv_tile_f8(const Ctx& c, const char* vb, const f32x16_t (&s)[2],
+                                           f32x16_t (&o)[4]) {
+  v8i32 vf[2];
+  vf[0] = vfrag8(vb, c, 0);
+  vf[1] = vfrag8(vb, c, 1);
+  v8i32 pt;
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    const f32x16_t& sk = s[ch >> 1];
+    const int b0 = 8 * (ch & 1);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 0], sk[b0 + 1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 2], sk[b0 + 3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 4], sk[b0 + 5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 6], sk[b0 + 7], w1, true);
+    pt[2 * ch] = w0;
+    pt[2 * ch + 1] = w1;
+  }
+  step_fence();
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    if (db + 2 < 4) {
+      const v8i32 nx = vfrag8(vb, c, db + 2);
+      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db & 1], pt, o[db], 0, 0, 0, 0, 0, 0);
+      vf[db & 1] = nx;
+    } else {
+      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db & 1], pt, o[db], 0, 0, 0, 0, 0, 0);
+    }
+    step_fence();
+  }
+}
+
+// Reference raise: a lane sum of 2^64 (bf16 V) or of 448 * 2^-E_h (FP8 V, where P' * s_v
+// must stay a finite e4m3 value) or more means a row met scores far above its reference.
+// The wave then finds for each such row a power of two 2^e -- bf16: the tile's largest
+// probability is 2^e * [1, 2); FP8: the one that brings the row's larger 32-key sum back
+// under the threshold -- and divides that row's probabilities, O and l by 2^e (exact
+// power-of-two scaling) while m_ref moves up by e.  Ordinary data never takes this branch
+// on bf16 and rarely on FP8; scores with large outliers take it a few times per row at
+// most.  A probability that is already infinite (a score >= 128 above the reference)
+// cannot be rescaled: l and O become infinite and the workgroup hands its rows to the
+// exact pass.
+template <bool F8, bool MASK, bool FIRST, int SLOT>
 __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&o)[4],
                                      float& m_ref, f32x16_t& negm, float& l_part, Stream& st) {
-  const char* vb = c.lds + slot_of<SLOT>(j) * TILE_BYTES;  // + vread (which holds V_RING)
-  issue(c, j + NS - 1, st);
+  // K slot base; V^T reads add vread / vread8 (which hold V_RING) to their slot's base
+  const char* vb = c.lds + slot_of<SLOT>(j) * (F8 ? V8_TILE : TILE_BYTES);
+  issue<F8>(c, j + NS - 1, st);
   f32x16_t s[2];
-  qk_tile<MASK, SLOT>(c, j, qf, negm, s);  // tile 0: negm = 0
+  qk_tile<F8, MASK, SLOT>(c, j, qf, negm, s);  // tile 0: negm = 0
+  const char* sb = c.lds + slot_of<SLOT>(j) * S_TILE;  // FP8 scale terms (+ sread)
   float sum;
   if (FIRST) {
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
     m_ref = fmaxf(mx, __shfl_xor(mx, 32));
+    if (F8) m_ref -= (float)KSHIFT;  // P~ <= 2^KSHIFT on this tile
 #pragma unroll
     for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
-    sum = exp_tile<true>(s, m_ref);
+    sum = F8 ? exp_tile_f8<true>(s, m_ref, sb, c) : exp_tile<true>(s, m_ref);
   } else {
-    sum = exp_tile<false>(s, 0.0f);
+    sum = F8 ? exp_tile_f8<false>(s, 0.0f, sb, c) : exp_tile<false>(s, 0.0f);
   }
-  if (!FIRST && __builtin_expect(__any(!(sum < 0x1p64f)), 0)) {
-    float mx = fmaxf(s[0][0], s[1][0]);
+  if (!FIRST && __builtin_expect(__any(!(sum < (F8 ? c.thr : 0x1p64f))), 0)) {
+    int e;
+    if (F8) {
+      const float smax = fmaxf(sum, __shfl_xor(sum, 32));
+      e = (smax >= c.thr && smax < INFINITY) ? __builtin_amdgcn_frexp_expf(smax) - c.thr_exp + 1 : 0;
+    } else {
+      float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // e = floor(log2(mx)) for a finite mx >= 2, else 0
-    const int e = (mx >= 2.0f && mx < INFINITY) ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // e = floor(log2(mx)) for a finite mx >= 2, else 0
+      e = (mx >= 2.0f && mx < INFINITY) ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;
+    }
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -503,23 +689,10 @@ __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8
     for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
   }
   l_part += sum;
-  bf16x8_t p[4];
-#pragma unroll
-  for (int ch = 0; ch < 4; ++ch)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) p[ch][t] = (__bf16)s[ch >> 1][8 * (ch & 1) + t];
-  // O^T += V^T P^T: 16 MFMAs (chunk ch, channel block db) in 4 independent chains, V^T
-  // fragments read four MFMAs (128 cycles) ahead
-  constexpr int VAHEAD = 4;
-  bf16x8_t vf[VAHEAD + 1];
-#pragma unroll
-  for (int i = 0; i < VAHEAD; ++i) vf[i] = vfrag(vb, c, i >> 2, i & 3);
-  step_fence();
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i + VAHEAD < 16) vf[(i + VAHEAD) % (VAHEAD + 1)] = vfrag(vb, c, (i + VAHEAD) >> 2, (i + VAHEAD) & 3);
-    o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (VAHEAD + 1)], p[i >> 2], o[i & 3], 0, 0, 0);
-    step_fence();
+  if (F8) {
+    pv_tile_f8(c, vb, s, o);
+  } else {
+    pv_tile_bf16(c, vb, s, o);
   }
   static_assert((NS - 2) * VMEM_PER_TILE == 8, "the wait count below assumes 4 stages");
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
@@ -528,9 +701,11 @@ __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8
 
 }  // namespace d128
 
+template <bool F8>
 __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   using namespace d128;
-  __shared__ __align__(1024) char lds[2 * NS * TILE_BYTES];
+  __shared__ __align__(1024) char lds[F8 ? LDS_F8 : LDS_BF16];
+  constexpr int VROW = F8 ? V8_ROW : ROW_BYTES;  // bytes of one stored V row
 
   // XCD-aware mapping: workgroup id b runs on XCD b % 8; give each XCD a contiguous range
   // of (head, query tile) items so one head's tiles run on one XCD together.
@@ -547,7 +722,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   c.g.v_ring = static_cast<const char*>(a.v_ring);
   c.g.v_cur = static_cast<const char*>(a.v_cur);
   c.g.v_ref = static_cast<const char*>(a.v_ref);
-  c.g.frame_bytes = (int64_t)a.T * a.H * ROW_BYTES;
+  c.g.frame_bytes = (int64_t)a.T * a.H * VROW;
   c.g.T = a.T;
   c.g.Lk = a.Lk;
   c.g.nf = a.Lk / a.T;
@@ -566,7 +741,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   c.lds = lds;
   c.lds_u32 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   c.kbase = static_cast<const char*>(a.k) + (int64_t)h * a.k_head_stride * 2;
-  c.hrow = (int64_t)a.H * ROW_BYTES;
+  c.hrow = (int64_t)a.H * VROW;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = c.wave * 8 + i * 4 + (c.lane >> 4);
@@ -588,6 +763,38 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
       c.vread[db][0] = V_RING + row * ROW_BYTES + ((chunk ^ swz(row)) * 16) + half;
       c.vread[db][1] = V_RING + (row + 4) * ROW_BYTES + ((chunk ^ swz(row + 4)) * 16) + half;
     }
+  }
+  if (F8) {
+    // copies: lane l moves 16 B of key row 8 wave + l / 8; its LDS position l mod 8 holds
+    // the row's chunk (l mod 8) ^ (row mod 8), so the transposed reads below (8 consecutive
+    // rows, one chunk) hit 8 different 16-byte positions
+    c.vrow8 = c.wave * 8 + (c.lane >> 3);
+    const int chunk = (c.lane & 7) ^ (c.vrow8 & 7);
+    c.voff8 = (c.vrow8 * a.H + h) * V8_ROW + chunk * 16;
+    // V^T reads: 16-lane group g covers channels 16 (g mod 2) of the 32-channel block and
+    // keys 8 (g / 2) of each 16-key chunk; lane i addresses row i / 2, byte half i mod 2
+    const int g = c.lane >> 4, i = c.lane & 15;
+    const int vr = (g >> 1) * 8 + (i >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      c.vread8[db] = V_RING + vr * V8_ROW + (((2 * db + (g & 1)) ^ (vr & 7)) * 16) + (i & 1) * 8;
+    c.sread = S_RING + c.hi * 64;
+    const int m = perm32(c.lr);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = kb * 32 + m;
+      c.lread[kb] = S_RING + (key >> 3) * 64 + 32 + (key & 7) * 4;
+    }
+    c.vsbase = reinterpret_cast<const char*>(a.vscale + (c.lane < 8 ? 1 : 2) * a.vs_plane +
+                                             (int64_t)h * a.vs_head_stride);
+    float smax = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kVmaxParts; ++p) smax = fmaxf(smax, a.vmax[h * kVmaxParts + p]);
+    const int eh = (smax > 0.0f && smax < INFINITY) ? __builtin_amdgcn_frexp_expf(smax) : 0;
+    c.thr = __builtin_ldexpf(448.0f, -eh);
+    c.thr_exp = __builtin_amdgcn_frexp_expf(c.thr);
+    const u32x4_t ones = {c.hi ? 0u : 0x3F803F80u, 0u, 0u, 0u};  // bf16 (1, 1, 0, ...)
+    c.augb = __builtin_bit_cast(bf16x8_t, ones);
   }
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.q_head_stride;
   const int q0 = qt * BM;
@@ -612,25 +819,25 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   float m_ref = 0.0f, l_part = 0.0f;
   f32x16_t negm = f32x16_t{};  // -m_ref in every element (the QK^T chains' starting value)
   Stream st{0, 0, frame_base(c.g, 0), frame_base(c.g, 1)};
-  for (int t = 0; t < NS - 1; ++t) issue(c, t, st);
+  for (int t = 0; t < NS - 1; ++t) issue<F8>(c, t, st);
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile 0 landed
   __syncthreads();
 
   if (n_free > 0)
-    tile<false, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st);
+    tile<F8, false, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st);
   else
-    tile<true, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st);
+    tile<F8, true, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st);
   int j = 1;
   const int free_end = n_free < nt ? n_free : nt;
   static_assert(NS == 4, "the unrolled loop below walks the slots 1, 2, 3, 0");
   for (; j + 4 <= free_end; j += 4) {
-    tile<false, false, 1>(c, j, qf, o, m_ref, negm, l_part, st);
-    tile<false, false, 2>(c, j + 1, qf, o, m_ref, negm, l_part, st);
-    tile<false, false, 3>(c, j + 2, qf, o, m_ref, negm, l_part, st);
-    tile<false, false, 0>(c, j + 3, qf, o, m_ref, negm, l_part, st);
+    tile<F8, false, false, 1>(c, j, qf, o, m_ref, negm, l_part, st);
+    tile<F8, false, false, 2>(c, j + 1, qf, o, m_ref, negm, l_part, st);
+    tile<F8, false, false, 3>(c, j + 2, qf, o, m_ref, negm, l_part, st);
+    tile<F8, false, false, 0>(c, j + 3, qf, o, m_ref, negm, l_part, st);
   }
-  for (; j < free_end; ++j) tile<false, false, -1>(c, j, qf, o, m_ref, negm, l_part, st);
-  for (; j < nt; ++j) tile<true, false, -1>(c, j, qf, o, m_ref, negm, l_part, st);
+  for (; j < free_end; ++j) tile<F8, false, false, -1>(c, j, qf, o, m_ref, negm, l_part, st);
+  for (; j < nt; ++j) tile<F8, true, false, -1>(c, j, qf, o, m_ref, negm, l_part, st);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
 
   const float l = l_part + __shfl_xor(l_part, 32);
@@ -743,17 +950,31 @@ hipError_t launch_attention(const AttnArgs& a, int32_t op_dtype, hipStream_t s) 
     dim3 grid((a.Lq + 127) / 128, a.H);
     if (a.D == 128 && a.T >= d128::BN && a.flags) {
       const int items = ((a.Lq + d128::BM - 1) / d128::BM) * a.H;
-      hipLaunchKernelGGL(k_attn_bf16_d128, dim3(items), dim3(64 * d128::WAVES), 0, s, a);
+      if (a.v_fp8) {
+        hipLaunchKernelGGL(k_attn_bf16_d128<true>, dim3(items), dim3(64 * d128::WAVES), 0, s, a);
+      } else {
+        hipLaunchKernelGGL(k_attn_bf16_d128<false>, dim3(items), dim3(64 * d128::WAVES), 0, s, a);
+      }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(256), 0, s, a);  // flagged tiles only
+      if (a.v_fp8)  // flagged tiles only
+        hipLaunchKernelGGL((k_attn_bf16<128, true>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_attn_bf16<128, false>), grid, dim3(256), 0, s, a);
     } else {
       AttnArgs g = a;
       g.flags = nullptr;
-      if (a.D == 128)
-        hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(256), 0, s, g);
-      else
-        hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(256), 0, s, g);
+      if (a.D == 128) {
+        if (a.v_fp8)
+          hipLaunchKernelGGL((k_attn_bf16<128, true>), grid, dim3(256), 0, s, g);
+        else
+          hipLaunchKernelGGL((k_attn_bf16<128, false>), grid, dim3(256), 0, s, g);
+      } else {
+        if (a.v_fp8)
+          hipLaunchKernelGGL((k_attn_bf16<64, true>), grid, dim3(256), 0, s, g);
+        else
+          hipLaunchKernelGGL((k_attn_bf16<64, false>), grid, dim3(256), 0, s, g);
+      }
     }
   } else if (op_dtype == DT_F32) {
     dim3 grid((a.Lq + 63) / 64, a.H);

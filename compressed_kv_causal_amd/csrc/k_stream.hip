@@ -3,6 +3,7 @@
 //   k_compress     ConvKV depthwise strided temporal conv, r frames -> one memory slot
 //   k_rope_table   cos/sin table of the bounded reset positions (double, once per cache)
 //   k_rope         RoPE reset + apply: rotated history keys, rotated block Q/K, staged V
+//   k_vscale_stage FP8 cache: every key's V scale terms in attention order
 //
 // Work unit everywhere: one (token, head) row of D channels, handled by D/8 consecutive
 // lanes, 8 channels (16 bytes of bf16) per lane, so a wave reads and writes 64 x 16 B
@@ -263,9 +264,10 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32
 // rotated at t = fi into krot[h][fi*T + u] (only when the history is rebuilt, else the grid
 // starts at the block's frames); frames after are the block's frames i = fi - n_hist at
 // t = fi: q -> qrot (times q_scale = log2(e)/sqrt(D), so that q . k is the base-2 exponent
-// of the softmax), k -> krot[h][t*T + u], v -> vcur.  Every output is in the operand
-// dtype (in_dtype).  An FP8 cache is dequantised on the way (code * row scale), and its
-// history V rows are dequantised into vhist in attention order as well.
+// of the softmax), k -> krot[h][t*T + u], v -> vcur.  krot and qrot are in the operand
+// dtype (in_dtype); an FP8 cache's keys are read as code * row scale.  An FP8 cache's
+// attention reads V as stored (codes), so the pass leaves history V alone and quantises
+// the block's V like the cache stores it (codes to vcur, row scales to vcur_scale).
 template <int LPR>
 __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
   const int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
@@ -291,12 +293,6 @@ __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
     rope_rotate8(a, fi, u, li, x);
     const int64_t drow = h * KFT + (int64_t)fi * a.T + u;
     store8_op(a.krot, a.in_dtype, drow * D + li * 8, x);
-    if (fp8) {
-      const void* vsrc = src == SRC_REF ? a.ref_v : (src == SRC_MEM ? a.mem_v : a.ring_v);
-      const float* vscale = src == SRC_REF ? a.ref_v_scale : (src == SRC_MEM ? a.mem_v_scale : a.ring_v_scale);
-      load8_kv(vsrc, DT_FP8, srow * D + li * 8, vscale[srow], x);
-      store8_op(a.vhist, a.in_dtype, ((int64_t)fi * rows + row) * D + li * 8, x);
-    }
     return;
   }
   const int32_t i = fi - n_hist;                           // frame inside the block
@@ -312,7 +308,58 @@ __global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
   store8_op(a.krot, a.in_dtype, (h * KFT + (int64_t)fi * a.T + u) * D + li * 8, x);
 
   load8_in(a.v_cur, a.in_dtype, crow * D + li * 8, x);
-  store8_op(a.vcur, a.in_dtype, crow * D + li * 8, x);
+  if (fp8) {
+    const float sc = store8_kv<LPR>(a.vcur, DT_FP8, crow * D + li * 8, x);
+    if (li == 0) a.vcur_scale[crow] = sc;
+  } else {
+    store8_op(a.vcur, a.in_dtype, crow * D + li * 8, x);
+  }
+}
+
+// FP8 attention's per-key V scale terms, in attention order (see VscaleArgs): workgroup
+// (h, p) takes the p-th of kVmaxParts slices of head h's keys, reads each key's row scale
+// where the cache keeps it (reference, memory or ring slot; the staged block) and writes
+// s_v, 1/s_v and the bf16 (hi, lo) split of log2(s_v), contiguous per head, and the
+// slice's largest s_v.  The attention scales its probabilities by 2^-E_h, 2^E_h the power
+// of two above the head's largest s_v, so that probability times s_v stays inside e4m3's
+// range, and adds the log2 pair to its scores.  An s_v below the smallest normal f32 (a
+// row of all but zero values) counts as that normal in the 1/s_v and log2 planes, where
+// it only has to give P~ = 0 and a finite 1/s_v.
+__global__ __launch_bounds__(256) void k_vscale_stage(const VscaleArgs a) {
+  const int32_t h = blockIdx.x;
+  const int32_t per = (a.Lk + kVmaxParts - 1) / kVmaxParts;
+  const int32_t j0 = blockIdx.y * per;
+  const int32_t j1 = j0 + per < a.Lk ? j0 + per : a.Lk;
+  const int32_t nh = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
+  const int64_t P = (int64_t)a.H * a.key_frames_max * a.T;
+  float* s0 = a.vscale + (int64_t)h * a.key_frames_max * a.T;
+  float m = 0.0f;
+  for (int32_t j = j0 + threadIdx.x; j < j1; j += 256) {
+    const int32_t fi = j / a.T, u = j - fi * a.T;
+    float sv;
+    if (fi < nh) {
+      int32_t slot;
+      const int32_t src = hist_src(a.hist, fi, &slot);
+      const float* base = src == SRC_REF ? a.ref_v_scale : (src == SRC_MEM ? a.mem_v_scale : a.ring_v_scale);
+      sv = base[((int64_t)slot * a.T + u) * a.H + h];
+    } else {
+      sv = a.vcur_scale[((int64_t)(fi - nh) * a.T + u) * a.H + h];
+    }
+    m = fmaxf(m, sv);
+    const float sn = fmaxf(sv, 0x1p-126f);
+    const float l = log2f(sn);
+    const uint16_t hi = f32_to_bf16(l);
+    const uint16_t lo = f32_to_bf16(l - bf16_to_f32(hi));
+    s0[j] = sv;
+    s0[P + j] = 1.0f / sn;
+    reinterpret_cast<uint32_t*>(s0)[2 * P + j] = (uint32_t)hi | ((uint32_t)lo << 16);
+  }
+  m = group_max<64>(m);
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    a.vmax[h * kVmaxParts + blockIdx.y] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -362,6 +409,12 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_compress<16>, grid, dim3(64), 0, s, a);
   else
     hipLaunchKernelGGL(k_compress<8>, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_vscale_stage(const VscaleArgs& a, hipStream_t s) {
+  if (a.H <= 0 || a.Lk <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_vscale_stage, dim3(a.H, kVmaxParts), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -55,8 +55,9 @@ struct CompressArgs {
 };
 
 // RoPE reset + apply: rebuild rotated history keys (if hist_rows) and stage the block.
-// Staged operands (krot, qrot, vcur, vhist) are in the operand dtype = in_dtype (the q
-// dtype): an FP8 cache is dequantised here, once per step, and attention runs on bf16.
+// krot and qrot are in the operand dtype = in_dtype (the q dtype; an FP8 cache's keys are
+// dequantised here).  vcur is in the kv dtype: an FP8 cache's block V is quantised per
+// (token, head) row as the cache stores it, its row scales going to vcur_scale.
 struct RopeArgs {
   const void* q;
   const void* k_cur;
@@ -75,11 +76,11 @@ struct RopeArgs {
   const float* ref_v_scale;
   void* krot;              // [H][KF*T][D] operand dtype
   void* qrot;              // [H][B_max*T][D]
-  void* vcur;              // [B_max][T][H][D]
-  void* vhist;             // FP8 only: [ref+M+W][T][H][D] dequantised V of the history
+  void* vcur;              // [B_max][T][H][D] kv dtype
+  float* vcur_scale;       // FP8 only: [B_max][T][H]
   const float2* table;
   HistMap hist;
-  int32_t hist_rows;       // 1: rebuild history keys (and, FP8, history values)
+  int32_t hist_rows;       // 1: rebuild history keys (and, FP8, the history V scales)
   int32_t n_cur, T, H, D, grid_h, grid_w, key_frames_max, block_frames_max;
   int32_t rope_mode, split_t, split_h, split_w;
   int32_t in_dtype, kv_dtype;
@@ -103,6 +104,13 @@ struct AttnArgs {
   const void* v_mem;       // V rows of memory frames (memory slots)
   const void* v_ref;       // V rows of reference frames (reference slots)
   const void* v_cur;       // V rows of the block's frames
+  // FP8 cache: V rows above are e4m3 codes; the value of key j, head h is code *
+  // vscale[h * vs_head_stride + j] (plane 0; plane p at + p * vs_plane); vmax[h * 32 ..
+  // h * 32 + 31] are partial maxima of the head's scales
+  const float* vscale;
+  const float* vmax;
+  int64_t vs_head_stride, vs_plane;
+  int32_t v_fp8;
   void* out;               // [Lq][H][D] q dtype
   float* lse;              // [H][Lq] or null
   int32_t* flags;          // per (head, 256-row query tile): 1 = redo with the exact pass
@@ -117,6 +125,22 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
 hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
+// FP8 cache: every key's V row scale s_v in attention order [reference | memory | window |
+// block], as 3 planes [H][KF*T]: s_v, 1/s_v, and log2(s_v) as a bf16 (hi, lo) pair; and
+// vmax[h * kVmaxParts + p] = the largest s_v of the p-th of kVmaxParts slices of head h's
+// keys (0 for an empty slice).
+constexpr int kVmaxParts = 32;
+struct VscaleArgs {
+  const float* ring_v_scale;  // [R][T][H]
+  const float* mem_v_scale;   // [M][T][H]
+  const float* ref_v_scale;   // [ref][T][H]
+  const float* vcur_scale;    // [B_max][T][H]
+  float* vscale;              // [3][H][KF*T]
+  float* vmax;                // [H][kVmaxParts]
+  HistMap hist;
+  int32_t T, H, Lk, key_frames_max;
+};
+hipError_t launch_vscale_stage(const VscaleArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int32_t op_dtype, hipStream_t s);
 
 }  // namespace lact

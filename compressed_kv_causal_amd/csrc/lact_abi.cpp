@@ -123,10 +123,12 @@ void compute_layout(const lact_cfg& c, int32_t members, lact_layout* L) {
   off = L->member_bytes * (size_t)members;
   L->krot = take(ob * KF);
   L->qrot = take(ob * B);
-  L->vcur = take(ob * B);
-  L->vhist = take(fp8 ? ob * (size_t)(c.ref_frames + M + c.window_frames) : 0);
+  L->vcur = take(fb * B);
+  L->vcur_scale = take(fp8 ? sb * B : 0);
+  L->vscale = take(fp8 ? 3 * sizeof(float) * (size_t)c.heads * (size_t)KF * (size_t)T : 0);
   L->rope_table = take(sizeof(float) * 2 * (size_t)rope_table_entries(c));
   L->attn_flags = take(sizeof(int32_t) * (size_t)c.heads * (size_t)((B * T + 255) / 256));
+  L->vmax = take(fp8 ? sizeof(float) * lact::kVmaxParts * (size_t)c.heads : 0);
   L->total = off;
   L->frame_bytes = fb;
   L->ring_slots = R;
@@ -145,7 +147,7 @@ struct lact_cache {
   uint64_t staged_version = 0;  // ... of this state version
   int32_t staged_frames = 0;
   int32_t staged_member = 0;
-  bool hist_built = false;    // the staged history (krot, vhist) is hist_member's ...
+  bool hist_built = false;    // the staged history (krot, FP8 vscale) is hist_member's ...
   uint64_t hist_version = 0;  // ... at this version
   int32_t hist_member = 0;
   std::vector<uint8_t> ref_valid;  // per member: the reference segment has been stored
@@ -312,7 +314,8 @@ lact_status lact_member_rope_reset_apply(lact_cache* c, int32_t member, const vo
   a.krot = c->at(c->lay.krot);
   a.qrot = c->at(c->lay.qrot);
   a.vcur = c->at(c->lay.vcur);
-  a.vhist = g.kv_dtype == LACT_FP8_E4M3 ? c->at(c->lay.vhist) : nullptr;
+  const bool fp8 = g.kv_dtype == LACT_FP8_E4M3;
+  a.vcur_scale = fp8 ? reinterpret_cast<float*>(c->at(c->lay.vcur_scale)) : nullptr;
   a.table = static_cast<const float2*>(c->at(c->lay.rope_table));
   a.hist = c->hist();
   const bool rebuild = capturing || !(c->hist_built && c->hist_version == c->plan.version() &&
@@ -335,6 +338,22 @@ lact_status lact_member_rope_reset_apply(lact_cache* c, int32_t member, const vo
   a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)g.head_dim));
   hipError_t e = lact::launch_rope(a, s);
   if (e != hipSuccess) return hip_fail(e, "rope launch");
+  if (fp8) {
+    lact::VscaleArgs v;
+    v.ring_v_scale = a.ring_v_scale;
+    v.mem_v_scale = a.mem_v_scale;
+    v.ref_v_scale = a.ref_v_scale;
+    v.vcur_scale = a.vcur_scale;
+    v.vscale = reinterpret_cast<float*>(c->at(c->lay.vscale));
+    v.vmax = reinterpret_cast<float*>(c->at(c->lay.vmax));
+    v.hist = a.hist;
+    v.T = c->T();
+    v.H = g.heads;
+    v.Lk = (c->plan.history_frames() + n_frames) * c->T();
+    v.key_frames_max = c->lay.key_frames_max;
+    e = lact::launch_vscale_stage(v, s);
+    if (e != hipSuccess) return hip_fail(e, "V scale staging launch");
+  }
   c->hist_built = !capturing;
   c->hist_version = c->plan.version();
   c->hist_member = member;
@@ -458,21 +477,17 @@ static lact_status block_attention_impl(lact_cache* c, int32_t member, const int
   a.q_head_stride = (int64_t)g.max_block_frames * T * g.head_dim;
   a.k_head_stride = (int64_t)c->lay.key_frames_max * T * g.head_dim;
   a.hist = c->hist();
+  // V is read where it is stored: the member's reference, memory and ring rows, and the
+  // staged block (an FP8 cache's as e4m3 codes, with every key's row scale in vscale)
+  a.v_ring = c->mat(member, c->lay.ring_v);
+  a.v_mem = c->mat(member, c->lay.mem_v);
+  a.v_ref = c->mat(member, c->lay.ref_v);
   if (g.kv_dtype == LACT_FP8_E4M3) {
-    // history V was dequantised into vhist in attention order: reference frames from its
-    // start, then memory ranks, then window ranks
-    const size_t ob = (size_t)T * g.heads * g.head_dim * elem_bytes(g.q_dtype);
-    a.v_ref = c->at(c->lay.vhist);
-    a.v_mem = c->at(c->lay.vhist + ob * (size_t)a.hist.ref_len);
-    a.v_ring = c->at(c->lay.vhist + ob * (size_t)(a.hist.ref_len + a.hist.mem_len));
-    a.hist.mem_slot0 = 0;
-    a.hist.ring_slot0 = 0;
-    a.hist.M = a.hist.mem_len > 0 ? a.hist.mem_len : 1;
-    a.hist.R = a.hist.win_len > 0 ? a.hist.win_len : 1;
-  } else {
-    a.v_ring = c->mat(member, c->lay.ring_v);
-    a.v_mem = c->mat(member, c->lay.mem_v);
-    a.v_ref = c->mat(member, c->lay.ref_v);
+    a.v_fp8 = 1;
+    a.vscale = reinterpret_cast<const float*>(c->at(c->lay.vscale));
+    a.vmax = reinterpret_cast<const float*>(c->at(c->lay.vmax));
+    a.vs_head_stride = (int64_t)c->lay.key_frames_max * T;
+    a.vs_plane = a.vs_head_stride * g.heads;
   }
   a.T = T;
   a.H = g.heads;

@@ -121,11 +121,13 @@ typedef struct {
 } lact_state;
 
 /* Offsets (bytes, 256-aligned) of the regions inside the cache buffer, so a caller can
- * inspect or snapshot it.  Scale regions and vhist are 0-sized unless kv_dtype is
+ * inspect or snapshot it.  Scale regions, vcur_scale, vscale and vmax are 0-sized unless
+ * kv_dtype is
  * FP8_E4M3.  The persistent regions (ring_*, mem_*, ref_* and their scales) come first and
  * are per member: member m's copy of a region starts at offset + m * member_bytes.  The
- * staging regions (krot, qrot, vcur, vhist, rope_table, attn_flags) follow all members
- * and are shared by them.
+ * staging regions (krot, qrot, vcur, vcur_scale, vscale, rope_table, attn_flags, vmax)
+ * follow all
+ * members and are shared by them.
  *   ring_k/ring_v  [R][T][H][D] kv dtype            raw ring (pre-RoPE K, V)
  *   mem_k/mem_v    [M][T][H][D] kv dtype            compressed memory slots
  *   ref_k/ref_v    [ref_frames][T][H][D] kv dtype   reference segment (pre-RoPE K, V)
@@ -133,21 +135,27 @@ typedef struct {
  *   qrot           [H][B_max*T][D] operand          rotated queries of the block, times
  *                                                   log2(e)/sqrt(D) (the softmax scale
  *                                                   and the change to base 2)
- *   vcur           [B_max][T][H][D] operand         current V staged for attention
- *   vhist          [ref+M+W][T][H][D] operand       FP8: reference + memory + window V
- *                                                   dequantised, in attention order
+ *   vcur           [B_max][T][H][D] kv dtype        current V staged for attention (FP8:
+ *                                                   quantised per (token, head) row as the
+ *                                                   cache stores it)
+ *   vcur_scale     [B_max][T][H] f32                FP8: the row scales of vcur
+ *   vscale         [3][H][(ref+M+W+B_max)*T] 4 B    FP8: of every key in attention order
+ *                                                   its V row scale s_v (f32), 1/s_v (f32)
+ *                                                   and log2(s_v) as a bf16 (hi, lo) pair
  *   *_scale        f32 per (token, head): ring/mem/ref [slots][T][H]
  *   rope_table     float2 (cos, sin) table
  *   attn_flags     int32 per (head, 256-row query tile): attention work queue of the exact
  *                  fallback pass (rows whose fast pass could not be trusted)
+ *   vmax           [H][32] f32: FP8, partial maxima of each head's V scales
  * The persistent state is ring_*, mem_* and ref_* (and their scales); the rest is rewritten by
- * every step.  operand dtype = q_dtype: an FP8 cache is dequantised (code * scale) when the
- * RoPE pass stages a step, and attention runs on bf16 operands. */
+ * every step.  operand dtype = q_dtype: an FP8 cache's keys are dequantised (code * scale)
+ * and rotated into bf16 by the RoPE pass; its V stays e4m3 and attention multiplies it in
+ * on fp8 matrix cores. */
 typedef struct {
   size_t total;
-  size_t ring_k, ring_v, mem_k, mem_v, ref_k, ref_v, krot, qrot, vcur, vhist;
+  size_t ring_k, ring_v, mem_k, mem_v, ref_k, ref_v, krot, qrot, vcur, vcur_scale, vscale;
   size_t ring_k_scale, ring_v_scale, mem_k_scale, mem_v_scale, ref_k_scale, ref_v_scale;
-  size_t rope_table, attn_flags;
+  size_t rope_table, attn_flags, vmax;
   size_t frame_bytes;    /* T*H*D * kv element size                                       */
   int32_t ring_slots, key_frames_max;
   size_t member_bytes;   /* stride between members' persistent regions                    */
@@ -218,12 +226,14 @@ lact_status lact_member_ref_set(lact_cache* cache, int32_t member, const void* k
  * t = ref + mem_len + k; current frame i -> t = ref + mem_len + win_len + i (ref =
  * ref_frames); (h, w) = the token's grid cell.  Rotation of interleaved channel pairs
  * (2i, 2i+1) of each part by pos * theta^(-2i/d_part).
- * Writes krot (reference + memory + window + current keys), qrot and vcur in the operand
- * dtype (q_dtype).  The stored history is read as stored (FP8_E4M3: code * per-(token,
- * head) scale; the model card's FP8 KV cache option keeps K/V in FP8 and widens them for
- * the attention), and an FP8 cache also gets its reference + memory + window V dequantised
- * into vhist.  The history part is rebuilt only when the state changed since the last
- * call.  A call made while `stream` is being captured into a HIP graph records the
+ * Writes krot (reference + memory + window + current keys) and qrot in the operand dtype
+ * (q_dtype), and the block's V to vcur in the kv dtype.  The stored history keys are read
+ * as stored (FP8_E4M3: code * per-(token, head) scale; the model card's FP8 KV cache option
+ * keeps K/V in FP8 and dequantises them for use).  An FP8 cache's V stays in e4m3 for the
+ * attention: the pass quantises the block's V per (token, head) row as the cache stores it
+ * (vcur, vcur_scale), then writes every key's V row scale terms to vscale in attention
+ * order and, per head, partial maxima of those scales to vmax.  The history part is rebuilt only when the state changed
+ * since the last call.  A call made while `stream` is being captured into a HIP graph records the
  * history rebuild (and the cache's one-time cos/sin table) every time, so each replay
  * stages everything itself, and leaves both marked absent for the next eager call.
  *   q, k_cur, v_cur: [n_frames*T][H][D] in q_dtype.  1 <= n_frames <= B_max. */

@@ -49,24 +49,28 @@ def test_footprint_is_pure_and_matches_layout():
         # persistent regions first (one member), then the staging
         names = ("ring_k", "ring_v", "mem_k", "mem_v", "ref_k", "ref_v") + \
             (("ring_k_scale", "ring_v_scale", "mem_k_scale", "mem_v_scale", "ref_k_scale",
-              "ref_v_scale") if fp8 else ()) + ("krot", "qrot", "vcur", "vhist", "rope_table",
-                                                "attn_flags")
+              "ref_v_scale") if fp8 else ()) + ("krot", "qrot", "vcur", "vcur_scale", "vscale",
+                                                "rope_table", "attn_flags", "vmax")
         offs = [getattr(lay, n) for n in names]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         assert lay.members == 1 and lay.krot == lay.member_bytes
         fb, M, W = lay.frame_bytes, w["mem_slots"], w["window_frames"]
         assert lay.mem_k - lay.ring_v >= fb * R and lay.ref_k - lay.mem_v >= fb * M
-        # staged operands are in the q dtype; FP8 adds the dequantised history V
+        # staged keys and queries are in the q dtype, the block's V in the kv dtype; FP8
+        # adds every key's V row scale per head and the heads' exponent bounds
         ob = w["tokens"] * w["channels"] * {0: 4, 1: 2}[w["q_dtype"]]
         KF = lay.key_frames_max
         assert lay.qrot - lay.krot >= ob * KF and lay.vcur - lay.qrot >= ob * w["max_block_frames"]
+        assert lay.vcur_scale - lay.vcur >= fb * w["max_block_frames"]
         if fp8:
-            assert lay.vhist - lay.vcur >= ob * w["max_block_frames"]
-            assert lay.rope_table - lay.vhist >= ob * (ref + M + W)
+            assert lay.vscale - lay.vcur_scale >= w["tokens"] * w["heads"] * 4 * w["max_block_frames"]
+            assert lay.rope_table - lay.vscale >= 3 * 4 * w["heads"] * KF * w["tokens"]
+            assert lay.total - lay.vmax >= 4 * 32 * w["heads"]
             sb = w["tokens"] * w["heads"] * 4
             assert lay.member_bytes - lay.ref_v_scale >= sb * ref
         else:
-            assert lay.ring_k_scale == 0 and lay.vhist == lay.rope_table
+            assert lay.ring_k_scale == 0 and lay.vcur_scale == lay.vscale == lay.rope_table
+            assert lay.vmax == lay.total
     # 512x512 bf16: 2R + 2M + KF + 2 B_max = 120 frames of 10 MiB, plus the small tables
     mib = L.lact_cache_footprint(_cfg("s512_bf16")) / 2 ** 20
     assert 1200 <= mib < 1201
@@ -89,7 +93,7 @@ def test_set_layout_and_footprint():
                       "mem_v_scale", "frame_bytes", "ring_slots", "key_frames_max"):
                 assert getattr(lay, f) == getattr(one, f), f
             shift = (n - 1) * one.member_bytes
-            for f in ("krot", "qrot", "vcur", "vhist", "rope_table", "attn_flags", "total"):
+            for f in ("krot", "qrot", "vcur", "vscale", "rope_table", "attn_flags", "vmax", "vcur_scale", "total"):
                 assert getattr(lay, f) == getattr(one, f) + shift, f
             assert L.lact_set_footprint(c, n) == lay.total
     # 40 layers x 3 denoising steps at 512x512 bf16: 120 x 720 MiB persistent + 480 MiB staging
