@@ -40,7 +40,7 @@ class AttnArgs(ctypes.Structure):
         ("n_blocks", ctypes.c_int32), ("block_start", _i64),
         ("n_sel", ctypes.c_int64), ("sel_head", _i32), ("sel_row", _i64),
         ("form", ctypes.c_int32), ("threads", ctypes.c_int32),
-        ("out", _d), ("lse", _d),
+        ("out", _d), ("lse", _d), ("rms", _d),
     ]
 
 
@@ -199,14 +199,15 @@ def rope_rotate(x, t, u, mode, split, T, grid_w, theta=10000.0):
 def attention(q, k_cur, v_cur, k_hist, v_hist, hist_t, hist_u, cur_t, cur_u, block_frames,
               T, rope_mode, rope_split, grid_w, theta=10000.0, sel=None, form=1,
               q_scale=None, k_cur_scale=None, v_cur_scale=None, k_hist_scale=None,
-              v_hist_scale=None, threads=None):
+              v_hist_scale=None, threads=None, want_rms=False):
     """Oracle attention of the current queries over [history | current].
 
     q, k_cur, v_cur: [Lq][H][D]; k_hist, v_hist: [Lhist][H][D] (float32 stored values, or
     e4m3 code values with the *_scale arrays [L][H]).  block_frames: query block sizes in
     frames.  sel: (heads, rows) int arrays of outputs to compute (default all), which are
     sorted by head here.  Returns (O [n_sel][D] float64, LSE [n_sel] float64, heads, rows)
-    in the sorted order.
+    in the sorted order, and with want_rms also RMS [n_sel] = sqrt(sum_j w_j^2 |v_j|^2)
+    (w the softmax weights of the row).
     """
     q = _c(q, np.float32)
     Lq, H, D = q.shape
@@ -239,6 +240,7 @@ def attention(q, k_cur, v_cur, k_hist, v_hist, hist_t, hist_u, cur_t, cur_u, blo
     n_sel = heads.size
     out = np.zeros((n_sel, D), np.float64)
     lse = np.zeros(n_sel, np.float64)
+    rms = np.zeros(n_sel, np.float64) if want_rms else None
     keep = []
 
     def sc(a):
@@ -269,8 +271,10 @@ def attention(q, k_cur, v_cur, k_hist, v_hist, hist_t, hist_u, cur_t, cur_u, blo
     args.sel_head, args.sel_row = _p(heads, _i32), _p(rows, _i64)
     args.form = form
     args.threads = threads if threads else min(16, os.cpu_count() or 1)
-    args.out, args.lse = _p(out, _d), _p(lse, _d)
+    args.out, args.lse, args.rms = _p(out, _d), _p(lse, _d), _p(rms, _d)
     rc = lib().lacto_attention(ctypes.byref(args))
     if rc != 0:
         raise ValueError(f"lacto_attention failed with {rc}")
+    if want_rms:
+        return out, lse, heads, rows, rms
     return out, lse, heads, rows

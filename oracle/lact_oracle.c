@@ -31,6 +31,8 @@
  * the stored (quantised) values; what a kernel's own extra rounding adds is held to the
  * FP8 bar, not pinned to a value.
  */
+#include "lact_oracle.h"
+
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
@@ -264,29 +266,6 @@ void lacto_rope_rotate(double* x, int64_t n, int32_t H, int32_t D, const int32_t
 /* ===================================================================================== */
 
 typedef struct {
-  int32_t H, D;
-  int64_t Lq, Lhist;
-  const float *q, *q_scale;            /* [Lq][H][D], [Lq][H] or NULL                     */
-  const float *k_hist, *k_hist_scale;  /* [Lhist][H][D], [Lhist][H] or NULL               */
-  const float *v_hist, *v_hist_scale;
-  const float *k_cur, *k_cur_scale;    /* [Lq][H][D]                                      */
-  const float *v_cur, *v_cur_scale;
-  const int32_t *hist_t, *hist_u;      /* positions of the history tokens                 */
-  const int32_t *cur_t, *cur_u;        /* positions of the current tokens (q and k)       */
-  int32_t rope_mode, rope_split[3], T, grid_w;
-  double rope_theta;
-  int32_t n_blocks;
-  const int64_t* block_start;          /* [n_blocks + 1] query-token offsets, 0 .. Lq     */
-  int64_t n_sel;
-  const int32_t* sel_head;             /* selected (head, row) outputs, sorted by head    */
-  const int64_t* sel_row;
-  int32_t form;                        /* 0 explicit mask matrix, 1 segments             */
-  int32_t threads;
-  double* out;                         /* [n_sel][D]                                      */
-  double* lse;                         /* [n_sel]                                         */
-} lacto_attn_args;
-
-typedef struct {
   const lacto_attn_args* a;
   const double* hist_cs; /* [Lhist][D] cos/sin pairs */
   const double* cur_cs;  /* [Lq][D] */
@@ -317,6 +296,7 @@ static void* attn_worker(void* p) {
   double* s = (double*)malloc(sizeof(double) * (size_t)Lk);
   double* raw = (double*)malloc(sizeof(double) * (size_t)D);
   double* qh = (double*)malloc(sizeof(double) * (size_t)D);
+  double* vn2 = (double*)malloc(sizeof(double) * (size_t)Lk); /* |v_j|^2 of head cur_head */
   int32_t cur_head = -1;
   const double inv_sqrt_d = 1.0 / sqrt((double)D);
   for (int64_t n = job->sel_lo; n < job->sel_hi; ++n) {
@@ -327,11 +307,13 @@ static void* attn_worker(void* p) {
         int hist = j < a->Lhist;
         int64_t tok = hist ? j : j - a->Lhist;
         const double* cs = hist ? job->hist_cs + tok * D : job->cur_cs + tok * D;
+        vn2[j] = 0.0;
         for (int32_t d = 0; d < D; ++d) {
           raw[d] = hist ? value_at(a->k_hist, a->k_hist_scale, tok, h, H, D, d)
                         : value_at(a->k_cur, a->k_cur_scale, tok, h, H, D, d);
           vals[j * D + d] = hist ? value_at(a->v_hist, a->v_hist_scale, tok, h, H, D, d)
                                  : value_at(a->v_cur, a->v_cur_scale, tok, h, H, D, d);
+          vn2[j] += vals[j * D + d] * vals[j * D + d];
         }
         rope_apply_row(cs, D, raw, krot + j * D);
       }
@@ -362,23 +344,26 @@ static void* attn_worker(void* p) {
       }
       n_vis = end;
     }
-    double l = 0.0;
+    double l = 0.0, q2 = 0.0;
     double* o = a->out + n * D;
     for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
     for (int64_t j = 0; j < n_vis; ++j) {
       double pj = exp(s[j] - mx);
       if (pj == 0.0) continue;
       l += pj;
+      q2 += pj * pj * vn2[j];
       for (int32_t d = 0; d < D; ++d) o[d] += pj * vals[j * D + d];
     }
     for (int32_t d = 0; d < D; ++d) o[d] /= l;
     a->lse[n] = mx + log(l);
+    if (a->rms) a->rms[n] = sqrt(q2) / l;
   }
   free(krot);
   free(vals);
   free(s);
   free(raw);
   free(qh);
+  free(vn2);
   return NULL;
 }
 

@@ -136,9 +136,10 @@ class OracleCache:
         return (cat(ks), cat(kss) if fp8 else None, cat(vs), cat(vss) if fp8 else None,
                 cat(ts), u)
 
-    def attention(self, q, k_cur, v_cur, block_frames=None, sel=None, form=1, threads=None):
+    def attention(self, q, k_cur, v_cur, block_frames=None, sel=None, form=1, threads=None,
+                  want_rms=False):
         """q, k_cur, v_cur: [n*T][H][D] float32 input values of the current block.
-        Returns (O, LSE, heads, rows) for the selected outputs (see oracle.attention)."""
+        Returns (O, LSE, heads, rows[, RMS]) for the selected outputs (see oracle.attention)."""
         n = q.shape[0] // self.T
         if block_frames is None:
             block_frames = [n]
@@ -150,4 +151,4 @@ class OracleCache:
         return O.attention(q, k_cur, v_cur, kh, vh, ht, hu, cur_t, cur_u, block_frames, self.T,
                            c["rope_mode"], c["rope_split"], c["grid_w"], c["rope_theta"],
                            sel=sel, form=form, k_hist_scale=khs, v_hist_scale=vhs,
-                           threads=threads)
+                           threads=threads, want_rms=want_rms)

@@ -16,6 +16,60 @@ def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
+ATTN_BAR = {F32: 1e-5, BF16: 1e-2, FP8: 5e-2}
+
+
+def row_bounds(O, rms, qnorm, kpair, heads, kv_dtype, D):
+    """Per-row bound on |O_gpu - O| (L2 over the row's D outputs) from a rounding model:
+    each key's softmax weight w_j gets an independent relative error -- the rounding of
+    the probability fed to the PV product (unit roundoff u_P: 2^-8 in bf16, 2^-4 in e4m3),
+    the block's own V rounded to e4m3 on the FP8 path (u_V = 2^-4), and the score error
+    from bf16 Q and K (each element rounded with relative error <= 2^-8, uniform), whose
+    variance per key is at most (2 u^2 / 3D) |q_i|^2 k_pair^2 (k_pair: the largest norm of
+    a channel pair of any visible key of the head; RoPE keeps pair norms).  The error is
+    then a sum of independent terms w_j e_j v_j whose RMS is at most
+    sqrt(u_P^2/3 + u_V^2/3 + sigma_s^2) * RMS_i, RMS_i = sqrt(sum_j w_j^2 |v_j|^2) from the
+    oracle; the bound takes 4 of those plus the bf16 rounding of the output.  None for the
+    f32 path (no rounding beyond f32)."""
+    if kv_dtype == F32:
+        return None
+    u = 2.0 ** -8
+    uP = 2.0 ** -4 if kv_dtype == FP8 else u
+    uV = 2.0 ** -4 if kv_dtype == FP8 else 0.0
+    ss = u * np.sqrt(2.0 / (3.0 * D)) * qnorm * kpair[heads]
+    sigma = np.sqrt(uP ** 2 / 3 + uV ** 2 / 3 + ss ** 2)
+    return 4.0 * sigma * rms + u * np.linalg.norm(O, axis=1) + 1e-6
+
+
+def check_heads_and_rows(got, O, heads, kv_dtype, bounds=None, label=""):
+    """Every head's relative L2 within the dtype's bar, and (bounds) every row within its
+    bound.  Returns (worst head rel L2, worst row error / bound)."""
+    bar = ATTN_BAR[kv_dtype]
+    worst_head, worst_h = 0.0, -1
+    for h in np.unique(heads):
+        sel = heads == h
+        e = rel_l2(got[sel], O[sel])
+        if e > worst_head:
+            worst_head, worst_h = e, int(h)
+    assert worst_head <= bar, f"{label}: head {worst_h} rel L2 {worst_head:.3e} > {bar}"
+    worst_row = 0.0
+    if bounds is not None:
+        e = np.linalg.norm(np.asarray(got, np.float64) - O, axis=1)
+        ratio = e / bounds
+        i = int(np.argmax(ratio))
+        worst_row = float(ratio[i])
+        assert worst_row <= 1.0, (f"{label}: row {i} (head {int(heads[i])}) error {e[i]:.3e} > "
+                                  f"bound {bounds[i]:.3e}")
+    return worst_head, worst_row
+
+
+def pair_norm_max(vals):
+    """vals [..., H, D] -> [H]: the largest norm of a channel pair (2i, 2i+1)."""
+    x = np.asarray(vals, np.float64)
+    pn = np.sqrt(x[..., 0::2] ** 2 + x[..., 1::2] ** 2)      # [..., H, D/2]
+    return pn.reshape(-1, pn.shape[-2], pn.shape[-1]).max(axis=(0, 2))
+
+
 def io_dtype(w):
     return torch.float32 if w["q_dtype"] == F32 else torch.bfloat16
 
@@ -95,7 +149,11 @@ class Runner:
             out = self.cache.block_attention(blocks, lse=lse_t, member=self.member)
             res["out"], res["lse"] = out, lse_t
             if self.oc is not None and sel is not False:
-                res["ref"] = self.oc.attention(qh, kh, vh, block_frames=blocks, sel=sel, form=form)
+                *ref, rms = self.oc.attention(qh, kh, vh, block_frames=blocks, sel=sel, form=form,
+                                              want_rms=True)
+                res["ref"] = tuple(ref)
+                res["rms"] = rms
+                res["kpair"] = np.maximum(self._hist_kpair(), pair_norm_max(kh))
                 if self.w["kv_dtype"] == FP8:
                     res["hist_kmax"] = self._hist_kmax()
             res["q"] = qh
@@ -103,16 +161,42 @@ class Runner:
 
     # ---- comparisons -------------------------------------------------------------------
     def compare_attention(self, res):
-        """(rel L2 of O over the oracle's selected rows, max |dLSE|)."""
+        """(rel L2 of O over the oracle's selected rows, max |dLSE|).  Also holds every
+        head's rel L2 to the dtype's bar and, with the oracle's per-row RMS, every row to
+        its bound (row_bounds); records them as res["worst_head"], res["worst_row"]."""
         O, LSE, heads, rows = res["ref"]
         out = res["out"].float().cpu().numpy()           # [Lq][H][D]
         got = out[rows, heads, :]
         err = rel_l2(got, O)
+        if "rms" in res:
+            kv = self.w["kv_dtype"]
+            qn = np.linalg.norm(res["q"][rows, heads, :].astype(np.float64), axis=1)
+            b = row_bounds(O, res["rms"], qn, res["kpair"], heads, kv, self.D)
+            res["worst_head"], res["worst_row"] = check_heads_and_rows(
+                got, O, heads, kv, b, label=f"{self.w['name']} step {self.step_index}")
         dl = 0.0
         if res.get("lse") is not None:
             lse = res["lse"].cpu().numpy()
             dl = float(np.abs(lse[heads, rows] - LSE).max())
         return err, dl
+
+    def _hist_kpair(self):
+        """Per head, the largest channel-pair norm of a stored history key (0 if none)."""
+        from oracle.bookkeeping import SEG_MEMORY, SEG_REF
+        kp = np.zeros(self.H)
+        for kf in self.oc.keys(0):
+            if kf["segment"] == SEG_MEMORY:
+                sk = self.oc.mem[kf["slot"]][1]
+            elif kf["segment"] == SEG_REF:
+                sk = self.oc.ref[kf["slot"]][0]
+            else:
+                sk = self.oc.raw[kf["id"]][0]
+            vals, scales = self.oc.stored_value(sk)
+            v = vals.astype(np.float64)
+            if scales is not None:
+                v = v * scales[..., None]
+            kp = np.maximum(kp, pair_norm_max(v))
+        return kp
 
     def _hist_kmax(self):
         """Per head, the largest norm of a stored history key at the present state."""

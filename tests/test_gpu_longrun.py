@@ -11,7 +11,7 @@ import compressed_kv_causal_amd as L
 import synth
 from oracle.bookkeeping import Bookkeeping
 from oracle.stream import OracleCache
-from stream_helpers import rel_l2, sample_rows
+from stream_helpers import BF16, check_heads_and_rows, pair_norm_max, rel_l2, row_bounds, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -66,11 +66,18 @@ def test_long_run_1000_steps():
             oc = OracleCache.at_state(w, bkp.F, frame_kv, wk, bk, wv, bv)
             qh, kh, vh = host[(step - 1) % pool_blocks]
             sel = sample_rows(w, B, seed=step, per_head=2)
-            O, LSE, heads, rows = oc.attention(qh, kh, vh, sel=sel)
+            O, LSE, heads, rows, rms = oc.attention(qh, kh, vh, sel=sel, want_rms=True)
             got = out.float().cpu().numpy()[rows, heads]
             errs[step] = rel_l2(got, O)
             dl = float(np.abs(lse.cpu().numpy()[heads, rows] - LSE).max())
-            print(f"step {step}: rel L2 {errs[step]:.3e}, max dLSE {dl:.2e}", flush=True)
+            kh_hist = oc.history()[0]
+            kpair = pair_norm_max(kh) if kh_hist is None else \
+                np.maximum(pair_norm_max(kh), pair_norm_max(kh_hist))
+            qn = np.linalg.norm(qh[rows, heads].astype(np.float64), axis=1)
+            b = row_bounds(O, rms, qn, kpair, heads, BF16, D)
+            wh, wr = check_heads_and_rows(got, O, heads, BF16, b, label=f"long run step {step}")
+            print(f"step {step}: rel L2 {errs[step]:.3e}, worst head {wh:.3e}, worst row / bound "
+                  f"{wr:.3f}, max dLSE {dl:.2e}", flush=True)
             assert errs[step] <= 1e-2 and dl <= 2e-2
         L.lact_kv_ring_append(cache.h, k, v, B)
         L.lact_convkv_compress(cache.h, *d_w)

@@ -215,7 +215,8 @@ def _big_step_parity(name, warm, n_last, per_head=6, first_check=False, **overri
             sel = sample_rows(w, n, seed=s, per_head=per_head)
             res = run.step(n, sel=sel)
             err, dl = run.compare_attention(res)
-            say(f"{name} step 1 ({n} frames, no history): rel L2 {err:.3e}, max dLSE {dl:.2e}")
+            say(f"{name} step 1 ({n} frames, no history): rel L2 {err:.3e}, worst head "
+                f"{res['worst_head']:.3e}, worst row / bound {res['worst_row']:.3f}, max dLSE {dl:.2e}")
             assert err <= ATTN_TOL[kv]
             assert_lse(run, res, kv)
             errs.append(err)
@@ -229,7 +230,8 @@ def _big_step_parity(name, warm, n_last, per_head=6, first_check=False, **overri
     sel = sample_rows(w, n_last, seed=99, per_head=per_head)
     res = run.step(n_last, sel=sel)
     err, dl = run.compare_attention(res)
-    say(f"{name} step {warm + 1}: Lq {n_last * w['tokens']}, rel L2 {err:.3e}, max dLSE {dl:.2e}")
+    say(f"{name} step {warm + 1}: Lq {n_last * w['tokens']}, rel L2 {err:.3e}, worst head "
+        f"{res['worst_head']:.3e}, worst row / bound {res['worst_row']:.3f}, max dLSE {dl:.2e}")
     assert err <= ATTN_TOL[kv]
     assert_lse(run, res, kv)
     return run

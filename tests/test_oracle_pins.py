@@ -676,3 +676,47 @@ def test_reference_zero_query_is_mean_of_visible_values():
         for i in sel:
             np.testing.assert_allclose(O_[i], mean[heads[i]], rtol=0, atol=1e-12)
             assert abs(LSE[i] - math.log(visible.shape[0])) < 1e-12
+
+
+# ---- the per-row size of the weighted terms (used by the per-row parity bounds) ---------
+
+def test_attention_rms_closed_forms():
+    """RMS = sqrt(sum_j w_j^2 |v_j|^2): one visible key gives |v|; a zero query gives
+    uniform weights 1/N over the visible keys, so RMS = sqrt(sum |v_j|^2) / N; the two-key
+    hand example gives sqrt(w_h^2 |v_h|^2 + w_c^2 |v_c|^2) with its hand-worked weights."""
+    inp = _tiny_attn_inputs(11, 1, 0, gh=1, gw=1)
+    _, _, _, _, rms = _attn(inp, [1], 1, mode=1, split=(64, 0, 0), want_rms=True)
+    assert np.allclose(rms, np.linalg.norm(inp["v_cur"][0].astype(np.float64), axis=-1), rtol=1e-13)
+
+    blocks = [1, 2]
+    inp = _tiny_attn_inputs(12, 3, 2, scale=0.0)
+    _, _, heads, rows, rms = _attn(inp, blocks, 0, want_rms=True)
+    T = inp["T"]
+    vh, vc = inp["v_hist"].astype(np.float64), inp["v_cur"].astype(np.float64)
+    for n, (h, i) in enumerate(zip(heads, rows)):
+        vis = np.concatenate([vh[:, h], vc[: (1 if i < T else 3) * T, h]])
+        want = math.sqrt((vis ** 2).sum()) / len(vis)
+        assert abs(rms[n] - want) <= 1e-13 * want
+
+    q = np.array([[[0.5, -1.0]]], np.float32)
+    kc = np.array([[[1.0, 2.0]]], np.float32)
+    vc = np.array([[[3.0, -1.0]]], np.float32)
+    kh = np.array([[[-0.5, 1.5]]], np.float32)
+    vh = np.array([[[0.25, 4.0]]], np.float32)
+    _, _, _, _, rms = O.attention(q, kc, vc, kh, vh, [0], [0], [1], [0], [1], 1, 1, (2, 0, 0), 1,
+                                  want_rms=True)
+    c, s_ = math.cos(1.0), math.sin(1.0)
+    rq = (0.5 * c + 1.0 * s_, 0.5 * s_ - 1.0 * c)
+    s_h = (rq[0] * -0.5 + rq[1] * 1.5) / math.sqrt(2)
+    s_c = (0.5 * 1.0 + -1.0 * 2.0) / math.sqrt(2)
+    eh, ec = math.exp(s_h), math.exp(s_c)
+    wh, wc = eh / (eh + ec), ec / (eh + ec)
+    want = math.sqrt(wh ** 2 * (0.25 ** 2 + 4.0 ** 2) + wc ** 2 * (3.0 ** 2 + 1.0))
+    assert abs(rms[0] - want) < 1e-14 * want
+
+
+def test_attention_rms_does_not_change_o_or_lse():
+    inp = _tiny_attn_inputs(16, 2, 2)
+    o1, l1, _, _ = _attn(inp, [1, 1], 1)
+    o2, l2, _, _, _ = _attn(inp, [1, 1], 1, want_rms=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
