@@ -44,10 +44,12 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per head in the sample")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="run one device copy of MIB MiB first (reference for HBM byte counters)")
-    p.add_argument("--cold", type=int, default=0, metavar="STEPS",
+    p.add_argument("--cold", type=int, default=5, metavar="STEPS",
                    help="after the timed steps, run STEPS more with a 512 MiB write before each "
                         "RoPE, append and compress call (last-level cache flushed) and report "
-                        "those calls' times as 'cold'")
+                        "those calls' times as 'cold' (0: skip)")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured ceilings (matrix-core loop, streaming copies)")
     return p.parse_args()
 
 
@@ -211,8 +213,11 @@ def main():
     peak = PEAK[op]
     # algorithmic bytes of the streaming kernels (per step)
     hist_k = n_hist * (fe * (kvb + ob) + sb)         # stored K read, rotated operand written
-    hist_v = n_hist * (fe * (kvb + ob) + sb) if dt == "fp8" else 0   # V dequantised
-    rope_bytes = hist_k + hist_v + 3 * B * fe * 2 * ob
+    # the block: q, k, v read; qrot, krot written in the operand dtype, v in the kv dtype
+    cur = B * (fe * (5 * ob + kvb) + sb)
+    # FP8: every key's V scale read, its three attention-order terms written
+    vstage = Lk * H * 16 if dt == "fp8" else 0
+    rope_bytes = hist_k + cur + vstage
     append_bytes = 2 * B * (fe * (ob + kvb) + sb)
     slots_per_step = B / w["ratio"]
     compress_bytes = slots_per_step * 2 * (fe * kvb + sb) * (w["ratio"] + 1)
@@ -262,6 +267,13 @@ def main():
                      "algorithmic_per_launch": f"{attn_flop:.4e} flop = 4*Lq*Lk*D*H"},
         "cpu_baseline": None,
     }
+    if dt == "fp8":
+        # QK^T runs on bf16 matrix cores and PV on fp8 ones: half the flops at each rate
+        mixed = 1.0 / (0.5 / PEAK["bf16"] + 0.5 / PEAK["fp8"])
+        rec["attn_vs_peaks"] = {"bf16": round(attn_tflops / PEAK["bf16"], 4),
+                                "fp8": round(attn_tflops / PEAK["fp8"], 4),
+                                "qk_bf16_pv_fp8": round(attn_tflops / mixed, 4),
+                                "qk_bf16_pv_fp8_peak_tflops": round(mixed, 1)}
 
     if args.cold:
         # the streaming calls with their inputs out of the last-level cache: a 512 MiB write
@@ -298,10 +310,50 @@ def main():
                                "kv_ring_append": round(append_bytes / (cm[1] * 1e-3) / 1e9, 1),
                                "convkv_compress": round(compress_bytes / (cm[2] * 1e-3) / 1e9, 1)}}
         del scratch
+    stream_bytes = {"rope_reset_apply": rope_bytes, "kv_ring_append": append_bytes,
+                    "convkv_compress": compress_bytes}
+    if not args.no_ceilings:
+        rec["ceilings"], rec["stream"] = ceilings(stream_bytes, rec, w)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["parity"] = cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool,
                                                           i, wk, bk, wv, bv)
     print(json.dumps(rec), flush=True)
+
+
+def ceilings(stream_bytes, rec, w):
+    """Measured ceilings (microbench/: a matrix-core loop per dtype and streaming copies with
+    each streaming kernel's read:write mix and bytes, hot and with the last-level cache
+    flushed), and each streaming kernel against the 8 TB/s peak and its copy ceiling."""
+    import torch
+    import microbench as MB
+    r = w["ratio"]
+    out = {"mfma_loop_tflops": {"bf16": round(MB.mfma_tflops(torch, False), 1),
+                                "fp8": round(MB.mfma_tflops(torch, True), 1)},
+           "read_only_gbs": {"bytes": 1 << 30,
+                             "hot": round(MB.copy_gbs(torch, 1 << 30, 0, cold=False), 1),
+                             "cold": round(MB.copy_gbs(torch, 1 << 30, 0, cold=True), 1)},
+           "copy_gbs": {}}
+    mix = {"rope_reset_apply": 1, "kv_ring_append": 1, "convkv_compress": r}
+    ours = {}
+    for name, total in stream_bytes.items():
+        k = mix[name]
+        write = int(total / (k + 1))
+        read = k * write
+        if k != 1 and k != 5:
+            continue
+        hot = MB.copy_gbs(torch, read, write, cold=False)
+        cold = MB.copy_gbs(torch, read, write, cold=True)
+        out["copy_gbs"][name] = {"read_bytes": read, "write_bytes": write, "mix": f"{k}:1",
+                                 "hot": round(hot, 1), "cold": round(cold, 1)}
+        got = rec["stream_gbs"][name]
+        ent = {"gbs": got, "frac_hbm_peak": round(got / HBM_PEAK_GBS, 3),
+               "frac_copy_hot": round(got / hot, 3)}
+        if "cold" in rec:
+            gc = rec["cold"]["gbs"][name]
+            ent.update({"cold_gbs": gc, "cold_frac_hbm_peak": round(gc / HBM_PEAK_GBS, 3),
+                        "cold_frac_copy_cold": round(gc / cold, 3)})
+        ours[name] = ent
+    return out, ours
 
 
 def train_main(args, w):
@@ -548,12 +600,46 @@ def _cpu_model():
     return "unknown"
 
 
+def _tiny_full():
+    """The oracle on the tiny workload, whole: 27 history blocks and 20 AR steps, every
+    step's attention on every row, append and compress.  Returns (seconds, steps)."""
+    import synth
+    from oracle.stream import OracleCache
+    w = synth.workload("tiny_f32")
+    T, H, D = w["tokens"], w["heads"], w["head_dim"]
+    wk, bk = synth.conv_weights(w, 0, synth.TENSOR_WK)
+    wv, bv = synth.conv_weights(w, 0, synth.TENSOR_WV)
+    oc = OracleCache(w)
+    steps = w["history_blocks"] + w["steps"]
+    t0 = time.perf_counter()
+    f = 0
+    for _ in range(steps):
+        ids = list(range(f, f + 2))
+        q, k, v = (synth.frames(w, 0, t, ids).reshape(2 * T, H, D)
+                   for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V))
+        oc.attention(q, k, v, threads=1)
+        oc.append(k.reshape(2, -1), v.reshape(2, -1))
+        oc.compress(wk, bk, wv, bv)
+        f += 2
+    return time.perf_counter() - t0, steps
+
+
 def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv, bv):
-    """The oracle, as it stands, on a bounded sample of the same steady-state step: the
-    attention of every head for a few query rows over the full key set (history rebuilt
-    by the oracle's own compressor from the same frames), extrapolated to the whole step."""
+    """The oracle, as it stands, on a bounded sample of the same steady-state step, every
+    part of the step timed (the plan of the CPU baseline: full where it is small,
+    row-sampled attention extrapolated and labelled as such):
+      attention   all heads x args.cpu_rows query rows over the full key set, all cores
+                  and (on a sixteenth of that sample) one thread; extrapolated by rows;
+      RoPE        the oracle's rotation of the step's history keys and block Q, K (timed
+                  on the block's Q, scaled by the frame count);
+      append      the oracle's storage of the block's K and V (bf16 rounding or FP8 rows);
+      compress    the oracle's compression of one group of 5 frames (K and V), times the
+                  groups of an average step (B / r);
+      bookkeeping 1000 steps of the oracle's planner, per step;
+    plus, reported beside, the tiny workload run whole and the 80 -> 16 memory build."""
     import oracle as O
     import synth
+    from oracle.bookkeeping import Bookkeeping
     from oracle.stream import OracleCache
     T, H, D = w["tokens"], w["heads"], w["head_dim"]
     io_bf16 = w["q_dtype"] == 1
@@ -580,20 +666,23 @@ def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv,
         v = np_pool[blk % len(pool)][2][f % B]
         oc.raw[f] = (oc._store(k), oc._store(v))
     oc.bk.F = st["F"]
-    groups = []
-    while len(groups) < st["mem_len"]:
-        # compress the groups present in memory (each from its own 5 frames)
-        groups.append(oc.bk.G)
+    r = w["ratio"]
+    group_s = []
+    while len(group_s) < st["mem_len"]:
+        # compress the groups present in memory (each from its own r frames), timed per group
         g = oc.bk.G
-        r = w["ratio"]
+        tg = time.perf_counter()
         xk = np.stack([oc._f32(oc.raw[r * g + k][0]) for k in range(r)])
         xv = np.stack([oc._f32(oc.raw[r * g + k][1]) for k in range(r)])
         oc.mem[g % w["mem_slots"]] = (g, oc._store(O.compress_chain_f32(xk, wk, bk)),
                                       oc._store(O.compress_chain_f32(xv, wv, bv)))
+        group_s.append(time.perf_counter() - tg)
         oc.bk.G += 1
     setup_s = time.perf_counter() - t_setup
     assert oc.bk.E == E and len(oc.keys(0)) == n_hist
     q, k, v = (np_pool[(next_step) % len(pool)][j].reshape(B * T, H, D) for j in range(3))
+
+    # attention, row-sampled
     rows = np.linspace(0, Lq - 1, args.cpu_rows).astype(np.int64)
     heads = np.repeat(np.arange(H, dtype=np.int32), len(rows))
     rr = np.tile(rows, H)
@@ -602,13 +691,39 @@ def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv,
     O_ref = oc.attention(q, k, v, sel=(heads, rr), threads=threads)[0]
     secs = time.perf_counter() - t0
     frac = len(rr) / float(H * Lq)
-    full = secs / frac
-    # one thread on a sixteenth of the sample (the same rows of every 16th head)
-    few = np.arange(0, len(rr), 16)
+    attn_full = secs / frac
+    few = np.arange(0, len(rr), 16)          # one thread on the same rows of every 16th head
     t1 = time.perf_counter()
     oc.attention(q, k, v, sel=(heads[few], rr[few]), threads=1)
     secs1 = time.perf_counter() - t1
-    full1 = secs1 / (len(few) / float(H * Lq))
+    attn_full1 = secs1 / (len(few) / float(H * Lq))
+
+    # RoPE: the block's Q (B frames) rotated at its reset positions, scaled to the step's
+    # n_hist + 2 B rotated frames
+    t_pos = np.repeat(np.arange(B, dtype=np.int32) + n_hist, T)
+    u_pos = np.tile(np.arange(T, dtype=np.int32), B)
+    t2 = time.perf_counter()
+    O.rope_rotate(q, t_pos, u_pos, w["rope_mode"], w["rope_split"], T, w["grid_w"], w["rope_theta"])
+    rope_s = (time.perf_counter() - t2) * (n_hist + 2 * B) / B
+    # append: storing the block's K and V
+    t3 = time.perf_counter()
+    for i in range(B):
+        oc._store(k.reshape(B, -1)[i])
+        oc._store(v.reshape(B, -1)[i])
+    append_s = time.perf_counter() - t3
+    compress_s = float(np.mean(group_s)) * B / r
+    # bookkeeping: the planner over 1000 steps
+    bkp = Bookkeeping(w["window_frames"], w["mem_slots"], r, B, w.get("ref_frames", 0))
+    t4 = time.perf_counter()
+    for _ in range(1000):
+        bkp.keys(B)
+        bkp.append(B)
+        bkp.compress()
+    book_s = (time.perf_counter() - t4) / 1000
+    tiny_s, tiny_steps = _tiny_full()
+    step_s = attn_full + rope_s + append_s + compress_s + book_s
+    step_s1 = attn_full1 + rope_s + append_s + compress_s + book_s
+
     # The timed configuration's own output for that step (RoPE + attention on the device,
     # after the timed region) on the same rows, against the oracle's.
     cache.rope_reset_apply(*pool[next_step % len(pool)])
@@ -620,13 +735,24 @@ def cpu_baseline(w, args, n_hist, B, Lq, Lk, cache, pool, next_step, wk, bk, wv,
     parity = {"rel_l2": float(f"{err:.3e}"), "bar": bar, "ok": err <= bar,
               "rows": f"all {H} heads x {len(rows)} query rows of the next steady-state step, "
                       "attention output against the oracle"}
-    return {"value": round(B / full, 6), "unit": "latent frames/s (one layer, one diffusion step)",
+    return {"value": round(B / step_s, 6), "unit": "latent frames/s (one layer, one diffusion step)",
             "cores": threads, "kind": "oracle", "cpu_model": _cpu_model(),
-            "value_1_thread": round(B / full1, 6),
+            "value_1_thread": round(B / step_s1, 6),
+            "step_seconds": {"attention_extrapolated": round(attn_full, 2),
+                             "attention_extrapolated_1_thread": round(attn_full1, 2),
+                             "rope": round(rope_s, 3), "append": round(append_s, 3),
+                             "compress": round(compress_s, 3), "bookkeeping": round(book_s, 6)},
+            "tiny_full": {"steps": tiny_steps, "seconds": round(tiny_s, 2),
+                          "steps_per_s_1_thread": round(tiny_steps / tiny_s, 2)},
+            "memory_build_80_to_16_seconds": round(float(np.sum(group_s)), 2),
             "sample": (f"attention of all {H} heads x {len(rows)} query rows over Lk={Lk} keys "
-                       f"({secs:.1f} s, double precision), extrapolated x{1 / frac:.0f} to the "
-                       f"full step; history built by the oracle's compressor in {setup_s:.1f} s "
-                       "(not counted); rope/append/compress not counted")}, parity
+                       f"({secs:.1f} s on {threads} threads, double precision), extrapolated "
+                       f"x{1 / frac:.0f} by rows to the full step; one thread on a sixteenth of "
+                       f"those rows ({secs1:.1f} s); RoPE ({rope_s:.2f} s), append "
+                       f"({append_s:.2f} s), compress ({compress_s:.2f} s for {B / r:.1f} groups) "
+                       "and bookkeeping timed on the oracle's single-threaded routines and "
+                       "added; memory of 16 slots built in "
+                       f"{setup_s:.1f} s before timing")}, parity
 
 
 if __name__ == "__main__":
