@@ -366,7 +366,7 @@ struct Ctx {
   int sread;          // 1/s_v of the lane's probabilities' keys (S_RING + hi * 64)
   int lread[2];       // log2(s_v) pair of the A-operand key row of key block kb
   const char* vsbase; // the copy source of this lane: 1/s_v (lanes 0-7) or log2 pairs
-                      // (lanes 8-15) of this head, attention order
+                      // (lanes 8-15) of this head, attention order, at key lane & 7
   float thr;          // raise threshold 448 * 2^-E_h on a lane's 32-key sum of P'
   int thr_exp;        // frexp exponent of thr
   bf16x8_t augb;      // B operand of the log2(s_v) step
@@ -412,10 +412,13 @@ __device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
     // scale terms of keys 8 wave .. 8 wave + 7 of the tile: lanes 0-7 1/s_v, lanes 8-15
     // the log2 pairs (keys past the end repeat the last one)
     if (c.lane < 16) {
-      int key = t * BN + c.wave * 8 + (c.lane & 7);
-      key = key < a.Lk ? key : a.Lk - 1;
-      copy_dword_to_lds(c.vsbase + (int64_t)key * 4,
-                        c.lds_u32 + S_RING + slot * S_TILE + (unsigned)c.wave * 64);
+      const int key0 = t * BN + c.wave * 8;   // wave-uniform; c.vsbase holds lane & 7
+      const char* src = c.vsbase + (int64_t)key0 * 4;
+      if (key0 + 8 > a.Lk) {
+        const int key = key0 + (c.lane & 7) < a.Lk ? key0 + (c.lane & 7) : a.Lk - 1;
+        src = c.vsbase + (int64_t)(key - (c.lane & 7)) * 4;
+      }
+      copy_dword_to_lds(src, c.lds_u32 + S_RING + slot * S_TILE + (unsigned)c.wave * 64);
     }
   } else if (st.u0 + BN <= a.T) {  // the whole tile lies in frame f0
 #pragma unroll
@@ -598,19 +601,20 @@ __device__ __forceinline__ void pv_tile_bf16(const Ctx& c, const char* vb, const
 // rounded to e4m3 (the raise keeps it <= 448), against the stored e4m3 codes: 4 MFMAs of
 // 32 channels x 64 keys on v_mfma_f32_32x32x64_f8f6f4 (unit block scales).  The lane's 32
 // values are keys 16 ch + 8 hi + t (ch < 4, t < 8), the B operand's byte 8 ch + t.
+// pt: the previous tile's P~ registers, whose old contents the conversions merge into
+// (both halves of every word are written, so nothing has to be cleared first).
 __device__ __forceinline__ void pv_tile_f8(const Ctx& c, const char* vb, const f32x16_t (&s)[2],
-                                           f32x16_t (&o)[4]) {
+                                           f32x16_t (&o)[4], v8i32& pt) {
   v8i32 vf[2];
   vf[0] = vfrag8(vb, c, 0);
   vf[1] = vfrag8(vb, c, 1);
-  v8i32 pt;
 #pragma unroll
   for (int ch = 0; ch < 4; ++ch) {
     const f32x16_t& sk = s[ch >> 1];
     const int b0 = 8 * (ch & 1);
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 0], sk[b0 + 1], 0, false);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 0], sk[b0 + 1], pt[2 * ch], false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 2], sk[b0 + 3], w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 4], sk[b0 + 5], 0, false);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 4], sk[b0 + 5], pt[2 * ch + 1], false);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 6], sk[b0 + 7], w1, true);
     pt[2 * ch] = w0;
     pt[2 * ch + 1] = w1;
@@ -641,7 +645,8 @@ __device__ __forceinline__ void pv_tile_f8(const Ctx& c, const char* vb, const f
 // exact pass.
 template <bool F8, bool MASK, bool FIRST, int SLOT>
 __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&o)[4],
-                                     float& m_ref, f32x16_t& negm, float& l_part, Stream& st) {
+                                     float& m_ref, f32x16_t& negm, float& l_part, Stream& st,
+                                     v8i32& pt) {
   // K slot base; V^T reads add vread / vread8 (which hold V_RING) to their slot's base
   const char* vb = c.lds + slot_of<SLOT>(j) * (F8 ? V8_TILE : TILE_BYTES);
   issue<F8>(c, j + NS - 1, st);
@@ -690,7 +695,7 @@ __device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8
   }
   l_part += sum;
   if (F8) {
-    pv_tile_f8(c, vb, s, o);
+    pv_tile_f8(c, vb, s, o, pt);
   } else {
     pv_tile_bf16(c, vb, s, o);
   }
@@ -786,7 +791,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
       c.lread[kb] = S_RING + (key >> 3) * 64 + 32 + (key & 7) * 4;
     }
     c.vsbase = reinterpret_cast<const char*>(a.vscale + (c.lane < 8 ? 1 : 2) * a.vs_plane +
-                                             (int64_t)h * a.vs_head_stride);
+                                             (int64_t)h * a.vs_head_stride + (c.lane & 7));
     float smax = 0.0f;
 #pragma unroll
     for (int p = 0; p < kVmaxParts; ++p) smax = fmaxf(smax, a.vmax[h * kVmaxParts + p]);
@@ -818,26 +823,27 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
   float m_ref = 0.0f, l_part = 0.0f;
   f32x16_t negm = f32x16_t{};  // -m_ref in every element (the QK^T chains' starting value)
+  v8i32 pt = v8i32{};          // FP8: the last tile's e4m3 P~
   Stream st{0, 0, frame_base(c.g, 0), frame_base(c.g, 1)};
   for (int t = 0; t < NS - 1; ++t) issue<F8>(c, t, st);
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile 0 landed
   __syncthreads();
 
   if (n_free > 0)
-    tile<F8, false, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st);
+    tile<F8, false, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st, pt);
   else
-    tile<F8, true, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st);
+    tile<F8, true, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st, pt);
   int j = 1;
   const int free_end = n_free < nt ? n_free : nt;
   static_assert(NS == 4, "the unrolled loop below walks the slots 1, 2, 3, 0");
   for (; j + 4 <= free_end; j += 4) {
-    tile<F8, false, false, 1>(c, j, qf, o, m_ref, negm, l_part, st);
-    tile<F8, false, false, 2>(c, j + 1, qf, o, m_ref, negm, l_part, st);
-    tile<F8, false, false, 3>(c, j + 2, qf, o, m_ref, negm, l_part, st);
-    tile<F8, false, false, 0>(c, j + 3, qf, o, m_ref, negm, l_part, st);
+    tile<F8, false, false, 1>(c, j, qf, o, m_ref, negm, l_part, st, pt);
+    tile<F8, false, false, 2>(c, j + 1, qf, o, m_ref, negm, l_part, st, pt);
+    tile<F8, false, false, 3>(c, j + 2, qf, o, m_ref, negm, l_part, st, pt);
+    tile<F8, false, false, 0>(c, j + 3, qf, o, m_ref, negm, l_part, st, pt);
   }
-  for (; j < free_end; ++j) tile<F8, false, false, -1>(c, j, qf, o, m_ref, negm, l_part, st);
-  for (; j < nt; ++j) tile<F8, true, false, -1>(c, j, qf, o, m_ref, negm, l_part, st);
+  for (; j < free_end; ++j) tile<F8, false, false, -1>(c, j, qf, o, m_ref, negm, l_part, st, pt);
+  for (; j < nt; ++j) tile<F8, true, false, -1>(c, j, qf, o, m_ref, negm, l_part, st, pt);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
 
   const float l = l_part + __shfl_xor(l_part, 32);

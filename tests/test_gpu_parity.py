@@ -291,6 +291,31 @@ def test_fp8_append_compress_bitexact():
     assert_ring_bitexact(run)
 
 
+@pytest.mark.parametrize("kv,ratio", [(BF16, 3), (BF16, 4), (FP8, 3), (FP8, 4)],
+                         ids=["bf16_r3", "bf16_r4", "fp8_r3", "fp8_r4"])
+def test_other_ratio_compress_bitexact(kv, ratio):
+    """Ratios other than 5 take the generic compressor (any r, tokens one after another):
+    over a stream whose memory wraps, every memory slot and ring frame (FP8: codes and
+    scales) bit-exact against the oracle, the bookkeeping every step, and attention
+    parity at the end."""
+    name = "fp8_kv" if kv == FP8 else "s512_bf16"
+    w = synth.workload(name, heads=8, grid_h=16, grid_w=16, window_frames=4, mem_slots=4,
+                       max_block_frames=4, ratio=ratio)
+    run = Runner(w)
+    for s_ in range(14):
+        run.step(4 if s_ % 3 else 3, attend=False)
+        assert_state_matches(run)
+    assert run.oc.bk.G > w["mem_slots"]
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    sel = sample_rows(w, 4, seed=5, per_head=16)
+    res = run.step(4, sel=sel)
+    err, dl = run.compare_attention(res)
+    say(f"ratio {ratio} {name}: rel L2 {err:.3e}, worst head {res['worst_head']:.3e}")
+    assert err <= ATTN_TOL[kv]
+    assert_lse(run, res, kv)
+
+
 def test_fp8_kv_step_parity():
     """512x512-shaped FP8 KV cache with 1% x8 outliers: first step (no history) and the
     step after 11 warm-up blocks, attention over the stored e4m3 history against the oracle
