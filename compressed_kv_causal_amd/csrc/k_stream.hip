@@ -234,29 +234,32 @@ __global__ __launch_bounds__(256) void k_rope_table(const RopeTableArgs a) {
   a.table[i] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-// Rotates the 4 pairs of one lane (channels 8*li .. 8*li+7) at temporal position t.
-__device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32_t u, int li,
-                                             float* x) {
+// cos/sin of the 4 pairs of one lane (channels 8*li .. 8*li+7) at temporal position t of
+// token u, whose grid row and column are gr and gc (3D mode; all three are wave-uniform, so
+// the table index is a select and an add per pair, with no division).
+__device__ __forceinline__ void rope_cs(const RopeArgs& a, int32_t t, int32_t u, int32_t gr, int32_t gc,
+                                        int li, float2* cs) {
+  const int32_t ht = a.split_t / 2, hh = a.split_h / 2, hw = a.split_w / 2;
+  const int32_t base_t = t * ht;
+  const int32_t base_r = a.key_frames_max * ht + gr * hh - ht;
+  const int32_t base_c = a.key_frames_max * ht + a.grid_h * hh + gc * hw - ht - hh;
+  const int64_t base_1d = ((int64_t)t * a.T + u) * (a.D / 2);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int32_t pair = li * 4 + p;
-    float2 cs;
-    if (a.rope_mode == 1) {
-      cs = a.table[((int64_t)t * a.T + u) * (a.D / 2) + pair];
-    } else {
-      const int32_t ht = a.split_t / 2, hh = a.split_h / 2, hw = a.split_w / 2;
-      if (pair < ht) {
-        cs = a.table[t * ht + pair];
-      } else if (pair < ht + hh) {
-        cs = a.table[a.key_frames_max * ht + (u / a.grid_w) * hh + (pair - ht)];
-      } else {
-        cs = a.table[a.key_frames_max * ht + a.grid_h * hh + (u % a.grid_w) * hw +
-                     (pair - ht - hh)];
-      }
-    }
+    if (a.rope_mode == 1)
+      cs[p] = a.table[base_1d + pair];
+    else
+      cs[p] = a.table[(pair < ht ? base_t : (pair < ht + hh ? base_r : base_c)) + pair];
+  }
+}
+
+__device__ __forceinline__ void rope_rotate8(const float2* cs, float* x) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
     const float x0 = x[2 * p], x1 = x[2 * p + 1];
-    x[2 * p] = x0 * cs.x - x1 * cs.y;
-    x[2 * p + 1] = x0 * cs.y + x1 * cs.x;
+    x[2 * p] = x0 * cs[p].x - x1 * cs[p].y;
+    x[2 * p + 1] = x0 * cs[p].y + x1 * cs[p].x;
   }
 }
 
@@ -268,51 +271,63 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& a, int32_t t, int32
 // dtype (in_dtype); an FP8 cache's keys are read as code * row scale.  An FP8 cache's
 // attention reads V as stored (codes), so the pass leaves history V alone and quantises
 // the block's V like the cache stores it (codes to vcur, row scales to vcur_scale).
+//
+// Work split: blockIdx.x = token u, so u and its grid coordinates are scalars; the
+// workgroup's lanes cover the token's H x D/8 chunks (LPR consecutive lanes per head, a
+// wave reads 64 x 16 B contiguous).  A block frame's Q, K and V loads are issued before
+// its stores (which the compiler must otherwise assume may alias them).
 template <int LPR>
-__global__ __launch_bounds__(256) void k_rope(const RopeArgs a) {
-  const int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+__global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
+  const int32_t u = blockIdx.x;
   const int32_t rows = a.T * a.H;
-  const int32_t row = e / LPR, li = e % LPR;              // row = u * H + h inside the frame
-  if (row >= rows) return;
-  const int32_t u = row / a.H, h = row - u * a.H;
   const int32_t n_hist = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   const int32_t fi = blockIdx.y + (a.hist_rows ? 0 : n_hist);
+  const int32_t gr = a.rope_mode == 1 ? 0 : u / a.grid_w;
+  const int32_t gc = a.rope_mode == 1 ? 0 : u - gr * a.grid_w;
   const int64_t KFT = (int64_t)a.key_frames_max * a.T;
   const int64_t QT = (int64_t)a.block_frames_max * a.T;
   const int64_t D = a.D;
   const bool fp8 = a.kv_dtype == DT_FP8;
-  float x[8];
   if (fi < n_hist) {
     int32_t slot;
     const int32_t src = hist_src(a.hist, fi, &slot);
-    const int64_t srow = (int64_t)slot * rows + row;
     const void* ksrc = src == SRC_REF ? a.ref_k : (src == SRC_MEM ? a.mem_k : a.ring_k);
     const float* kscale = src == SRC_REF ? a.ref_k_scale : (src == SRC_MEM ? a.mem_k_scale : a.ring_k_scale);
-    const float sc = fp8 ? kscale[srow] : 1.0f;
-    load8_kv(ksrc, a.kv_dtype, srow * D + li * 8, sc, x);
-    rope_rotate8(a, fi, u, li, x);
-    const int64_t drow = h * KFT + (int64_t)fi * a.T + u;
-    store8_op(a.krot, a.in_dtype, drow * D + li * 8, x);
+    for (int32_t e = threadIdx.x; e < a.H * LPR; e += blockDim.x) {
+      const int32_t h = e / LPR, li = e % LPR;
+      const int64_t srow = (int64_t)slot * rows + (int64_t)u * a.H + h;
+      const float sc = fp8 ? kscale[srow] : 1.0f;
+      float x[8];
+      float2 cs[4];
+      load8_kv(ksrc, a.kv_dtype, srow * D + li * 8, sc, x);
+      rope_cs(a, fi, u, gr, gc, li, cs);
+      rope_rotate8(cs, x);
+      store8_op(a.krot, a.in_dtype, (h * KFT + (int64_t)fi * a.T + u) * D + li * 8, x);
+    }
     return;
   }
   const int32_t i = fi - n_hist;                           // frame inside the block
-  const int64_t crow = (int64_t)i * rows + row;            // row of the block's [n*T][H][D]
-  load8_in(a.q, a.in_dtype, crow * D + li * 8, x);
-  rope_rotate8(a, fi, u, li, x);
+  for (int32_t e = threadIdx.x; e < a.H * LPR; e += blockDim.x) {
+    const int32_t h = e / LPR, li = e % LPR;
+    const int64_t crow = (int64_t)i * rows + (int64_t)u * a.H + h;  // block [n*T][H][D]
+    float xq[8], xk[8], xv[8];
+    float2 cs[4];
+    load8_in(a.q, a.in_dtype, crow * D + li * 8, xq);
+    load8_in(a.k_cur, a.in_dtype, crow * D + li * 8, xk);
+    load8_in(a.v_cur, a.in_dtype, crow * D + li * 8, xv);
+    rope_cs(a, fi, u, gr, gc, li, cs);
+    rope_rotate8(cs, xq);
 #pragma unroll
-  for (int e2 = 0; e2 < 8; ++e2) x[e2] *= a.q_scale;
-  store8_op(a.qrot, a.in_dtype, (h * QT + (int64_t)i * a.T + u) * D + li * 8, x);
-
-  load8_in(a.k_cur, a.in_dtype, crow * D + li * 8, x);
-  rope_rotate8(a, fi, u, li, x);
-  store8_op(a.krot, a.in_dtype, (h * KFT + (int64_t)fi * a.T + u) * D + li * 8, x);
-
-  load8_in(a.v_cur, a.in_dtype, crow * D + li * 8, x);
-  if (fp8) {
-    const float sc = store8_kv<LPR>(a.vcur, DT_FP8, crow * D + li * 8, x);
-    if (li == 0) a.vcur_scale[crow] = sc;
-  } else {
-    store8_op(a.vcur, a.in_dtype, crow * D + li * 8, x);
+    for (int e2 = 0; e2 < 8; ++e2) xq[e2] *= a.q_scale;
+    store8_op(a.qrot, a.in_dtype, (h * QT + (int64_t)i * a.T + u) * D + li * 8, xq);
+    rope_rotate8(cs, xk);
+    store8_op(a.krot, a.in_dtype, (h * KFT + (int64_t)fi * a.T + u) * D + li * 8, xk);
+    if (fp8) {
+      const float sc = store8_kv<LPR>(a.vcur, DT_FP8, crow * D + li * 8, xv);
+      if (li == 0) a.vcur_scale[crow] = sc;
+    } else {
+      store8_op(a.vcur, a.in_dtype, crow * D + li * 8, xv);
+    }
   }
 }
 
@@ -422,12 +437,15 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
   const int32_t n_hist = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   const int32_t frames = (a.hist_rows ? n_hist : 0) + a.n_cur;
   if (frames <= 0) return hipSuccess;
-  const int lpr = a.D / 8;
-  dim3 grid(blocks_for((int64_t)a.T * a.H * lpr), frames);
+  // one workgroup per token: H x D/8 lanes, rounded up to whole waves (at most 1024; more
+  // heads loop)
+  const int64_t lanes = (int64_t)a.H * (a.D / 8);
+  const int threads = lanes >= 1024 ? 1024 : (int)((lanes + 63) / 64 * 64);
+  dim3 grid(a.T, frames);
   if (a.D == 128)
-    hipLaunchKernelGGL(k_rope<16>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rope<16>, grid, dim3(threads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_rope<8>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rope<8>, grid, dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
