@@ -321,14 +321,18 @@ def main():
 
 
 def ceilings(stream_bytes, rec, w):
-    """Measured ceilings (microbench/: a matrix-core loop per dtype and streaming copies with
-    each streaming kernel's read:write mix and bytes, hot and with the last-level cache
-    flushed), and each streaming kernel against the 8 TB/s peak and its copy ceiling."""
+    """Measured ceilings (microbench/: a matrix-core loop per dtype, the bf16 loop fed from
+    LDS, the softmax's exponentials beside MFMAs, and streaming copies with each streaming
+    kernel's read:write mix and bytes, hot and with the last-level cache flushed), and each
+    streaming kernel against the 8 TB/s peak and its copy ceiling."""
     import torch
     import microbench as MB
     r = w["ratio"]
     out = {"mfma_loop_tflops": {"bf16": round(MB.mfma_tflops(torch, False), 1),
                                 "fp8": round(MB.mfma_tflops(torch, True), 1)},
+           "mfma_lds_tflops": {"ds_read_b128": round(MB.mfma_lds_tflops(torch, False), 1),
+                               "ds_read_b64_tr_b16": round(MB.mfma_lds_tflops(torch, True), 1)},
+           "softmax_overlap_ms": MB.overlap_ms(torch),
            "read_only_gbs": {"bytes": 1 << 30,
                              "hot": round(MB.copy_gbs(torch, 1 << 30, 0, cold=False), 1),
                              "cold": round(MB.copy_gbs(torch, 1 << 30, 0, cold=True), 1)},

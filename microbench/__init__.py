@@ -36,7 +36,9 @@ def lib():
         L.mb_copy.argtypes = [vp, vp, i64, vp]
         L.mb_copy5.argtypes = [vp, vp, i64, vp]
         L.mb_read.argtypes = [vp, i64, vp, vp]
-        for f in (L.mb_mfma_loop, L.mb_copy, L.mb_copy5, L.mb_read):
+        L.mb_mfma_lds.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.mb_overlap.argtypes = [i32, i32, i32, vp, vp, vp]
+        for f in (L.mb_mfma_loop, L.mb_copy, L.mb_copy5, L.mb_read, L.mb_mfma_lds, L.mb_overlap):
             f.restype = i32
         _lib = L
     return _lib
@@ -80,6 +82,41 @@ def mfma_tflops(torch, fp8, cus=256, iters=4096, reps=5):
     flop_per = 2.0 * 32 * 32 * (64 if fp8 else 16)
     flops = cus * 8 * iters * 4 * flop_per
     return flops / (ms * 1e-3) / 1e12
+
+
+def mfma_lds_tflops(torch, transposed, cus=256, iters=512, reps=5):
+    """bf16 MFMA rate with every A operand read from LDS (1 KiB per MFMA), 2 waves per SIMD:
+    ds_read_b128 fragments, or (transposed) pairs of ds_read_b64_tr_b16."""
+    dev = torch.device("cuda")
+    seed = torch.rand(64, device=dev)
+    sink = torch.zeros(cus, device=dev)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        _check(lib().mb_mfma_lds(int(transposed), cus, iters, ctypes.c_void_p(seed.data_ptr()),
+                                 ctypes.c_void_p(sink.data_ptr()), s), "mb_mfma_lds")
+    run()
+    ms = _timed(torch, run, reps)
+    flops = cus * 8 * iters * 16 * 2.0 * 32 * 32 * 16
+    return flops / (ms * 1e-3) / 1e12
+
+
+def overlap_ms(torch, cus=256, iters=4096, reps=5):
+    """Times (ms) of an MFMA stream and of the softmax's exponentials with their sums (one
+    exp2 and one add per MFMA): each alone, in two waves sharing a SIMD, and interleaved in
+    one wave."""
+    dev = torch.device("cuda")
+    seed = torch.rand(64, device=dev)
+    sink = torch.zeros(cus, device=dev)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    for mode, name in enumerate(("mfma_alone", "exp_alone", "two_waves", "one_wave")):
+        def run():
+            _check(lib().mb_overlap(mode, cus, iters, ctypes.c_void_p(seed.data_ptr()),
+                                    ctypes.c_void_p(sink.data_ptr()), s), "mb_overlap")
+        run()
+        out[name] = round(_timed(torch, run, reps), 4)
+    return out
 
 
 def copy_gbs(torch, read_bytes, write_bytes, reps=7, cold=False):
