@@ -326,6 +326,7 @@ struct Geo {
   const char* v_ref;
   int64_t frame_bytes;  // one V frame, T * H * (bytes of a V row)
   int T, Lk, nf, ref_len, mem_end, nh, M, R, mem_slot0, ring_slot0;
+  int s_last;           // FP8: first key of the last 8-key group of the zero-padded scale rows
 };
 
 // V base address of key frame f of [reference | memory | window | block] (frames past
@@ -410,15 +411,11 @@ __device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
       copy_to_lds((st.u0 + c.vrow8 >= a.T ? vB : vA) + c.voff8, vdst);
     }
     // scale terms of keys 8 wave .. 8 wave + 7 of the tile: lanes 0-7 1/s_v, lanes 8-15
-    // the log2 pairs (keys past the end repeat the last one)
+    // the log2 pairs.  The planes are zero-padded to a multiple of 64 keys, so a tile's
+    // groups never need a bound check; tiles copied past the end re-read the last group.
     if (c.lane < 16) {
-      const int key0 = t * BN + c.wave * 8;   // wave-uniform; c.vsbase holds lane & 7
-      const char* src = c.vsbase + (int64_t)key0 * 4;
-      if (key0 + 8 > a.Lk) {
-        const int key = key0 + (c.lane & 7) < a.Lk ? key0 + (c.lane & 7) : a.Lk - 1;
-        src = c.vsbase + (int64_t)(key - (c.lane & 7)) * 4;
-      }
-      copy_dword_to_lds(src, c.lds_u32 + S_RING + slot * S_TILE + (unsigned)c.wave * 64);
+      const int key0 = min(t * BN + c.wave * 8, a.s_last);  // wave-uniform; vsbase has lane & 7
+      copy_dword_to_lds(c.vsbase + (int64_t)key0 * 4, c.lds_u32 + S_RING + slot * S_TILE + (unsigned)c.wave * 64);
     }
   } else if (st.u0 + BN <= a.T) {  // the whole tile lies in frame f0
 #pragma unroll
@@ -738,6 +735,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
   c.g.R = a.hist.R;
   c.g.mem_slot0 = a.hist.mem_slot0;
   c.g.ring_slot0 = a.hist.ring_slot0;
+  c.g.s_last = (a.Lk + BN - 1) / BN * BN - 8;
   c.h = h;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   c.lane = threadIdx.x & 63;

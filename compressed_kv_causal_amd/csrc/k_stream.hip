@@ -335,7 +335,9 @@ __global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
 // (h, p) takes the p-th of kVmaxParts slices of head h's keys, reads each key's row scale
 // where the cache keeps it (reference, memory or ring slot; the staged block) and writes
 // s_v, 1/s_v and the bf16 (hi, lo) split of log2(s_v), contiguous per head, and the
-// slice's largest s_v.  The attention scales its probabilities by 2^-E_h, 2^E_h the power
+// slice's largest s_v; the last slice's workgroup also writes each plane's zero pad from
+// Lk up to the next multiple of 64 (1/s_v = 0 and log2 = 0 there: those keys are masked,
+// their probabilities 0).  The attention scales its probabilities by 2^-E_h, 2^E_h the power
 // of two above the head's largest s_v, so that probability times s_v stays inside e4m3's
 // range, and adds the log2 pair to its scores.  An s_v below the smallest normal f32 (a
 // row of all but zero values) counts as that normal in the 1/s_v and log2 planes, where
@@ -346,8 +348,9 @@ __global__ __launch_bounds__(256) void k_vscale_stage(const VscaleArgs a) {
   const int32_t j0 = blockIdx.y * per;
   const int32_t j1 = j0 + per < a.Lk ? j0 + per : a.Lk;
   const int32_t nh = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
-  const int64_t P = (int64_t)a.H * a.key_frames_max * a.T;
-  float* s0 = a.vscale + (int64_t)h * a.key_frames_max * a.T;
+  const int64_t row = (int64_t)a.key_frames_max * a.T + kVscalePad;
+  const int64_t P = (int64_t)a.H * row;
+  float* s0 = a.vscale + (int64_t)h * row;
   float m = 0.0f;
   for (int32_t j = j0 + threadIdx.x; j < j1; j += 256) {
     const int32_t fi = j / a.T, u = j - fi * a.T;
@@ -368,6 +371,14 @@ __global__ __launch_bounds__(256) void k_vscale_stage(const VscaleArgs a) {
     s0[j] = sv;
     s0[P + j] = 1.0f / sn;
     reinterpret_cast<uint32_t*>(s0)[2 * P + j] = (uint32_t)hi | ((uint32_t)lo << 16);
+  }
+  if (blockIdx.y == kVmaxParts - 1) {  // the zero pad after the last key
+    const int32_t lkp = (a.Lk + 63) / 64 * 64;
+    for (int32_t j = a.Lk + threadIdx.x; j < lkp; j += 256) {
+      s0[j] = 0.0f;
+      s0[P + j] = 0.0f;
+      reinterpret_cast<uint32_t*>(s0)[2 * P + j] = 0u;
+    }
   }
   m = group_max<64>(m);
   __shared__ float wmax[4];

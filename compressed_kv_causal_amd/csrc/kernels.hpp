@@ -126,16 +126,19 @@ hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 // FP8 cache: every key's V row scale s_v in attention order [reference | memory | window |
-// block], as 3 planes [H][KF*T]: s_v, 1/s_v, and log2(s_v) as a bf16 (hi, lo) pair; and
+// block], as 3 planes [H][KF*T + kVscalePad]: s_v, 1/s_v, and log2(s_v) as a bf16 (hi, lo)
+// pair, each head's row followed by zeros up to the next multiple of 64 keys (so that the
+// attention copies whole 8-key groups of a 64-key tile without a bound check); and
 // vmax[h * kVmaxParts + p] = the largest s_v of the p-th of kVmaxParts slices of head h's
 // keys (0 for an empty slice).
 constexpr int kVmaxParts = 32;
+constexpr int kVscalePad = 64;
 struct VscaleArgs {
   const float* ring_v_scale;  // [R][T][H]
   const float* mem_v_scale;   // [M][T][H]
   const float* ref_v_scale;   // [ref][T][H]
   const float* vcur_scale;    // [B_max][T][H]
-  float* vscale;              // [3][H][KF*T]
+  float* vscale;              // [3][H][KF*T + kVscalePad]
   float* vmax;                // [H][kVmaxParts]
   HistMap hist;
   int32_t T, H, Lk, key_frames_max;

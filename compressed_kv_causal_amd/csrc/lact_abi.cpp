@@ -125,7 +125,7 @@ void compute_layout(const lact_cfg& c, int32_t members, lact_layout* L) {
   L->qrot = take(ob * B);
   L->vcur = take(fb * B);
   L->vcur_scale = take(fp8 ? sb * B : 0);
-  L->vscale = take(fp8 ? 3 * sizeof(float) * (size_t)c.heads * (size_t)KF * (size_t)T : 0);
+  L->vscale = take(fp8 ? 3 * sizeof(float) * (size_t)c.heads * ((size_t)KF * (size_t)T + lact::kVscalePad) : 0);
   L->rope_table = take(sizeof(float) * 2 * (size_t)rope_table_entries(c));
   L->attn_flags = take(sizeof(int32_t) * (size_t)c.heads * (size_t)((B * T + 255) / 256));
   L->vmax = take(fp8 ? sizeof(float) * lact::kVmaxParts * (size_t)c.heads : 0);
@@ -486,7 +486,7 @@ static lact_status block_attention_impl(lact_cache* c, int32_t member, const int
     a.v_fp8 = 1;
     a.vscale = reinterpret_cast<const float*>(c->at(c->lay.vscale));
     a.vmax = reinterpret_cast<const float*>(c->at(c->lay.vmax));
-    a.vs_head_stride = (int64_t)c->lay.key_frames_max * T;
+    a.vs_head_stride = (int64_t)c->lay.key_frames_max * T + lact::kVscalePad;
     a.vs_plane = a.vs_head_stride * g.heads;
   }
   a.T = T;

@@ -139,9 +139,11 @@ typedef struct {
  *                                                   quantised per (token, head) row as the
  *                                                   cache stores it)
  *   vcur_scale     [B_max][T][H] f32                FP8: the row scales of vcur
- *   vscale         [3][H][(ref+M+W+B_max)*T] 4 B    FP8: of every key in attention order
- *                                                   its V row scale s_v (f32), 1/s_v (f32)
- *                                                   and log2(s_v) as a bf16 (hi, lo) pair
+ *   vscale         [3][H][(ref+M+W+B_max)*T + 64]   FP8: of every key in attention order
+ *                  4 B                              its V row scale s_v (f32), 1/s_v (f32)
+ *                                                   and log2(s_v) as a bf16 (hi, lo) pair;
+ *                                                   zeros after the last key up to the
+ *                                                   next multiple of 64
  *   *_scale        f32 per (token, head): ring/mem/ref [slots][T][H]
  *   rope_table     float2 (cos, sin) table
  *   attn_flags     int32 per (head, 256-row query tile): attention work queue of the exact

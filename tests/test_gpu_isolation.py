@@ -111,11 +111,12 @@ def _canary(run, n):
         if r.fp8:
             r.nan_fill(r.span(lay.vcur_scale + n * r.sb, (B - n) * r.sb), "f32")
     if r.fp8:
-        P = H * KF * T
+        row = KF * T + 64                                # each head's row ends in a zero pad
+        P = H * row
         for plane in range(3):
             for h in range(H):
-                at = lay.vscale + (plane * P + h * KF * T + Lk) * 4
-                r.nan_fill(r.span(at, (KF * T - Lk) * 4), "f32")
+                at = lay.vscale + (plane * P + h * row + Lk) * 4
+                r.nan_fill(r.span(at, (row - Lk) * 4), "f32")
     return saved
 
 
