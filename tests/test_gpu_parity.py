@@ -367,7 +367,7 @@ def test_fp8_small_stream_memory_wraps(D):
 @pytest.mark.parametrize("kv", [BF16, FP8], ids=["bf16", "fp8"])
 def test_many_heads_stream(kv):
     """72 heads x 128 on an 8x8 grid with a reference frame: one token's rows take 1152
-    RoPE lanes, more than one workgroup, so the pass splits each token over two; 10 steps
+    RoPE lanes, more than a workgroup's 1024, so the pass's lanes loop over them; 10 steps
     with history rebuilt from reference, memory and window, every row against the oracle,
     state and memory bit-exact."""
     w = synth.workload("tiny_ref", heads=72, head_dim=128, grid_h=8, grid_w=8, kv_dtype=kv,
