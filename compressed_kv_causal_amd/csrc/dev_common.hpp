@@ -173,6 +173,16 @@ __device__ __forceinline__ float store8_kv(void* base, int32_t dtype, int64_t of
   return rq.scale;
 }
 
+// Workgroup b of a launch runs on XCD b mod 8, and each XCD has its own L2.  Maps the
+// workgroup's linear id b to an item of [0, n) so that each XCD takes one contiguous range
+// of items: neighbouring items, which share cache lines, then share one L2.  A bijection
+// on [0, n).
+__device__ __forceinline__ int32_t xcd_item(int32_t b, int32_t n) {
+  const int32_t x = b & 7, j = b >> 3;
+  const int32_t q8 = n >> 3, r8 = n & 7;
+  return x < r8 ? x * (q8 + 1) + j : r8 * (q8 + 1) + (x - r8) * q8 + j;
+}
+
 // Sources of a key frame's rows.
 enum : int32_t { SRC_RING = 0, SRC_MEM = 1, SRC_CUR = 2, SRC_REF = 3 };
 

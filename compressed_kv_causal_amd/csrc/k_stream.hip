@@ -48,9 +48,11 @@ __global__ __launch_bounds__(256) void k_ring_write(const RingWriteArgs a) {
 // then stored in the cache dtype.  Each input frame is read once.
 // ---------------------------------------------------------------------------------------
 // Work split: a workgroup is one wave; lane = one 8-channel chunk of 64 consecutive chunks
-// (blockIdx.x), so a wave reads and writes 1 KiB contiguous per token and frame (512 B for
-// FP8); blockIdx.y = a run of TOK tokens, blockIdx.z = (member, group, tensor).  D/8 lanes
-// form one (token, head) row, which is what the FP8 row quantiser reduces over.
+// (the channel block), so a wave reads and writes 1 KiB contiguous per token and frame (512
+// B for FP8); each workgroup takes one (channel block, run of TOK tokens) item, the items
+// laid out over the XCDs so that a token run's channel blocks share one L2;
+// blockIdx.z = (member, group, tensor).  D/8 lanes form one (token, head) row, which is
+// what the FP8 row quantiser reduces over.
 struct CompressPtrs {
   const char* ring;
   const float* ring_scale;
@@ -91,11 +93,15 @@ template <int LPR, int R, int TOK, int KV>
 __global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
   using Raw = typename std::conditional<KV == DT_FP8, uint2, uint4>::type;  // 8 stored elements
   const int32_t C = a.H * a.D;
-  const int32_t c0 = (blockIdx.x * 64 + threadIdx.x) * 8;  // first channel of this lane
+  // (channel block, token run) of this workgroup, the head groups of a token run on one
+  // XCD (they share the FP8 row scales' cache lines)
+  const int32_t item = xcd_item(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int32_t bx = item % gridDim.x, by = item / gridDim.x;
+  const int32_t c0 = (bx * 64 + threadIdx.x) * 8;          // first channel of this lane
   if (c0 >= C) return;                                     // whole LPR groups leave together
   const CompressPtrs p = compress_ptrs(a);
   const int gi = p.gi;
-  const int32_t u0 = blockIdx.y * TOK;
+  const int32_t u0 = by * TOK;
   const int32_t rows = a.T * a.H;
   const char* ring = p.ring;
   constexpr int EB = KV == DT_FP8 ? 1 : 2;                 // stored bytes per element
@@ -272,22 +278,30 @@ __device__ __forceinline__ void rope_rotate8(const float2* cs, float* x) {
 // attention reads V as stored (codes), so the pass leaves history V alone and quantises
 // the block's V like the cache stores it (codes to vcur, row scales to vcur_scale).
 //
-// Work split: blockIdx.x = token u, so u and its grid coordinates are scalars; the
-// workgroup's lanes cover the token's H x D/8 chunks (LPR consecutive lanes per head, a
-// wave reads 64 x 16 B contiguous).  A block frame's Q, K and V loads are issued before
-// its stores (which the compiler must otherwise assume may alias them).
-template <int LPR>
+// Work split: blockIdx.x = a run of TPB tokens, so the tokens and their grid coordinates
+// are scalars; the workgroup's lanes cover a token's H x D/8 chunks (LPR consecutive lanes
+// per head, a wave reads 64 x 16 B contiguous).  A lane issues the history loads of all
+// TPB tokens, and a block frame's Q, K and V loads of one token, before the stores that
+// use them (the compiler must otherwise assume the stores may alias them).
+template <int LPR, int TPB, int IN, int KV>
 __global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
-  const int32_t u = blockIdx.x;
   const int32_t rows = a.T * a.H;
   const int32_t n_hist = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   const int32_t fi = blockIdx.y + (a.hist_rows ? 0 : n_hist);
-  const int32_t gr = a.rope_mode == 1 ? 0 : u / a.grid_w;
-  const int32_t gc = a.rope_mode == 1 ? 0 : u - gr * a.grid_w;
   const int64_t KFT = (int64_t)a.key_frames_max * a.T;
   const int64_t QT = (int64_t)a.block_frames_max * a.T;
   const int64_t D = a.D;
-  const bool fp8 = a.kv_dtype == DT_FP8;
+  constexpr bool fp8 = KV == DT_FP8;
+  int32_t u[TPB], gr[TPB], gc[TPB];
+  bool ok[TPB];
+#pragma unroll
+  for (int t = 0; t < TPB; ++t) {
+    const int32_t uu = blockIdx.x * TPB + t;
+    ok[t] = uu < a.T;
+    u[t] = ok[t] ? uu : a.T - 1;                           // a tail token repeats the last's loads
+    gr[t] = a.rope_mode == 1 ? 0 : u[t] / a.grid_w;
+    gc[t] = a.rope_mode == 1 ? 0 : u[t] - gr[t] * a.grid_w;
+  }
   if (fi < n_hist) {
     int32_t slot;
     const int32_t src = hist_src(a.hist, fi, &slot);
@@ -295,38 +309,49 @@ __global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
     const float* kscale = src == SRC_REF ? a.ref_k_scale : (src == SRC_MEM ? a.mem_k_scale : a.ring_k_scale);
     for (int32_t e = threadIdx.x; e < a.H * LPR; e += blockDim.x) {
       const int32_t h = e / LPR, li = e % LPR;
-      const int64_t srow = (int64_t)slot * rows + (int64_t)u * a.H + h;
-      const float sc = fp8 ? kscale[srow] : 1.0f;
-      float x[8];
-      float2 cs[4];
-      load8_kv(ksrc, a.kv_dtype, srow * D + li * 8, sc, x);
-      rope_cs(a, fi, u, gr, gc, li, cs);
-      rope_rotate8(cs, x);
-      store8_op(a.krot, a.in_dtype, (h * KFT + (int64_t)fi * a.T + u) * D + li * 8, x);
+      float x[TPB][8];
+      float2 cs[TPB][4];
+#pragma unroll
+      for (int t = 0; t < TPB; ++t) {
+        const int64_t srow = (int64_t)slot * rows + (int64_t)u[t] * a.H + h;
+        const float sc = fp8 ? kscale[srow] : 1.0f;
+        load8_kv(ksrc, KV, srow * D + li * 8, sc, x[t]);
+        rope_cs(a, fi, u[t], gr[t], gc[t], li, cs[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < TPB; ++t) {
+        if (!ok[t]) continue;
+        rope_rotate8(cs[t], x[t]);
+        store8_op(a.krot, IN, (h * KFT + (int64_t)fi * a.T + u[t]) * D + li * 8, x[t]);
+      }
     }
     return;
   }
   const int32_t i = fi - n_hist;                           // frame inside the block
   for (int32_t e = threadIdx.x; e < a.H * LPR; e += blockDim.x) {
     const int32_t h = e / LPR, li = e % LPR;
-    const int64_t crow = (int64_t)i * rows + (int64_t)u * a.H + h;  // block [n*T][H][D]
-    float xq[8], xk[8], xv[8];
-    float2 cs[4];
-    load8_in(a.q, a.in_dtype, crow * D + li * 8, xq);
-    load8_in(a.k_cur, a.in_dtype, crow * D + li * 8, xk);
-    load8_in(a.v_cur, a.in_dtype, crow * D + li * 8, xv);
-    rope_cs(a, fi, u, gr, gc, li, cs);
-    rope_rotate8(cs, xq);
 #pragma unroll
-    for (int e2 = 0; e2 < 8; ++e2) xq[e2] *= a.q_scale;
-    store8_op(a.qrot, a.in_dtype, (h * QT + (int64_t)i * a.T + u) * D + li * 8, xq);
-    rope_rotate8(cs, xk);
-    store8_op(a.krot, a.in_dtype, (h * KFT + (int64_t)fi * a.T + u) * D + li * 8, xk);
-    if (fp8) {
-      const float sc = store8_kv<LPR>(a.vcur, DT_FP8, crow * D + li * 8, xv);
-      if (li == 0) a.vcur_scale[crow] = sc;
-    } else {
-      store8_op(a.vcur, a.in_dtype, crow * D + li * 8, xv);
+    for (int t = 0; t < TPB; ++t) {                        // block frames: one token at a time
+      if (!ok[t]) continue;                                // uniform over the workgroup
+      const int64_t crow = (int64_t)i * rows + (int64_t)u[t] * a.H + h;  // block [n*T][H][D]
+      float xq[8], xk[8], xv[8];
+      float2 cs[4];
+      load8_in(a.q, IN, crow * D + li * 8, xq);
+      load8_in(a.k_cur, IN, crow * D + li * 8, xk);
+      load8_in(a.v_cur, IN, crow * D + li * 8, xv);
+      rope_cs(a, fi, u[t], gr[t], gc[t], li, cs);
+      rope_rotate8(cs, xq);
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) xq[e2] *= a.q_scale;
+      store8_op(a.qrot, IN, (h * QT + (int64_t)i * a.T + u[t]) * D + li * 8, xq);
+      rope_rotate8(cs, xk);
+      store8_op(a.krot, IN, (h * KFT + (int64_t)fi * a.T + u[t]) * D + li * 8, xk);
+      if (fp8) {
+        const float sc = store8_kv<LPR>(a.vcur, DT_FP8, crow * D + li * 8, xv);
+        if (li == 0) a.vcur_scale[crow] = sc;
+      } else {
+        store8_op(a.vcur, IN, crow * D + li * 8, xv);
+      }
     }
   }
 }
@@ -343,9 +368,12 @@ __global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
 // row of all but zero values) counts as that normal in the 1/s_v and log2 planes, where
 // it only has to give P~ = 0 and a finite 1/s_v.
 __global__ __launch_bounds__(256) void k_vscale_stage(const VscaleArgs a) {
-  const int32_t h = blockIdx.x;
+  // (head, slice) of this workgroup: all heads of a slice on one XCD, since they gather from
+  // the same cache lines of the [slot][T][H] row scales
+  const int32_t item = xcd_item(blockIdx.x + a.H * blockIdx.y, a.H * kVmaxParts);
+  const int32_t h = item % a.H, part = item / a.H;
   const int32_t per = (a.Lk + kVmaxParts - 1) / kVmaxParts;
-  const int32_t j0 = blockIdx.y * per;
+  const int32_t j0 = part * per;
   const int32_t j1 = j0 + per < a.Lk ? j0 + per : a.Lk;
   const int32_t nh = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
   const int64_t row = (int64_t)a.key_frames_max * a.T + kVscalePad;
@@ -372,7 +400,7 @@ __global__ __launch_bounds__(256) void k_vscale_stage(const VscaleArgs a) {
     s0[P + j] = 1.0f / sn;
     reinterpret_cast<uint32_t*>(s0)[2 * P + j] = (uint32_t)hi | ((uint32_t)lo << 16);
   }
-  if (blockIdx.y == kVmaxParts - 1) {  // the zero pad after the last key
+  if (part == kVmaxParts - 1) {  // the zero pad after the last key
     const int32_t lkp = (a.Lk + 63) / 64 * 64;
     for (int32_t j = a.Lk + threadIdx.x; j < lkp; j += 256) {
       s0[j] = 0.0f;
@@ -385,7 +413,7 @@ __global__ __launch_bounds__(256) void k_vscale_stage(const VscaleArgs a) {
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0)
-    a.vmax[h * kVmaxParts + blockIdx.y] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    a.vmax[h * kVmaxParts + part] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -452,11 +480,22 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
   // heads loop)
   const int64_t lanes = (int64_t)a.H * (a.D / 8);
   const int threads = lanes >= 1024 ? 1024 : (int)((lanes + 63) / 64 * 64);
-  dim3 grid(a.T, frames);
-  if (a.D == 128)
-    hipLaunchKernelGGL(k_rope<16>, grid, dim3(threads), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_rope<8>, grid, dim3(threads), 0, s, a);
+  constexpr int TPB = 2;
+  dim3 grid((a.T + TPB - 1) / TPB, frames);
+  // dtypes at compile time: a load's conversion inside a runtime dtype branch makes the
+  // compiler wait for that load at once, so a block frame's Q, K, V loads would not overlap
+#define LACT_ROPE(L, I, K) hipLaunchKernelGGL((k_rope<L, TPB, I, K>), grid, dim3(threads), 0, s, a)
+  const bool d128 = a.D == 128;
+  if (a.in_dtype == DT_F32 && a.kv_dtype == DT_F32) {
+    if (d128) LACT_ROPE(16, DT_F32, DT_F32); else LACT_ROPE(8, DT_F32, DT_F32);
+  } else if (a.in_dtype == DT_BF16 && a.kv_dtype == DT_BF16) {
+    if (d128) LACT_ROPE(16, DT_BF16, DT_BF16); else LACT_ROPE(8, DT_BF16, DT_BF16);
+  } else if (a.in_dtype == DT_BF16 && a.kv_dtype == DT_FP8) {
+    if (d128) LACT_ROPE(16, DT_BF16, DT_FP8); else LACT_ROPE(8, DT_BF16, DT_FP8);
+  } else {
+    return hipErrorNotSupported;
+  }
+#undef LACT_ROPE
   return hipGetLastError();
 }
 
