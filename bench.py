@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="run one device copy of MIB MiB first (reference for HBM byte counters)")
     p.add_argument("--cold", type=int, default=5, metavar="STEPS",
-                   help="after the timed steps, run STEPS more with a 512 MiB write before each "
+                   help="after the timed steps, run STEPS more with a 512 MiB read before each "
                         "RoPE, append and compress call (last-level cache flushed) and report "
                         "those calls' times as 'cold' (0: skip)")
     p.add_argument("--no-ceilings", action="store_true",
@@ -276,23 +276,25 @@ def main():
                                 "qk_bf16_pv_fp8_peak_tflops": round(mixed, 1)}
 
     if args.cold:
-        # the streaming calls with their inputs out of the last-level cache: a 512 MiB write
-        # before each (the attention call between them keeps the step order)
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # the streaming calls with their inputs out of the last-level cache: a 512 MiB read
+        # before each (no dirty lines, so no write-back overlaps the timed call; the
+        # attention call between them keeps the step order)
+        import microbench as MB
+        flush = MB.read_flush(torch)
         cold = []
         for _ in range(args.cold):
             q, k, v = pool[i % len(pool)]
             e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-            scratch.fill_(1)
+            flush()
             e[0].record(stream)
             L.lact_rope_reset_apply(h, q, k, v, B, stream)
             e[1].record(stream)
             L.lact_block_attention(h, None, out, lse, stream)
-            scratch.fill_(2)
+            flush()
             e[2].record(stream)
             L.lact_kv_ring_append(h, k, v, B, stream)
             e[3].record(stream)
-            scratch.fill_(3)
+            flush()
             e[4].record(stream)
             L.lact_convkv_compress(h, d_wk, d_bk, d_wv, d_bv, stream)
             e[5].record(stream)
@@ -309,7 +311,7 @@ def main():
                        "gbs": {"rope_reset_apply": round(rope_bytes / (cm[0] * 1e-3) / 1e9, 1),
                                "kv_ring_append": round(append_bytes / (cm[1] * 1e-3) / 1e9, 1),
                                "convkv_compress": round(compress_bytes / (cm[2] * 1e-3) / 1e9, 1)}}
-        del scratch
+        del flush
     stream_bytes = {"rope_reset_apply": rope_bytes, "kv_ring_append": append_bytes,
                     "convkv_compress": compress_bytes}
     if not args.no_ceilings:

@@ -49,6 +49,23 @@ def _check(rc, what):
         raise RuntimeError(f"{what} launch failed (hipError {rc})")
 
 
+def read_flush(torch, nbytes=512 << 20):
+    """A callable that evicts the last-level cache by reading nbytes once (mb_read on the
+    current stream).  A read leaves no dirty lines behind, so no write-back of the flush
+    overlaps the call timed after it, as it would after a fill."""
+    dev = torch.device("cuda")
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    bp, sp = ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(sink.data_ptr())
+
+    def flush():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        _check(lib().mb_read(bp, nbytes, sp, s), "mb_read")
+    flush.buffers = (buf, sink)   # keeps the buffers alive with the callable
+    return flush
+
+
 def _timed(torch, fn, reps, flush=None):
     """Median over reps of fn() timed with events on the current stream; flush() (a
     last-level cache flush) runs before each rep, outside the timed interval."""
@@ -122,7 +139,7 @@ def overlap_ms(torch, cus=256, iters=4096, reps=5):
 def copy_gbs(torch, read_bytes, write_bytes, reps=7, cold=False):
     """GB/s (bytes read + written per second) of a streaming kernel with the given read and
     write sizes: 1:1 (read == write), 5:1 (read == 5 * write) or read-only (write == 0).
-    cold: a 512 MiB write before each rep evicts the inputs from the last-level cache."""
+    cold: a 512 MiB read before each rep evicts the inputs from the last-level cache."""
     dev = torch.device("cuda")
     five = write_bytes > 0 and read_bytes == 5 * write_bytes
     ronly = write_bytes == 0
@@ -131,7 +148,7 @@ def copy_gbs(torch, read_bytes, write_bytes, reps=7, cold=False):
     src = torch.empty(5 * n if five else n, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty(1024 * 4 if ronly else n, dtype=torch.uint8, device=dev)
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
+    flush = read_flush(torch) if cold else None
     sp, dp = ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr())
 
     def run():
@@ -140,7 +157,7 @@ def copy_gbs(torch, read_bytes, write_bytes, reps=7, cold=False):
         else:
             _check((lib().mb_copy5 if five else lib().mb_copy)(sp, dp, n, s), "mb_copy")
     run()
-    ms = _timed(torch, run, reps, flush=(lambda: flush_buf.fill_(7)) if cold else None)
+    ms = _timed(torch, run, reps, flush=flush)
     total = n if ronly else (5 * n if five else n) + n
-    del src, dst, flush_buf
+    del src, dst, flush
     return total / (ms * 1e-3) / 1e9
