@@ -365,6 +365,32 @@ def test_fp8_small_stream_memory_wraps(D):
 
 
 @pytest.mark.parametrize("kv", [BF16, FP8], ids=["bf16", "fp8"])
+def test_odd_tokens_stream(kv):
+    """T = 81 (a 9x9 grid, odd): the RoPE pass's workgroups take two tokens, so the last one
+    holds one token and the other's loads repeat it; the D = 128 attention kernel's key
+    tiles straddle frames and its query tiles end mid-frame; the compressor's 42 (channel
+    block, token run) items fill the 8 XCDs unevenly.  14 steps of 1-4 frames, every row
+    against the oracle (each head and row to its bound), state every step, memory and
+    ring bit-exact."""
+    name = "fp8_kv" if kv == FP8 else "s512_bf16"
+    w = synth.workload(name, heads=8, grid_h=9, grid_w=9, window_frames=4, mem_slots=4,
+                       max_block_frames=4)
+    run = Runner(w)
+    worst = 0.0
+    for s, n in enumerate([4, 2, 3, 4, 4, 1, 4, 3, 4, 4, 2, 4, 4, 4]):
+        res = run.step(n)
+        err, dl = run.compare_attention(res)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[kv], (s, err, dl)
+        assert_lse(run, res, kv)
+        assert_state_matches(run)
+    assert run.oc.bk.G > w["mem_slots"]
+    assert_memory_bitexact(run)
+    assert_ring_bitexact(run)
+    say(f"T=81 {'fp8' if kv == FP8 else 'bf16'} stream: worst rel L2 {worst:.3e}")
+
+
+@pytest.mark.parametrize("kv", [BF16, FP8], ids=["bf16", "fp8"])
 def test_many_heads_stream(kv):
     """72 heads x 128 on an 8x8 grid with a reference frame: one token's rows take 1152
     RoPE lanes, more than a workgroup's 1024, so the pass's lanes loop over them; 10 steps
