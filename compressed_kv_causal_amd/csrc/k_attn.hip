@@ -7,7 +7,10 @@
 // query row i sees exactly the key prefix [0, Lhist + block_end[block(i)]).
 //
 // Kernels:
-//   k_attn_bf16_d128  the D = 128 production kernel (described at its definition).
+//   k_attn_bf16_d128_dual  the D = 128 production kernel for a bf16 V (described at its
+//                     definition).
+//   k_attn_bf16_d128<true>  the D = 128 production kernel for an FP8 cache's e4m3 V; its
+//                     tile ring, copies and fragment layouts are shared with the above.
 //   k_attn_bf16<D, F8V>  exact online-softmax flash attention on v_mfma_f32_32x32x16_bf16,
 //                     4 waves x 32 query rows, 64-key tiles staged in LDS (K row-major, V
 //                     transposed by the staging threads, an FP8 cache's V codes widened to
@@ -237,7 +240,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// k_attn_bf16_d128: the D = 128 production kernel (T >= 64).
+// k_attn_bf16_d128<F8>: the D = 128 kernel in the lockstep layout (T >= 64), launched for
+// an FP8 cache's V (F8 = true).  Its bf16-V form (F8 = false) is not launched:
+// k_attn_bf16_d128_dual below replaces it for a bf16 V.
 //
 //   * 256 query rows per workgroup, 8 waves x 32 rows: two waves per SIMD, so one wave's
 //     softmax (VALU) and barrier waits overlap the other's MFMAs.
@@ -876,6 +881,537 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
 }
 
 // Plain f32 kernel: one lane per query row, 32-key tiles of K and V in LDS.
+// ---------------------------------------------------------------------------------------
+// k_attn_bf16_d128_dual: the D = 128 kernel for a bf16 V (T >= 64).  One wave per SIMD
+// (4 waves, 256 query rows per workgroup) and two 32-row query blocks per wave, A and B,
+// software-pipelined across key tiles so that every run of MFMAs carries half a softmax:
+//
+//     X(i): S(i+1) = Q K(i+1)^T - m for A and B (32 MFMAs; each K fragment read feeds two)
+//           beside B's exponentials, row sum and bf16 packing of tile i
+//     Y(i): O^T += V(i)^T P(i)^T for A and B (32 MFMAs; each V^T fragment read feeds two)
+//           beside A's exponentials, row sum and bf16 packing of tile i + 1
+//
+// Per MFMA step the wave issues one exponential, one add and every other step one packing;
+// the fragment reads are half those of the two-waves-per-SIMD layout of k_attn_bf16_d128.
+// Key tile ring, copies, swizzles, fragment layouts, the lazy reference (the first tile's
+// row maximum, folded into the start of every QK^T chain) and the flags are those of
+// k_attn_bf16_d128.  Differences:
+//   * a tile sum that reaches 2^64 (scores far above the reference) is not rescaled in
+//     place: the wave records it, finishes, and the workgroup flags its rows for the exact
+//     pass;
+//   * the free tiles run in pipelined passes of four (ring slots as compile-time
+//     constants); the pass remainder and the tiles that need a per-element mask run
+//     unpipelined after them.
+// Register use is the point of the layout: O (2 x 64) and the Q fragments (2 x 32) stay in
+// AGPRs, the scores, probabilities and addresses in the 256 arch VGPRs.  The MFMAs are
+// inline asm so that each operand keeps its register file; a loop with a branch out of
+// its passes, or tile state that stays live after the passes, makes the allocator spill,
+// hence the flag instead of an early exit and the state handover in (s0, p0) only.
+// ---------------------------------------------------------------------------------------
+namespace d128dual {
+
+constexpr int D = 128, BM = 256, BN = 64, NS = 4, WAVES = 4;
+constexpr int ROW_BYTES = D * 2;
+constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
+constexpr int V_RING = NS * TILE_BYTES;
+constexpr int LDS_BYTES = 2 * NS * TILE_BYTES;
+constexpr int VMEM_PER_TILE = 8;            // copy instructions per wave per tile: K 4, V 4
+constexpr int KAHEAD = 2;                   // K fragment pairs read ahead of their MFMAs
+constexpr int VAHEAD = 2;                   // V^T fragments read ahead (each feeds two MFMAs)
+
+using d128::Geo;
+using d128::Stream;
+using d128::copy_to_lds;
+using d128::frame_base;
+using d128::step_fence;
+using d128::swz;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+struct Ctx {
+  Geo g;
+  const char* kbase;  // this head's rotated keys [Lk][128]
+  char* lds;
+  unsigned lds_u32;
+  int wave, lane, hi, lr;
+  int kvis[2];        // keys visible to the lane's row of block A / B
+  int64_t hrow;       // bytes between consecutive tokens of one V frame
+  int crow[4];        // copies: the four 4-row groups of a tile this lane copies
+  int koff[4];
+  int voff[4];
+  int kread[8];       // fragment reads: LDS byte offsets from the ring base (slot 0)
+  int vread[4][2];
+};
+
+template <int SLOT>
+__device__ __forceinline__ int slot_of(int j) { return SLOT >= 0 ? SLOT : j % NS; }
+
+// Copy tile t's 64 key rows of K and V into ring slot t % NS (this wave: rows 16 wave ..
+// 16 wave + 15), then advance the stream.
+__device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
+  const Geo& a = c.g;
+  const unsigned slot = (unsigned)(t % NS);
+  const unsigned kdst = c.lds_u32 + slot * TILE_BYTES + (unsigned)c.wave * 16 * ROW_BYTES;
+  const unsigned vdst = kdst + V_RING;
+  if ((t + 1) * BN <= a.Lk) {
+    const char* ktile = c.kbase + (int64_t)t * TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy_to_lds(ktile + c.koff[i], kdst + i * 4 * ROW_BYTES);
+  } else {  // rows past the last key repeat it
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int key = t * BN + c.crow[i];
+      key = key < a.Lk ? key : a.Lk - 1;
+      copy_to_lds(c.kbase + (int64_t)key * ROW_BYTES + (c.koff[i] & (ROW_BYTES - 1)), kdst + i * 4 * ROW_BYTES);
+    }
+  }
+  const char* vA = st.baseA + st.u0 * c.hrow;
+  if (st.u0 + BN <= a.T) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy_to_lds(vA + c.voff[i], vdst + i * 4 * ROW_BYTES);
+  } else {
+    const char* vB = st.baseB + (st.u0 - a.T) * c.hrow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      copy_to_lds((st.u0 + c.crow[i] >= a.T ? vB : vA) + c.voff[i], vdst + i * 4 * ROW_BYTES);
+  }
+  st.u0 += BN;  // T >= BN: at most one frame boundary per tile
+  if (st.u0 >= a.T) {
+    st.u0 -= a.T;
+    st.f0 += 1;
+    st.baseA = st.baseB;
+    st.baseB = frame_base(c.g, st.f0 + 1);
+  }
+}
+
+// The MFMAs.  QK^T: K and Q fragments from AGPRs, scores (destination and accumulator) in
+// arch VGPRs, where the exponentials read them.  PV: O in AGPRs for the whole kernel.  The
+// compiler does not see inline asm as MFMAs, so it inserts no wait states between them and
+// the VALU instructions around them.  They are used only in the pipelined passes, where the
+// first VALU read of a score follows the MFMA that last wrote it by three MFMA steps and
+// about 25 more instructions (the v_mfma_f32_32x32x16_bf16, 8 passes, needs about 11) and
+// no VALU instruction writes an MFMA operand shortly before its MFMA; drain_o separates the
+// passes from the builtin MFMAs and VALU uses of O after them.  The generated code is
+// checked for this by the tests (tests/asm_hazards.py).
+__device__ __forceinline__ f32x16_t qk_first(const bf16x8_t& k, const bf16x8_t& q, const f32x16_t& init) {
+  f32x16_t d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "a"(k), "a"(q), "v"(init));
+  return d;
+}
+__device__ __forceinline__ void qk_next(f32x16_t& d, const bf16x8_t& k, const bf16x8_t& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "a"(k), "a"(q));
+}
+__device__ __forceinline__ void pv_mfma(f32x16_t& o, const bf16x8_t& v, const u32x4_t& p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+}
+// After the inline-asm passes: 24 wait states that every later use of O must follow (O
+// passes through the asm, so nothing reading it can be placed before).
+__device__ __forceinline__ void drain_o(f32x16_t (&o)[2][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                 "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+}
+
+// Moves a value into AGPRs once (the asm operands then take it without a copy per use).
+template <typename T>
+__device__ __forceinline__ T in_agprs(T v) {
+  T r;
+  asm volatile("" : "=a"(r) : "0"(v));
+  return r;
+}
+// Defines the packed probabilities and the sum at this point, so that the code producing
+// them stays in the phase it was written in (instead of sinking to where they are used).
+__device__ __forceinline__ void pin(u32x4_t (&p)[4], float& sum) {
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) asm volatile("" : "+v"(p[ch]));
+  asm volatile("" : "+v"(sum));
+}
+
+__device__ __forceinline__ bf16x8_t kfrag(const char* kb, const Ctx& c, int kk, int kb2) {
+  return *reinterpret_cast<const bf16x8_t*>(kb + c.kread[kk] + kb2 * 32 * ROW_BYTES);
+}
+
+// V^T fragment (16 keys of chunk ch, channels 32 db .. 32 db + 31)
+__device__ __forceinline__ bf16x8_t vfrag(const char* vb, const Ctx& c, int ch, int db) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + c.vread[db][0] + ch * 16 * ROW_BYTES));
+  const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + c.vread[db][1] + ch * 16 * ROW_BYTES));
+  bf16x8_t vf;
+  __builtin_memcpy(&vf, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&vf) + 8, &up, 8);
+  return vf;
+}
+
+// Softmax step e (0..31) of one block's tile: p_e = exp2(s_e) in place (the scores already
+// hold q.k - m_ref), the previous step's p into the row sum (so the add never waits on the
+// exponential it follows), and at odd e >= 3 the pair (e - 3, e - 2) packed to bf16: pair k
+// holds keys 16 (k / 4) + 8 hi + 2 (k mod 4), +1, word k mod 4 of chunk k / 4 of the PV
+// operand.
+__device__ __forceinline__ void exp_step(f32x16_t (&s)[2], u32x4_t (&p)[4], float& sum, int e) {
+  s[e >> 4][e & 15] = __builtin_amdgcn_exp2f(s[e >> 4][e & 15]);
+  if (e > 0) sum += s[(e - 1) >> 4][(e - 1) & 15];
+  if (e >= 3 && (e & 1)) {
+    const int k = (e - 3) >> 1;
+    p[k >> 2][k & 3] = pack_bf16x2(s[k >> 3][(2 * k) & 15], s[k >> 3][(2 * k + 1) & 15]);
+  }
+}
+// After step 31: the last value into the sum, the last pair packed.
+__device__ __forceinline__ void exp_finish(const f32x16_t (&s)[2], u32x4_t (&p)[4], float& sum) {
+  sum += s[1][15];
+  p[3][3] = pack_bf16x2(s[1][14], s[1][15]);
+}
+
+// X phase on K slot KS: sn[b] = Q_b K(t)^T - m_b for both blocks (from the broadcast
+// -m_ref of the rows, negm; INIT0: from 0), beside (EXPB) block B's exponentials of its
+// current tile sb, packed into pb, and their sum.  mid() runs after the second MFMA (the
+// copies); VS >= 0: the last steps also read the first VAHEAD V^T fragments of the Y phase
+// that follows (V slot VS) into vf.  ASM: the inline-asm MFMAs of the pipelined passes;
+// otherwise builtins, whose hazards the compiler handles (prologue and tail).
+template <int KS, bool EXPB, int VS = -2, bool INIT0 = false, bool ASM = true, typename Mid>
+__device__ __forceinline__ void phase_x(const Ctx& c, int t, const bf16x8_t (&qf)[2][8], const f32x16_t (&negm)[2],
+                                        f32x16_t (&sn)[2][2], f32x16_t (&sb)[2], u32x4_t (&pb)[4], float& sumb,
+                                        bf16x8_t (&vf)[VAHEAD + 1], Mid mid) {
+  static_assert(!(ASM && INIT0), "the asm MFMAs start from negm");
+  const char* kb = c.lds + slot_of<KS>(t) * TILE_BYTES;
+  bf16x8_t kf[KAHEAD + 1][2];
+#pragma unroll
+  for (int kk = 0; kk < KAHEAD; ++kk) {
+    kf[kk][0] = kfrag(kb, c, kk, 0);
+    kf[kk][1] = kfrag(kb, c, kk, 1);
+  }
+  if (EXPB) sumb = 0.0f;
+  step_fence();
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int blk = m & 1, kb2 = m >> 1;
+      if (m == 0 && kk + KAHEAD < 8) {
+        kf[(kk + KAHEAD) % (KAHEAD + 1)][0] = kfrag(kb, c, kk + KAHEAD, 0);
+        kf[(kk + KAHEAD) % (KAHEAD + 1)][1] = kfrag(kb, c, kk + KAHEAD, 1);
+      }
+      const bf16x8_t& kfr = kf[kk % (KAHEAD + 1)][kb2];
+      if (!ASM)
+        sn[blk][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            kfr, qf[blk][kk], kk > 0 ? sn[blk][kb2] : (INIT0 ? f32x16_t{} : negm[blk]), 0, 0, 0);
+      else if (kk > 0)
+        qk_next(sn[blk][kb2], kfr, qf[blk][kk]);
+      else
+        sn[blk][kb2] = qk_first(kfr, qf[blk][kk], negm[blk]);
+      if (EXPB) exp_step(sb, pb, sumb, 4 * kk + m);
+      if (kk == 0 && m == 1) mid();
+      if (VS >= 0 && kk == 7 && m < VAHEAD) vf[m] = vfrag(c.lds + VS * TILE_BYTES, c, m >> 2, m & 3);
+      step_fence();
+    }
+  }
+  if (EXPB) {
+    exp_finish(sb, pb, sumb);
+    pin(pb, sumb);
+  }
+}
+
+// Y phase on V slot VS: o[b] += V^T P_b^T for both blocks from the current tile's packed
+// probabilities pc, beside (EXPA) block A's exponentials of the next tile sa, packed into
+// pa, and their sum.  PRE: the first VAHEAD fragments are already in vf.  ASM: as for
+// phase_x.
+template <int VS, bool EXPA, bool PRE = false, bool ASM = true>
+__device__ __forceinline__ void phase_y(const Ctx& c, int t, const u32x4_t (&pc)[2][4], f32x16_t (&o)[2][4],
+                                        f32x16_t (&sa)[2], u32x4_t (&pa)[4], float& suma,
+                                        bf16x8_t (&vf)[VAHEAD + 1]) {
+  const char* vb = c.lds + slot_of<VS>(t) * TILE_BYTES;
+  if (!PRE) {
+#pragma unroll
+    for (int i = 0; i < VAHEAD; ++i) vf[i] = vfrag(vb, c, i >> 2, i & 3);
+  }
+  if (EXPA) suma = 0.0f;
+  step_fence();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ch = i >> 2, db = i & 3;
+    if (i + VAHEAD < 16) vf[(i + VAHEAD) % (VAHEAD + 1)] = vfrag(vb, c, (i + VAHEAD) >> 2, (i + VAHEAD) & 3);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (ASM)
+        pv_mfma(o[b][db], vf[i % (VAHEAD + 1)], pc[b][ch]);
+      else
+        o[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (VAHEAD + 1)],
+                                                           __builtin_bit_cast(bf16x8_t, pc[b][ch]), o[b][db], 0, 0, 0);
+      if (EXPA) exp_step(sa, pa, suma, 2 * i + b);
+      step_fence();
+    }
+  }
+  if (EXPA) {
+    exp_finish(sa, pa, suma);
+    pin(pa, suma);
+  }
+}
+
+// All 32 exponentials of one block's tile, packed, and their sum, unpipelined.
+__device__ __forceinline__ float exp_all(f32x16_t (&s)[2], u32x4_t (&p)[4]) {
+  float sum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    exp_step(s, p, sum, e);
+    if ((e & 7) == 7) step_fence();  // keeps the temporaries few
+  }
+  exp_finish(s, p, sum);
+  return sum;
+}
+
+__device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int key0, int hi, int kvis) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 32 * kb2 + perm32(((r >> 2) << 3) + (hi << 2) + (r & 3));
+      if (key >= kvis) s[kb2][r] = -INFINITY;
+    }
+}
+
+// True when some lane's tile sum reached 2^64: its row met scores far above the reference.
+// The kernel then finishes its tiles (their results are discarded) and flags its rows for
+// the exact pass.
+__device__ __forceinline__ bool overflow(const float (&sum)[2]) {
+  return __builtin_expect(__any(!(sum[0] < 0x1p64f) || !(sum[1] < 0x1p64f)), 0);
+}
+
+// End of a tile: every copy but the last tile's (VMEM_PER_TILE per wave) has landed, and
+// every wave is done with the ring slot the next tile's copy overwrites.
+__device__ __forceinline__ void tile_end() {
+  static_assert(VMEM_PER_TILE == 8, "the wait count below leaves one tile's copies in flight");
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  __syncthreads();
+}
+
+// One pipelined iteration: X on tile i + 1's K (slot KS), Y on tile i's V (slot VS).
+// sc: the scores of tile i (block B's not yet exponentiated), sn: tile i + 1's; pc: tile
+// i's packed probabilities (A's on entry, B's from X), pn[0]: A's of tile i + 1.
+template <int KS, int VS>
+__device__ __forceinline__ void iteration(const Ctx& c, int i, Stream& st, const bf16x8_t (&qf)[2][8],
+                                          f32x16_t (&o)[2][4], f32x16_t (&sc)[2][2], f32x16_t (&sn)[2][2],
+                                          u32x4_t (&pc)[2][4], u32x4_t (&pn)[2][4], float (&sum)[2],
+                                          float (&l_part)[2], const f32x16_t (&negm)[2], bool& ovf) {
+  bf16x8_t vf[VAHEAD + 1];
+  phase_x<KS, true, VS>(c, i + 1, qf, negm, sn, sc[1], pc[1], sum[1], vf, [&]() { issue(c, i + NS - 1, st); });
+  ovf |= overflow(sum);
+  l_part[0] += sum[0];
+  l_part[1] += sum[1];
+  phase_y<VS, true, true>(c, i, pc, o, sn[0], pn[0], sum[0], vf);
+  tile_end();
+}
+
+// Tile i (V in slot 0) after the pipelined passes: block B's exponentials, then PV.
+__device__ __forceinline__ void finish_tile(const Ctx& c, int i, Stream& st, f32x16_t (&o)[2][4],
+                                            f32x16_t (&sc)[2][2], u32x4_t (&pc)[2][4], float (&sum)[2],
+                                            float (&l_part)[2], bool& ovf) {
+  issue(c, i + NS - 1, st);
+  sum[1] = exp_all(sc[1], pc[1]);
+  ovf |= overflow(sum);
+  l_part[0] += sum[0];
+  l_part[1] += sum[1];
+  bf16x8_t vf[VAHEAD + 1];
+  phase_y<0, false, false, false>(c, i, pc, o, sc[0], pc[0], sum[0], vf);
+  tile_end();
+}
+
+// One tile (K and V in slot SLOT), unpipelined, with the per-element mask (a no-op for the
+// free tiles); s, p: its state.
+template <int SLOT>
+__device__ __forceinline__ void single_tile(const Ctx& c, int i, Stream& st, const bf16x8_t (&qf)[2][8],
+                                            f32x16_t (&o)[2][4], f32x16_t (&s)[2][2], u32x4_t (&p)[2][4],
+                                            float (&sum)[2], float (&l_part)[2], const f32x16_t (&negm)[2],
+                                            bool& ovf) {
+  issue(c, i + NS - 1, st);
+  f32x16_t unused_s[2];
+  u32x4_t unused_p[4];
+  bf16x8_t vf[VAHEAD + 1];
+  phase_x<SLOT, false, -2, false, false>(c, i, qf, negm, s, unused_s, unused_p, sum[1], vf, []() {});
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    mask_tile(s[b], i * BN, c.hi, c.kvis[b]);
+    sum[b] = exp_all(s[b], p[b]);
+  }
+  ovf |= overflow(sum);
+  l_part[0] += sum[0];
+  l_part[1] += sum[1];
+  phase_y<SLOT, false, false, false>(c, i, p, o, unused_s, unused_p, sum[0], vf);
+  tile_end();
+}
+
+}  // namespace d128dual
+
+__global__ __launch_bounds__(256, 1) void k_attn_bf16_d128_dual(const AttnArgs a) {
+  using namespace d128dual;
+  __shared__ __align__(1024) char lds[LDS_BYTES];
+
+  const int n_qt = (a.Lq + BM - 1) / BM;
+  const int item = xcd_item(blockIdx.x, n_qt * a.H);  // one head's tiles on one XCD
+  const int h = item / n_qt, qt = item - h * n_qt;
+
+  Ctx c;
+  c.g.v_mem = static_cast<const char*>(a.v_mem);
+  c.g.v_ring = static_cast<const char*>(a.v_ring);
+  c.g.v_cur = static_cast<const char*>(a.v_cur);
+  c.g.v_ref = static_cast<const char*>(a.v_ref);
+  c.g.frame_bytes = (int64_t)a.T * a.H * ROW_BYTES;
+  c.g.T = a.T;
+  c.g.Lk = a.Lk;
+  c.g.nf = a.Lk / a.T;
+  c.g.ref_len = a.hist.ref_len;
+  c.g.mem_end = a.hist.ref_len + a.hist.mem_len;
+  c.g.nh = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
+  c.g.M = a.hist.M;
+  c.g.R = a.hist.R;
+  c.g.mem_slot0 = a.hist.mem_slot0;
+  c.g.ring_slot0 = a.hist.ring_slot0;
+  c.g.s_last = 0;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.lane = threadIdx.x & 63;
+  c.hi = c.lane >> 5;
+  c.lr = c.lane & 31;
+  c.lds = lds;
+  c.lds_u32 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  c.kbase = static_cast<const char*>(a.k) + (int64_t)h * a.k_head_stride * 2;
+  c.hrow = (int64_t)a.H * ROW_BYTES;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = c.wave * 16 + i * 4 + (c.lane >> 4);
+    const int chunk = (c.lane & 15) ^ swz(r);
+    c.crow[i] = r;
+    c.koff[i] = r * ROW_BYTES + chunk * 16;
+    c.voff[i] = (r * a.H + h) * ROW_BYTES + chunk * 16;
+  }
+  {
+    const int m = perm32(c.lr);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) c.kread[kk] = m * ROW_BYTES + (((2 * kk + c.hi) ^ swz(m)) * 16);
+    const int g = c.lane >> 4, i = c.lane & 15;
+    const int row = c.hi * 8 + (i >> 2);
+    const int half = (i & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int chunk = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
+      c.vread[db][0] = V_RING + row * ROW_BYTES + ((chunk ^ swz(row)) * 16) + half;
+      c.vread[db][1] = V_RING + (row + 4) * ROW_BYTES + ((chunk ^ swz(row + 4)) * 16) + half;
+    }
+  }
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.q_head_stride;
+  const int q0 = qt * BM;
+  int rows[2];
+  bf16x8_t qf[2][8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    rows[b] = q0 + c.wave * 64 + b * 32 + c.lr;
+    const int rr = rows[b] < a.Lq ? rows[b] : a.Lq - 1;
+    c.kvis[b] = a.Lhist + a.block_end[block_of_row(a, rr)];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[b][kk] = in_agprs(rows[b] < a.Lq ? *reinterpret_cast<const bf16x8_t*>(qb + (int64_t)rows[b] * D + kk * 16 + c.hi * 8)
+                                          : bf16x8_t{});
+  }
+  const int last = (q0 + BM < a.Lq ? q0 + BM : a.Lq) - 1;
+  const int kend = a.Lhist + a.block_end[block_of_row(a, last)];
+  const int kfree = a.Lhist + a.block_end[block_of_row(a, q0)];
+  const int nt = (kend + BN - 1) / BN;
+  const int n_free = kfree / BN;  // >= 1: every row sees at least the first block's T >= 64 keys
+
+  f32x16_t o[2][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[b][db] = in_agprs(f32x16_t{});
+  float m_ref[2], l_part[2] = {0.0f, 0.0f}, sum[2];
+  f32x16_t negm[2];
+  f32x16_t s0[2][2], s1[2][2];
+  u32x4_t p0[2][4], p1[2][4];
+  Stream st{0, 0, frame_base(c.g, 0), frame_base(c.g, 1)};
+  for (int t = 0; t < NS - 1; ++t) issue(c, t, st);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tiles 0 and 1 landed
+  __syncthreads();
+
+  // tile 0: scores from 0; the reference m_ref = the row's largest; A's exponentials
+  {
+    bf16x8_t vf[VAHEAD + 1];
+    phase_x<0, false, -2, true, false>(c, 0, qf, negm, s0, s1[0], p1[0], sum[1], vf, []() {});
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float mx = fmaxf(s0[b][0][0], s0[b][1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[b][0][r], s0[b][1][r]));
+    m_ref[b] = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      negm[b][r] = -m_ref[b];
+      s0[b][0][r] -= m_ref[b];
+      s0[b][1][r] -= m_ref[b];
+    }
+  }
+  sum[0] = exp_all(s0[0], p0[0]);
+
+  // Free tiles, pipelined, in passes of four (the ring slots are compile-time constants;
+  // the state alternates between (s0, p0) and (s1, p1) and is back in (s0, p0) after a
+  // pass).  An overflowing tile sum only sets `raised`.
+  int i = 0;
+  bool raised = false;
+  static_assert(NS == 4, "the unrolled loop below walks the slots 0, 1, 2, 3");
+  while (i + 4 < n_free) {
+    iteration<1, 0>(c, i, st, qf, o, s0, s1, p0, p1, sum, l_part, negm, raised);
+    iteration<2, 1>(c, i + 1, st, qf, o, s1, s0, p1, p0, sum, l_part, negm, raised);
+    iteration<3, 2>(c, i + 2, st, qf, o, s0, s1, p0, p1, sum, l_part, negm, raised);
+    iteration<0, 3>(c, i + 3, st, qf, o, s1, s0, p1, p0, sum, l_part, negm, raised);
+    i += 4;
+  }
+  drain_o(o);
+  // tile i (slot 0); then the rest -- the last free tiles and those past n_free, which
+  // need the per-element mask -- unpipelined
+  finish_tile(c, i, st, o, s0, p0, sum, l_part, raised);
+  for (++i; i < nt; ++i) {
+    switch (i & 3) {
+      case 0: single_tile<0>(c, i, st, qf, o, s0, p0, sum, l_part, negm, raised); break;
+      case 1: single_tile<1>(c, i, st, qf, o, s0, p0, sum, l_part, negm, raised); break;
+      case 2: single_tile<2>(c, i, st, qf, o, s0, p0, sum, l_part, negm, raised); break;
+      default: single_tile<3>(c, i, st, qf, o, s0, p0, sum, l_part, negm, raised); break;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
+
+  int bad = 0;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float l = l_part[b] + __shfl_xor(l_part[b], 32);
+    const float inv = 1.0f / l;
+    bool ok = l > 0.0f && l < 3.0e38f;
+    float outv[4][16];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        outv[db][r] = o[b][db][r] * inv;
+        ok = ok && (fabsf(outv[db][r]) < 3.0e38f);
+      }
+    const int row = rows[b];
+    if (row < a.Lq) {
+      bad |= (ok && !raised) ? 0 : 1;
+      uint16_t* ob = static_cast<uint16_t*>(a.out) + ((int64_t)row * a.H + h) * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int d0 = db * 32 + jg * 8 + c.hi * 4;
+          uint2 w2;
+          w2.x = pack_bf16x2(outv[db][jg * 4 + 0], outv[db][jg * 4 + 1]);
+          w2.y = pack_bf16x2(outv[db][jg * 4 + 2], outv[db][jg * 4 + 3]);
+          *reinterpret_cast<uint2*>(ob + d0) = w2;
+        }
+      if (c.hi == 0 && a.lse) a.lse[(int64_t)h * a.Lq + row] = (m_ref[b] + log2f(l)) * 0.6931471805599453f;
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0 && a.flags) a.flags[item] = bad;
+}
+
+
 template <int D>
 __global__ __launch_bounds__(64) void k_attn_f32(const AttnArgs a) {
   constexpr int BN = 32;
@@ -957,7 +1493,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t op_dtype, hipStream_t s) 
       if (a.v_fp8) {
         hipLaunchKernelGGL(k_attn_bf16_d128<true>, dim3(items), dim3(64 * d128::WAVES), 0, s, a);
       } else {
-        hipLaunchKernelGGL(k_attn_bf16_d128<false>, dim3(items), dim3(64 * d128::WAVES), 0, s, a);
+        hipLaunchKernelGGL(k_attn_bf16_d128_dual, dim3(items), dim3(64 * d128dual::WAVES), 0, s, a);
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
