@@ -508,6 +508,30 @@ def test_bf16_d128_short_frames_stream():
     say(f"bf16 d128 T=16 stream: worst rel L2 {worst:.3e}")
 
 
+@pytest.mark.parametrize("grid_w", [8, 12], ids=["t64", "t96"])
+def test_bf16_d128_dual_kernel_tile_counts(grid_w):
+    """The dual-block kernel's control flow over every short key-tile count.  T = 64 (one
+    key tile per frame) or 96 (tiles straddle frames, a ragged last tile when the frame
+    count is odd); one-frame blocks from an empty cache up to the full context of 4 memory
+    + 4 window + 1 block frames, so 1 to 9 (T = 64) or 2 to 14 (T = 96) key tiles: no
+    pipelined pass, one or two passes of four and every remainder after them; every fifth
+    call two frames split into two query blocks (masked tiles).  Every row against the
+    oracle, with the per-head and per-row checks."""
+    w = synth.workload("s512_bf16", heads=2, grid_h=8, grid_w=grid_w, window_frames=4, mem_slots=4,
+                       max_block_frames=4)
+    run = Runner(w)
+    worst = 0.0
+    for s in range(24):
+        blocks = [1, 1] if s % 5 == 4 else None
+        res = run.step(2 if blocks else 1, blocks=blocks, form=0 if blocks else 1)
+        err, dl = run.compare_attention(res)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16], (s, err, dl)
+        assert_state_matches(run)
+    assert_memory_bitexact(run)
+    say(f"dual kernel tile counts, T = {8 * grid_w}: worst rel L2 {worst:.3e}")
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_s512_bf16_step_parity_other_seeds(seed):
     """The 512x512 bf16 step on two more input seeds (sampled rows of all heads)."""
