@@ -532,6 +532,36 @@ def test_bf16_d128_dual_kernel_tile_counts(grid_w):
     say(f"dual kernel tile counts, T = {8 * grid_w}: worst rel L2 {worst:.3e}")
 
 
+@pytest.mark.parametrize("name", ["s512_bf16", "fp8_kv"])
+def test_attention_repeats_bit_identical_and_unflagged(name):
+    """The 512x512 step's attention (bf16 cache: the dual-block kernel; FP8: the lockstep
+    one) called three times on one staged block, memory full: outputs and LSE bit-identical
+    (the kernels have fixed reduction orders, so a difference would mean a race in the LDS
+    ring or a result used before its MFMA wrote it), and no query tile handed to the exact
+    pass on these inputs."""
+    w = synth.workload(name)
+    run = Runner(w, with_oracle=False)
+    for n in synth.block_sizes(w, 11):
+        run.step(n, attend=False)
+    (q, _), (k, _), (v, _) = run.inputs(8)
+    run.cache.rope_reset_apply(q, k, v)
+    T, H = w["tokens"], w["heads"]
+    got = []
+    for _ in range(3):
+        lse = torch.empty((H, 8 * T), dtype=torch.float32, device="cuda")
+        out = run.cache.block_attention(lse=lse)
+        torch.cuda.synchronize()
+        got.append((out.clone(), lse.clone()))
+    n_items = (8 * T + 255) // 256 * H
+    flags = run.cache.buf[run.cache.layout.attn_flags:].view(torch.int32)[:n_items].cpu().numpy()
+    say(f"{name}: flagged tiles {int(flags.sum())} of {n_items}, repeats identical "
+        f"{[torch.equal(o, got[0][0]) and torch.equal(l, got[0][1]) for o, l in got[1:]]}")
+    assert flags.max() == 0
+    assert torch.isfinite(got[0][0].float()).all()
+    for o, l in got[1:]:
+        assert torch.equal(o, got[0][0]) and torch.equal(l, got[0][1])
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_s512_bf16_step_parity_other_seeds(seed):
     """The 512x512 bf16 step on two more input seeds (sampled rows of all heads)."""
