@@ -896,9 +896,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
 // Key tile ring, copies, swizzles, fragment layouts, the lazy reference (the first tile's
 // row maximum, folded into the start of every QK^T chain) and the flags are those of
 // k_attn_bf16_d128.  Differences:
-//   * a tile sum that reaches 2^64 (scores far above the reference) is not rescaled in
-//     place: the wave records it, finishes, and the workgroup flags its rows for the exact
-//     pass;
+//   * the reference lies a fixed margin above the first tile's row maximum, and a tile
+//     sum that still threatens the f32 range (scores far above the reference) is not
+//     rescaled in place: the wave records it, finishes, and the workgroup flags its rows
+//     for the exact pass (the margin and threshold at MDELTA, OVF);
 //   * the free tiles run in pipelined passes of four (ring slots as compile-time
 //     constants); the pass remainder and the tiles that need a per-element mask run
 //     unpipelined after them.
@@ -918,6 +919,15 @@ constexpr int LDS_BYTES = 2 * NS * TILE_BYTES;
 constexpr int VMEM_PER_TILE = 8;            // copy instructions per wave per tile: K 4, V 4
 constexpr int KAHEAD = 2;                   // K fragment pairs read ahead of their MFMAs
 constexpr int VAHEAD = 2;                   // V^T fragments read ahead (each feeds two MFMAs)
+// The reference starts MDELTA above the row's largest score of the first tile, and a tile
+// sum of probabilities of OVF = 2^108 or more flags the rows for the exact pass: scores up
+// to about 108 + MDELTA - 6 above the first tile's largest stay in the kernel (keys with
+// outlier channels reach well past 64), the first tile's largest probability is 2^-MDELTA,
+// far from f32 underflow, and l and O (at most l times the largest |V|) stay far below
+// f32 overflow for any V of ordinary size; a V large enough to overflow O gives a
+// non-finite output, which flags the rows too.
+constexpr int MDELTA = 56;
+constexpr float OVF = 0x1p108f;
 
 using d128::Geo;
 using d128::Stream;
@@ -1168,11 +1178,11 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int key0, int hi, in
     }
 }
 
-// True when some lane's tile sum reached 2^64: its row met scores far above the reference.
-// The kernel then finishes its tiles (their results are discarded) and flags its rows for
-// the exact pass.
+// True when some lane's tile sum reached OVF (or is not finite): its row met scores far
+// above the reference.  The kernel then finishes its tiles (their results are discarded)
+// and flags its rows for the exact pass.
 __device__ __forceinline__ bool overflow(const float (&sum)[2]) {
-  return __builtin_expect(__any(!(sum[0] < 0x1p64f) || !(sum[1] < 0x1p64f)), 0);
+  return __builtin_expect(__any(!(sum[0] < OVF) || !(sum[1] < OVF)), 0);
 }
 
 // End of a tile: every copy but the last tile's (VMEM_PER_TILE per wave) has landed, and
@@ -1339,7 +1349,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16_d128_dual(const AttnArgs a
     float mx = fmaxf(s0[b][0][0], s0[b][1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[b][0][r], s0[b][1][r]));
-    m_ref[b] = fmaxf(mx, __shfl_xor(mx, 32));
+    m_ref[b] = fmaxf(mx, __shfl_xor(mx, 32)) + (float)MDELTA;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       negm[b][r] = -m_ref[b];
@@ -1411,6 +1421,643 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16_d128_dual(const AttnArgs a
   if (threadIdx.x == 0 && a.flags) a.flags[item] = bad;
 }
 
+
+// ---------------------------------------------------------------------------------------
+// k_attn_f8v_d128_dual: the D = 128 kernel for an FP8 cache's e4m3 V (T >= 64), in the
+// two-block layout of k_attn_bf16_d128_dual (one wave per SIMD, 32-row blocks A and B):
+//
+//     X(i): S~(i+1) = Q K(i+1)^T + log2 s_v - m for A and B (36 bf16 MFMAs: each chain
+//           starts with one 16-channel step that adds the keys' log2 s_v to -m), beside
+//           A's e4m3 conversion and B's exponentials, row sum and conversion of tile i
+//     Y(i): O^T += V(i)^T P~(i)^T for A and B on the stored e4m3 codes (8 MFMAs of 64
+//           keys on v_mfma_scale_f32_32x32x64_f8f6f4) beside A's exponentials and row
+//           sum of tile i + 1
+//
+// P~ = 2^(s + log2 s_v - m) = P' s_v, with P' = 2^(s - m) the probability and s_v the
+// key's V row scale, so that the V codes times P~ give P' V.  Instead of a reference that
+// is raised when P~ outgrows e4m3, every row scales each tile by its own power of two:
+// 2^(E_h + e) bounds the tile's largest P~ (s_v < 2^E_h for every key of the head, and
+// the row's sum of P' over the tile's 64 keys, below 2^e, bounds each P'), the codes are
+// e4m3(P~ 2^-E) with E = E_h + e - 8, all below 2^8, and the MFMA's E8M0 block scale of
+// the P~ operand multiplies 2^E back in.  O is never rescaled: the reference m lies a
+// fixed margin above the row's largest s + log2 s_v over the first tile, and only a tile
+// sum of P' that threatens f32 range flags the rows for the exact pass (the margin and
+// the threshold at the constants MDELTA, OVF).  Copies, swizzles and fragment
+// layouts are those of k_attn_bf16_d128 (FP8 form); the pipelining, registers and
+// inline-asm MFMAs those of k_attn_bf16_d128_dual.
+// ---------------------------------------------------------------------------------------
+namespace d128dual8 {
+
+constexpr int D = 128, BM = 256, BN = 64, NS = 4, WAVES = 4;
+constexpr int ROW_BYTES = D * 2;                 // a bf16 key row
+constexpr int TILE_BYTES = BN * ROW_BYTES;       // 16 KiB of keys per ring slot
+constexpr int V8_ROW = D;                        // an e4m3 V row
+constexpr int V8_TILE = BN * V8_ROW;             // 8 KiB of V codes per slot
+constexpr int S_TILE = BN * 8;                   // per slot: 1/s_v and log2 s_v of 64 keys
+constexpr int V_RING = NS * TILE_BYTES;
+constexpr int S_RING = V_RING + NS * V8_TILE;
+constexpr int LDS_BYTES = S_RING + NS * S_TILE;  // 98 KiB
+constexpr int VMEM_PER_TILE = 7;                 // copies per wave and tile: K 4, V 2, scales 1
+constexpr int KAHEAD = 2;                        // K fragment pairs read ahead of their MFMAs
+
+using d128::Geo;
+using d128::Stream;
+using d128::copy_dword_to_lds;
+using d128::copy_to_lds;
+using d128::frame_base;
+using d128::lds_v2i32;
+using d128::step_fence;
+using d128::swz;
+using d128::v2i32;
+using d128::v8i32;
+using d128dual::drain_o;
+using d128dual::in_agprs;
+using d128dual::MDELTA;
+using d128dual::mask_tile;
+using d128dual::overflow;
+using d128dual::qk_next;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+
+struct Ctx {
+  Geo g;
+  const char* kbase;   // this head's rotated keys [Lk][128]
+  char* lds;
+  unsigned lds_u32;
+  int wave, lane, hi, lr;
+  int kvis[2];         // keys visible to the lane's row of block A / B
+  int64_t hrow;        // bytes between consecutive tokens of one V frame (H * 128)
+  int crow[4];         // K copies: the four 4-row groups of a tile this lane copies
+  int koff[4];
+  int vrow[2];         // V copies: the two 8-row groups
+  int voff[2];
+  int kread[8];        // K fragment reads (LDS byte offsets from the ring base, slot 0)
+  int vread[4];        // first of the four 8-key transposed reads of V^T fragment db
+  int sread;           // 1/s_v of the lane's keys, chunk 0 (+ 128 B per 8-key chunk)
+  int lread[2];        // log2 s_v pair of the A-operand key row of key block kb
+  const char* vsbase;  // scale-term copy source of this lane (1/s_v or log2 pairs)
+  int eh8;             // E_h - 8
+  bf16x8_t augb;       // B operand of the log2 s_v step: bf16 (1, 1) in channels 0, 1
+};
+
+template <int SLOT>
+__device__ __forceinline__ int slot_of(int j) { return SLOT >= 0 ? SLOT : j % NS; }
+
+// Copy tile t's 64 key rows of K, V codes and V scale terms into ring slot t % NS (this
+// wave: rows 16 wave .. 16 wave + 15), then advance the stream.
+__device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
+  const Geo& a = c.g;
+  const unsigned slot = (unsigned)(t % NS);
+  const unsigned kdst = c.lds_u32 + slot * TILE_BYTES + (unsigned)c.wave * 16 * ROW_BYTES;
+  const unsigned vdst = c.lds_u32 + V_RING + slot * V8_TILE + (unsigned)c.wave * 16 * V8_ROW;
+  if ((t + 1) * BN <= a.Lk) {
+    const char* ktile = c.kbase + (int64_t)t * TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy_to_lds(ktile + c.koff[i], kdst + i * 4 * ROW_BYTES);
+  } else {  // rows past the last key repeat it
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int key = t * BN + c.crow[i];
+      key = key < a.Lk ? key : a.Lk - 1;
+      copy_to_lds(c.kbase + (int64_t)key * ROW_BYTES + (c.koff[i] & (ROW_BYTES - 1)), kdst + i * 4 * ROW_BYTES);
+    }
+  }
+  const char* vA = st.baseA + st.u0 * c.hrow;
+  if (st.u0 + BN <= a.T) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy_to_lds(vA + c.voff[i], vdst + i * 8 * V8_ROW);
+  } else {
+    const char* vB = st.baseB + (st.u0 - a.T) * c.hrow;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      copy_to_lds((st.u0 + c.vrow[i] >= a.T ? vB : vA) + c.voff[i], vdst + i * 8 * V8_ROW);
+  }
+  // scale terms of keys 16 wave .. 16 wave + 15: lanes 16 g .. 16 g + 7 the 1/s_v and lanes
+  // 16 g + 8 .. 16 g + 15 the log2 pairs of keys 16 wave + 8 g + (lane mod 8).  The planes
+  // are zero-padded to a multiple of 64 keys; tiles copied past the end re-read the last group.
+  if (c.lane < 32) {
+    const int key0 = min(t * BN + c.wave * 16 + (c.lane >> 4) * 8, a.s_last);
+    copy_dword_to_lds(c.vsbase + (int64_t)key0 * 4, c.lds_u32 + S_RING + slot * S_TILE + (unsigned)c.wave * 128);
+  }
+  st.u0 += BN;  // T >= BN: at most one frame boundary per tile
+  if (st.u0 >= a.T) {
+    st.u0 -= a.T;
+    st.f0 += 1;
+    st.baseA = st.baseB;
+    st.baseB = frame_base(c.g, st.f0 + 1);
+  }
+}
+
+// The MFMAs beyond k_attn_bf16_d128_dual's (same conventions: scores in VGPRs, O in AGPRs,
+// the generated code checked for wait states by the tests).  aug_first starts a QK^T
+// chain: d = A B + init with A the key rows' (hi, lo) bf16 pairs of log2 s_v and B = augb.
+__device__ __forceinline__ f32x16_t aug_first(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& init) {
+  f32x16_t d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(init));
+  return d;
+}
+// O^T += V^T P~^T: 32 channels x 64 keys of e4m3 codes; the P~ operand's block scale is the
+// E8M0 byte eb (both 32-key blocks of a column), the V operand's 1.0 (one = 127).
+__device__ __forceinline__ void pv_mfma8(f32x16_t& o, const v8i32& v, const v8i32& p, int one, int eb) {
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+a"(o)
+               : "v"(v), "v"(p), "v"(one), "v"(eb));
+}
+
+// x + the value of the lane 32 apart (lanes j and j + 32 hold the same query row); the
+// wait states are those a VALU write needs before the swap reads its operands.
+__device__ __forceinline__ float pair_sum(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+
+// E8M0 byte 127 + E of a block's tile from the lane's sum of P' (see above), clamped to
+// the finite scales (the clamp only ever lowers the codes).
+__device__ __forceinline__ int tile_scale(float sum, int eh8) {
+  const int e = __builtin_amdgcn_frexp_expf(pair_sum(sum)) + eh8 + 127;
+  return min(max(e, 1), 254);
+}
+
+// Word w of a block's P~ operand: bytes 4 w .. 4 w + 3 are e4m3(P~ 2^-E) of the values
+// 4 w .. 4 w + 3 of s (the byte order of the V^T fragments); eb = 127 + E.
+__device__ __forceinline__ void conv_word(const f32x16_t (&s)[2], v8i32& p, int w, int eb) {
+  const float scale = __builtin_bit_cast(float, eb << 23);
+  const f32x16_t& v = s[w >> 2];
+  const int b0 = 4 * (w & 3);
+  v2i16 x = __builtin_bit_cast(v2i16, p[w]);
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, v[b0], v[b0 + 1], scale, false);
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, v[b0 + 2], v[b0 + 3], scale, true);
+  p[w] = __builtin_bit_cast(int, x);
+}
+
+__device__ __forceinline__ bf16x8_t kfrag(const char* kb, const Ctx& c, int kk, int kb2) {
+  return *reinterpret_cast<const bf16x8_t*>(kb + c.kread[kk] + kb2 * 32 * ROW_BYTES);
+}
+// A operand of the log2 s_v step of key block kb: (hi, lo, 0, ...) of the row's key.
+__device__ __forceinline__ bf16x8_t aug_frag(const char* sb, const Ctx& c, int kb) {
+  const u32x4_t w = {*reinterpret_cast<const uint32_t*>(sb + c.lread[kb]), 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+// V^T fragment of channels 32 db .. 32 db + 31 (the lane's 32 keys): four transposing
+// 8-bit reads of 8 keys each.
+__device__ __forceinline__ v8i32 vfrag(const char* vb, const Ctx& c, int db) {
+  v8i32 f;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const v2i32 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(vb + c.vread[db] + cc * 16 * V8_ROW));
+    f[2 * cc] = x[0];
+    f[2 * cc + 1] = x[1];
+  }
+  return f;
+}
+// 1/s_v of the keys of values 8 ch .. 8 ch + 7 of a block's tile.
+__device__ __forceinline__ void read_inv(const char* sb, const Ctx& c, int ch, float (&inv)[8]) {
+  const float4 i0 = *reinterpret_cast<const float4*>(sb + c.sread + ch * 128);
+  const float4 i1 = *reinterpret_cast<const float4*>(sb + c.sread + ch * 128 + 16);
+  inv[0] = i0.x; inv[1] = i0.y; inv[2] = i0.z; inv[3] = i0.w;
+  inv[4] = i1.x; inv[5] = i1.y; inv[6] = i1.z; inv[7] = i1.w;
+}
+
+// Softmax step e (0..31) of one block's tile: P~_e = exp2(s_e) in place and the previous
+// value's P' = P~ / s_v into the row sum (the FMA never waits on the exponential it
+// follows); at e = 8 ch the 1/s_v of chunk ch + 1 are read into the buffer chunk ch - 1
+// used.  exp_finish adds the last value.
+__device__ __forceinline__ void exp_step(const char* sb, const Ctx& c, f32x16_t (&s)[2], float& sum,
+                                         float (&inv)[2][8], int e) {
+  s[e >> 4][e & 15] = __builtin_amdgcn_exp2f(s[e >> 4][e & 15]);
+  if (e > 0) {
+    const int f = e - 1;
+    sum = __builtin_fmaf(s[f >> 4][f & 15], inv[(f >> 3) & 1][f & 7], sum);
+  }
+  if ((e & 7) == 0 && e < 24) read_inv(sb, c, (e >> 3) + 1, inv[((e >> 3) + 1) & 1]);
+}
+__device__ __forceinline__ void exp_finish(const f32x16_t (&s)[2], float& sum, const float (&inv)[2][8]) {
+  sum = __builtin_fmaf(s[1][15], inv[1][7], sum);
+}
+
+__device__ __forceinline__ void pin(v8i32& p, float& sum) {
+  asm volatile("" : "+v"(p));
+  asm volatile("" : "+v"(sum));
+}
+
+// The softmax work beside X-phase step j (0..35): A's codes (one word per step 0-7), B's
+// exponentials (steps 0-31), B's scale (32) and codes (33-35).
+__device__ __forceinline__ void soft_x(const Ctx& c, const char* sv, f32x16_t (&sc)[2][2], v8i32 (&pc)[2],
+                                       int (&eb)[2], float (&sum)[2], float (&inv)[2][8], int j) {
+  if (j < 8) conv_word(sc[0], pc[0], j, eb[0]);
+  if (j < 32) exp_step(sv, c, sc[1], sum[1], inv, j);
+  if (j == 32) {
+    exp_finish(sc[1], sum[1], inv);
+    eb[1] = tile_scale(sum[1], c.eh8);
+  }
+  if (j == 33) {
+    conv_word(sc[1], pc[1], 0, eb[1]);
+    conv_word(sc[1], pc[1], 1, eb[1]);
+    conv_word(sc[1], pc[1], 2, eb[1]);
+  }
+  if (j == 34) {
+    conv_word(sc[1], pc[1], 3, eb[1]);
+    conv_word(sc[1], pc[1], 4, eb[1]);
+    conv_word(sc[1], pc[1], 5, eb[1]);
+  }
+  if (j == 35) {
+    conv_word(sc[1], pc[1], 6, eb[1]);
+    conv_word(sc[1], pc[1], 7, eb[1]);
+  }
+}
+
+// X phase on slot KS (tile t): sn[b] = Q_b K(t)^T + log2 s_v - m_b for both blocks (from
+// the broadcast -m of the rows, negm; INIT0: from 0).  SOFT, beside it (tile t - 1, slot
+// VS): block A's codes from its exponentials sc[0] and their sum; block B's exponentials
+// of sc[1], their sum, scale and codes.  mid() runs after the sixth MFMA (the copies);
+// VS >= 0: the last steps also read the first two V^T fragments of the Y phase into vf.
+// ASM: the inline-asm MFMAs of the pipelined passes; otherwise builtins (prologue, tail).
+template <int KS, bool SOFT, int VS = -2, bool INIT0 = false, bool ASM = true, typename Mid>
+__device__ __forceinline__ void phase_x(const Ctx& c, int t, const bf16x8_t (&qf)[2][8], const f32x16_t (&negm)[2],
+                                        f32x16_t (&sn)[2][2], f32x16_t (&sc)[2][2], v8i32 (&pc)[2], int (&eb)[2],
+                                        float (&sum)[2], v8i32 (&vf)[2], Mid mid) {
+  static_assert(!(ASM && INIT0), "the asm MFMAs start from negm");
+  static_assert(!SOFT || VS >= 0, "the softmax reads the scale terms of slot VS");
+  const char* kb = c.lds + slot_of<KS>(t) * TILE_BYTES;
+  const char* sk = c.lds + slot_of<KS>(t) * S_TILE;
+  const char* sv = c.lds + (VS >= 0 ? VS : 0) * S_TILE;
+  bf16x8_t kf[KAHEAD + 1][2];
+  bf16x8_t ag[2];
+  float inv[2][8];
+  ag[0] = aug_frag(sk, c, 0);
+  ag[1] = aug_frag(sk, c, 1);
+  asm volatile("" : "+v"(ag[0]), "+v"(ag[1]));  // built here, not next to their MFMAs
+#pragma unroll
+  for (int kk = 0; kk < KAHEAD; ++kk) {
+    kf[kk][0] = kfrag(kb, c, kk, 0);
+    kf[kk][1] = kfrag(kb, c, kk, 1);
+  }
+  if (SOFT) {
+    read_inv(sv, c, 0, inv[0]);
+    eb[0] = tile_scale(sum[0], c.eh8);
+    sum[1] = 0.0f;
+  }
+  step_fence();
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {  // steps 0-3: the log2 s_v steps start the four chains
+    const int blk = m & 1, kb2 = m >> 1;
+    if (ASM)
+      sn[blk][kb2] = aug_first(ag[kb2], c.augb, negm[blk]);
+    else
+      sn[blk][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[kb2], c.augb, INIT0 ? f32x16_t{} : negm[blk], 0, 0, 0);
+    if (SOFT) soft_x(c, sv, sc, pc, eb, sum, inv, m);
+    step_fence();
+  }
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {  // steps 4-35
+      const int blk = m & 1, kb2 = m >> 1, j = 4 + 4 * kk + m;
+      if (m == 0 && kk + KAHEAD < 8) {
+        kf[(kk + KAHEAD) % (KAHEAD + 1)][0] = kfrag(kb, c, kk + KAHEAD, 0);
+        kf[(kk + KAHEAD) % (KAHEAD + 1)][1] = kfrag(kb, c, kk + KAHEAD, 1);
+      }
+      const bf16x8_t& kfr = kf[kk % (KAHEAD + 1)][kb2];
+      if (ASM)
+        qk_next(sn[blk][kb2], kfr, qf[blk][kk]);
+      else
+        sn[blk][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[blk][kk], sn[blk][kb2], 0, 0, 0);
+      if (SOFT) soft_x(c, sv, sc, pc, eb, sum, inv, j);
+      if (j == 5) mid();
+      if (VS >= 0 && (j == 32 || j == 33)) vf[j - 32] = vfrag(c.lds + VS * V8_TILE, c, j - 32);
+      step_fence();
+    }
+  }
+  if (SOFT) {
+    pin(pc[0], sum[0]);
+    pin(pc[1], sum[1]);
+  }
+}
+
+// Y phase on slot VS (tile t): o[b] += V^T P~_b^T for both blocks, fragment by fragment
+// (A, B for channel block db), beside (SOFT) block A's exponentials and row sum of tile
+// t + 1 (scores sa, scale terms in slot SA).  PRE: the first two fragments are already in
+// vf.  ASM: as for phase_x.
+template <int VS, bool SOFT, bool PRE = false, bool ASM = true>
+__device__ __forceinline__ void phase_y(const Ctx& c, int t, const v8i32 (&pc)[2], const int (&eb)[2],
+                                        f32x16_t (&o)[2][4], f32x16_t (&sa)[2], float& suma, v8i32 (&vf)[2],
+                                        int one) {
+  constexpr int SA = VS >= 0 ? (VS + 1) % NS : 0;
+  const char* vb = c.lds + slot_of<VS>(t) * V8_TILE;
+  const char* sb = c.lds + SA * S_TILE;
+  float inv[2][8];
+  if (!PRE) {
+    vf[0] = vfrag(vb, c, 0);
+    vf[1] = vfrag(vb, c, 1);
+  }
+  if (SOFT) {
+    suma = 0.0f;
+    read_inv(sb, c, 0, inv[0]);
+  }
+  step_fence();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = i & 1, db = i >> 1;
+    if (ASM)
+      pv_mfma8(o[b][db], vf[db & 1], pc[b], one, eb[b]);
+    else
+      o[b][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db & 1], pc[b], o[b][db], 0, 0, 0, 127, 0, eb[b]);
+    if (b == 1 && db + 2 < 4) vf[db & 1] = vfrag(vb, c, db + 2);
+    if (SOFT) {
+#pragma unroll
+      for (int e = 4 * i; e < 4 * i + 4; ++e) exp_step(sb, c, sa, suma, inv, e);
+    }
+    step_fence();
+  }
+  if (SOFT) {
+    exp_finish(sa, suma, inv);
+    asm volatile("" : "+v"(suma));
+  }
+}
+
+// All 32 exponentials of one block's tile and their sum of P', unpipelined.
+__device__ __forceinline__ float exp_all(const char* sb, const Ctx& c, f32x16_t (&s)[2]) {
+  float sum = 0.0f, inv[2][8];
+  read_inv(sb, c, 0, inv[0]);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    exp_step(sb, c, s, sum, inv, e);
+    if ((e & 7) == 7) step_fence();  // keeps the temporaries few
+  }
+  exp_finish(s, sum, inv);
+  return sum;
+}
+__device__ __forceinline__ void conv_all(const f32x16_t (&s)[2], v8i32& p, int eb) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) conv_word(s, p, w, eb);
+}
+
+__device__ __forceinline__ void tile_end() {
+  static_assert(VMEM_PER_TILE == 7, "the wait count below leaves one tile's copies in flight");
+  asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  __syncthreads();
+}
+
+// One pipelined iteration: X on tile i + 1's K (slot KS), Y on tile i's V (slot VS).
+// sc: tile i's scores (A's already exponentiated), sn: tile i + 1's.
+template <int KS, int VS>
+__device__ __forceinline__ void iteration(const Ctx& c, int i, Stream& st, const bf16x8_t (&qf)[2][8],
+                                          f32x16_t (&o)[2][4], f32x16_t (&sc)[2][2], f32x16_t (&sn)[2][2],
+                                          v8i32 (&pc)[2], int (&eb)[2], float (&sum)[2], float (&l_part)[2],
+                                          const f32x16_t (&negm)[2], bool& ovf, int one) {
+  static_assert(KS == (VS + 1) % NS, "X reads the slot after Y's");
+  v8i32 vf[2];
+  phase_x<KS, true, VS>(c, i + 1, qf, negm, sn, sc, pc, eb, sum, vf, [&]() { issue(c, i + NS - 1, st); });
+  ovf |= overflow(sum);
+  l_part[0] += sum[0];
+  l_part[1] += sum[1];
+  phase_y<VS, true, true>(c, i, pc, eb, o, sn[0], sum[0], vf, one);
+  tile_end();
+}
+
+// Tile i (slot 0) after the pipelined passes: A's codes, B's exponentials and codes, PV.
+__device__ __forceinline__ void finish_tile(const Ctx& c, int i, Stream& st, f32x16_t (&o)[2][4],
+                                            f32x16_t (&sc)[2][2], v8i32 (&pc)[2], int (&eb)[2], float (&sum)[2],
+                                            float (&l_part)[2], bool& ovf, int one) {
+  issue(c, i + NS - 1, st);
+  const char* sb = c.lds;  // slot 0's scale terms: S_RING is in the offsets
+  eb[0] = tile_scale(sum[0], c.eh8);
+  conv_all(sc[0], pc[0], eb[0]);
+  sum[1] = exp_all(sb, c, sc[1]);
+  eb[1] = tile_scale(sum[1], c.eh8);
+  conv_all(sc[1], pc[1], eb[1]);
+  ovf |= overflow(sum);
+  l_part[0] += sum[0];
+  l_part[1] += sum[1];
+  v8i32 vf[2];
+  float unused_sum;
+  phase_y<0, false, false, false>(c, i, pc, eb, o, sc[0], unused_sum, vf, one);
+  tile_end();
+}
+
+// One tile (slot SLOT), unpipelined, with the per-element mask (a no-op for free tiles).
+template <int SLOT>
+__device__ __forceinline__ void single_tile(const Ctx& c, int i, Stream& st, const bf16x8_t (&qf)[2][8],
+                                            f32x16_t (&o)[2][4], f32x16_t (&s)[2][2], v8i32 (&pc)[2], int (&eb)[2],
+                                            float (&sum)[2], float (&l_part)[2], const f32x16_t (&negm)[2],
+                                            bool& ovf, int one) {
+  issue(c, i + NS - 1, st);
+  f32x16_t unused_s[2][2];
+  v8i32 vf[2];
+  phase_x<SLOT, false, -2, false, false>(c, i, qf, negm, s, unused_s, pc, eb, sum, vf, []() {});
+  const char* sb = c.lds + SLOT * S_TILE;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    mask_tile(s[b], i * BN, c.hi, c.kvis[b]);
+    sum[b] = exp_all(sb, c, s[b]);
+    eb[b] = tile_scale(sum[b], c.eh8);
+    conv_all(s[b], pc[b], eb[b]);
+  }
+  ovf |= overflow(sum);
+  l_part[0] += sum[0];
+  l_part[1] += sum[1];
+  float unused_sum;
+  phase_y<SLOT, false, false, false>(c, i, pc, eb, o, s[0], unused_sum, vf, one);
+  tile_end();
+}
+
+}  // namespace d128dual8
+
+__global__ __launch_bounds__(256, 1) void k_attn_f8v_d128_dual(const AttnArgs a) {
+  using namespace d128dual8;
+  __shared__ __align__(1024) char lds[LDS_BYTES];
+
+  const int n_qt = (a.Lq + BM - 1) / BM;
+  const int item = xcd_item(blockIdx.x, n_qt * a.H);  // one head's tiles on one XCD
+  const int h = item / n_qt, qt = item - h * n_qt;
+
+  Ctx c;
+  c.g.v_mem = static_cast<const char*>(a.v_mem);
+  c.g.v_ring = static_cast<const char*>(a.v_ring);
+  c.g.v_cur = static_cast<const char*>(a.v_cur);
+  c.g.v_ref = static_cast<const char*>(a.v_ref);
+  c.g.frame_bytes = (int64_t)a.T * a.H * V8_ROW;
+  c.g.T = a.T;
+  c.g.Lk = a.Lk;
+  c.g.nf = a.Lk / a.T;
+  c.g.ref_len = a.hist.ref_len;
+  c.g.mem_end = a.hist.ref_len + a.hist.mem_len;
+  c.g.nh = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
+  c.g.M = a.hist.M;
+  c.g.R = a.hist.R;
+  c.g.mem_slot0 = a.hist.mem_slot0;
+  c.g.ring_slot0 = a.hist.ring_slot0;
+  c.g.s_last = (a.Lk + BN - 1) / BN * BN - 8;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.lane = threadIdx.x & 63;
+  c.hi = c.lane >> 5;
+  c.lr = c.lane & 31;
+  c.lds = lds;
+  c.lds_u32 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  c.kbase = static_cast<const char*>(a.k) + (int64_t)h * a.k_head_stride * 2;
+  c.hrow = (int64_t)a.H * V8_ROW;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = c.wave * 16 + i * 4 + (c.lane >> 4);
+    c.crow[i] = r;
+    c.koff[i] = r * ROW_BYTES + ((c.lane & 15) ^ swz(r)) * 16;
+  }
+  // V copies: lane l moves 16 B of row 16 wave + 8 i + l / 8; its LDS position l mod 8
+  // holds the row's chunk (l mod 8) ^ (row mod 8), so the transposed reads (8 consecutive
+  // rows, one chunk) hit 8 different 16-byte positions
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = c.wave * 16 + i * 8 + (c.lane >> 3);
+    c.vrow[i] = r;
+    c.voff[i] = (r * a.H + h) * V8_ROW + ((c.lane & 7) ^ (r & 7)) * 16;
+  }
+  {
+    const int m = perm32(c.lr);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) c.kread[kk] = m * ROW_BYTES + (((2 * kk + c.hi) ^ swz(m)) * 16);
+    // V^T reads: 16-lane group g covers channels 16 (g mod 2) of the 32-channel block and
+    // keys 8 (g / 2) of each 16-key chunk; lane i addresses row i / 2, byte half i mod 2
+    const int g = c.lane >> 4, i = c.lane & 15;
+    const int vr = (g >> 1) * 8 + (i >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      c.vread[db] = V_RING + vr * V8_ROW + (((2 * db + (g & 1)) ^ (vr & 7)) * 16) + (i & 1) * 8;
+    c.sread = S_RING + c.hi * 64;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = kb * 32 + m;
+      c.lread[kb] = S_RING + (key >> 3) * 64 + 32 + (key & 7) * 4;
+    }
+  }
+  c.vsbase = reinterpret_cast<const char*>(a.vscale + ((c.lane & 15) < 8 ? 1 : 2) * a.vs_plane +
+                                           (int64_t)h * a.vs_head_stride + (c.lane & 7));
+  {
+    float smax = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kVmaxParts; ++p) smax = fmaxf(smax, a.vmax[h * kVmaxParts + p]);
+    // s_v < 2^E_h for every key of the head
+    const int eh = (smax > 0.0f && smax < INFINITY) ? __builtin_amdgcn_frexp_expf(smax) : 0;
+    c.eh8 = eh - 8;
+    const u32x4_t ones = {c.hi ? 0u : 0x3F803F80u, 0u, 0u, 0u};  // bf16 (1, 1, 0, ...)
+    c.augb = __builtin_bit_cast(bf16x8_t, ones);
+  }
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.q_head_stride;
+  const int q0 = qt * BM;
+  int rows[2];
+  bf16x8_t qf[2][8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    rows[b] = q0 + c.wave * 64 + b * 32 + c.lr;
+    const int rr = rows[b] < a.Lq ? rows[b] : a.Lq - 1;
+    c.kvis[b] = a.Lhist + a.block_end[block_of_row(a, rr)];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[b][kk] = in_agprs(rows[b] < a.Lq ? *reinterpret_cast<const bf16x8_t*>(qb + (int64_t)rows[b] * D + kk * 16 + c.hi * 8)
+                                          : bf16x8_t{});
+  }
+  const int last = (q0 + BM < a.Lq ? q0 + BM : a.Lq) - 1;
+  const int kend = a.Lhist + a.block_end[block_of_row(a, last)];
+  const int kfree = a.Lhist + a.block_end[block_of_row(a, q0)];
+  const int nt = (kend + BN - 1) / BN;
+  const int n_free = kfree / BN;  // >= 1: every row sees at least the first block's T >= 64 keys
+  int one;  // E8M0 1.0, the V operand's block scale, in a VGPR of its own (not rematerialised
+            // next to the asm MFMAs that read it)
+  asm volatile("v_mov_b32 %0, 127" : "=v"(one));
+
+  f32x16_t o[2][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[b][db] = in_agprs(f32x16_t{});
+  float m_ref[2], l_part[2] = {0.0f, 0.0f}, sum[2];
+  int eb[2];
+  f32x16_t negm[2];
+  f32x16_t s0[2][2], s1[2][2];
+  v8i32 pc[2] = {v8i32{}, v8i32{}};
+  Stream st{0, 0, frame_base(c.g, 0), frame_base(c.g, 1)};
+  for (int t = 0; t < NS - 1; ++t) issue(c, t, st);
+  asm volatile("s_waitcnt vmcnt(7)" ::: "memory");  // tiles 0 and 1 landed
+  __syncthreads();
+
+  // tile 0: scores + log2 s_v from 0; the reference m_ref = the row's largest; A's
+  // exponentials
+  {
+    v8i32 vf[2];
+    phase_x<0, false, -2, true, false>(c, 0, qf, negm, s0, s1, pc, eb, sum, vf, []() {});
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float mx = fmaxf(s0[b][0][0], s0[b][1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[b][0][r], s0[b][1][r]));
+    m_ref[b] = fmaxf(mx, __shfl_xor(mx, 32)) + (float)MDELTA;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      negm[b][r] = -m_ref[b];
+      s0[b][0][r] -= m_ref[b];
+      s0[b][1][r] -= m_ref[b];
+    }
+  }
+  sum[0] = exp_all(c.lds, c, s0[0]);
+
+  // Free tiles, pipelined, in passes of four (state in (s0, pc) between passes).
+  int i = 0;
+  bool raised = false;
+  static_assert(NS == 4, "the unrolled loop below walks the slots 0, 1, 2, 3");
+  while (i + 4 < n_free) {
+    iteration<1, 0>(c, i, st, qf, o, s0, s1, pc, eb, sum, l_part, negm, raised, one);
+    iteration<2, 1>(c, i + 1, st, qf, o, s1, s0, pc, eb, sum, l_part, negm, raised, one);
+    iteration<3, 2>(c, i + 2, st, qf, o, s0, s1, pc, eb, sum, l_part, negm, raised, one);
+    iteration<0, 3>(c, i + 3, st, qf, o, s1, s0, pc, eb, sum, l_part, negm, raised, one);
+    i += 4;
+  }
+  drain_o(o);
+  finish_tile(c, i, st, o, s0, pc, eb, sum, l_part, raised, one);
+  for (++i; i < nt; ++i) {
+    switch (i & 3) {
+      case 0: single_tile<0>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, raised, one); break;
+      case 1: single_tile<1>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, raised, one); break;
+      case 2: single_tile<2>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, raised, one); break;
+      default: single_tile<3>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, raised, one); break;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
+
+  int bad = 0;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float l = l_part[b] + __shfl_xor(l_part[b], 32);
+    const float inv = 1.0f / l;
+    bool ok = l > 0.0f && l < 3.0e38f;
+    float outv[4][16];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        outv[db][r] = o[b][db][r] * inv;
+        ok = ok && (fabsf(outv[db][r]) < 3.0e38f);
+      }
+    const int row = rows[b];
+    if (row < a.Lq) {
+      bad |= (ok && !raised) ? 0 : 1;
+      uint16_t* ob = static_cast<uint16_t*>(a.out) + ((int64_t)row * a.H + h) * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int d0 = db * 32 + jg * 8 + c.hi * 4;
+          uint2 w2;
+          w2.x = pack_bf16x2(outv[db][jg * 4 + 0], outv[db][jg * 4 + 1]);
+          w2.y = pack_bf16x2(outv[db][jg * 4 + 2], outv[db][jg * 4 + 3]);
+          *reinterpret_cast<uint2*>(ob + d0) = w2;
+        }
+      if (c.hi == 0 && a.lse) a.lse[(int64_t)h * a.Lq + row] = (m_ref[b] + log2f(l)) * 0.6931471805599453f;
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0 && a.flags) a.flags[item] = bad;
+}
 
 template <int D>
 __global__ __launch_bounds__(64) void k_attn_f32(const AttnArgs a) {
@@ -1491,7 +2138,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t op_dtype, hipStream_t s) 
     if (a.D == 128 && a.T >= d128::BN && a.flags) {
       const int items = ((a.Lq + d128::BM - 1) / d128::BM) * a.H;
       if (a.v_fp8) {
-        hipLaunchKernelGGL(k_attn_bf16_d128<true>, dim3(items), dim3(64 * d128::WAVES), 0, s, a);
+        hipLaunchKernelGGL(k_attn_f8v_d128_dual, dim3(items), dim3(64 * d128dual8::WAVES), 0, s, a);
       } else {
         hipLaunchKernelGGL(k_attn_bf16_d128_dual, dim3(items), dim3(64 * d128dual::WAVES), 0, s, a);
       }

@@ -1,4 +1,4 @@
-"""The inline-asm MFMAs of the attention kernel keep their wait states in the generated
+"""The inline-asm MFMAs of the attention kernels keep their wait states in the generated
 code (CPU: compiles k_attn.hip for gfx950 with the library's flags and checks the
 assembly), and the checker itself flags the cases it is meant to find."""
 import os
@@ -8,7 +8,10 @@ import pytest
 
 from asm_hazards import check
 
-KERNEL = "_ZN4lact21k_attn_bf16_d128_dualENS_8AttnArgsE"  # lact::k_attn_bf16_d128_dual(AttnArgs)
+KERNELS = {
+    "bf16": "_ZN4lact21k_attn_bf16_d128_dualENS_8AttnArgsE",  # lact::k_attn_bf16_d128_dual(AttnArgs)
+    "f8v": "_ZN4lact20k_attn_f8v_d128_dualENS_8AttnArgsE",    # lact::k_attn_f8v_d128_dual(AttnArgs)
+}
 
 SNIPPET = """{name}:
 \tv_mov_b32 v1, 0
@@ -32,16 +35,25 @@ def test_checker_accepts_separated_instructions():
     assert check(text, "k") == []
 
 
-@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not installed")
-def test_dual_kernel_inline_asm_mfma_hazards(tmp_path):
+@pytest.fixture(scope="module")
+def kernel_asm(tmp_path_factory):
     from compressed_kv_causal_amd import build as B
-    out = tmp_path / "k_attn.s"
+    out = tmp_path_factory.mktemp("asm") / "k_attn.s"
     cmd = ([B.HIPCC] + B.COMMON + ["--offload-device-only", "-S", "-o", str(out),
                                    os.path.join(B.CSRC, "k_attn.hip")])
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    text = out.read_text()
-    assert KERNEL + ":" in text
-    assert text.count("v_mfma_f32_32x32x16_bf16") > 0
-    issues = check(text, KERNEL)
+    return out.read_text()
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not installed")
+@pytest.mark.parametrize("which", sorted(KERNELS))
+def test_dual_kernel_inline_asm_mfma_hazards(kernel_asm, which):
+    kernel = KERNELS[which]
+    text = kernel_asm
+    assert kernel + ":" in text
+    body = text[text.index(kernel + ":"):]
+    body = body[:body.index("s_endpgm")]
+    assert body.count(";;#ASMSTART") > 0 and "v_mfma" in body
+    issues = check(text, kernel)
     assert issues == [], "\n".join(issues[:20])

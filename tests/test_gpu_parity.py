@@ -509,16 +509,19 @@ def test_bf16_d128_short_frames_stream():
 
 
 @pytest.mark.parametrize("grid_w", [8, 12], ids=["t64", "t96"])
-def test_bf16_d128_dual_kernel_tile_counts(grid_w):
-    """The dual-block kernel's control flow over every short key-tile count.  T = 64 (one
+@pytest.mark.parametrize("name", ["s512_bf16", "fp8_kv"], ids=["bf16", "fp8"])
+def test_d128_dual_kernel_tile_counts(name, grid_w):
+    """The two-block kernels' control flow (bf16 cache: k_attn_bf16_d128_dual; FP8 cache
+    with x8 outliers: k_attn_f8v_d128_dual) over every short key-tile count.  T = 64 (one
     key tile per frame) or 96 (tiles straddle frames, a ragged last tile when the frame
     count is odd); one-frame blocks from an empty cache up to the full context of 4 memory
     + 4 window + 1 block frames, so 1 to 9 (T = 64) or 2 to 14 (T = 96) key tiles: no
     pipelined pass, one or two passes of four and every remainder after them; every fifth
     call two frames split into two query blocks (masked tiles).  Every row against the
     oracle, with the per-head and per-row checks."""
-    w = synth.workload("s512_bf16", heads=2, grid_h=8, grid_w=grid_w, window_frames=4, mem_slots=4,
+    w = synth.workload(name, heads=2, grid_h=8, grid_w=grid_w, window_frames=4, mem_slots=4,
                        max_block_frames=4)
+    kv = w["kv_dtype"]
     run = Runner(w)
     worst = 0.0
     for s in range(24):
@@ -526,16 +529,17 @@ def test_bf16_d128_dual_kernel_tile_counts(grid_w):
         res = run.step(2 if blocks else 1, blocks=blocks, form=0 if blocks else 1)
         err, dl = run.compare_attention(res)
         worst = max(worst, err)
-        assert err <= ATTN_TOL[BF16] and dl <= LSE_TOL[BF16], (s, err, dl)
+        assert err <= ATTN_TOL[kv], (s, err, dl)
+        assert_lse(run, res, kv)
         assert_state_matches(run)
     assert_memory_bitexact(run)
-    say(f"dual kernel tile counts, T = {8 * grid_w}: worst rel L2 {worst:.3e}")
+    say(f"{name} dual kernel tile counts, T = {8 * grid_w}: worst rel L2 {worst:.3e}")
 
 
 @pytest.mark.parametrize("name", ["s512_bf16", "fp8_kv"])
 def test_attention_repeats_bit_identical_and_unflagged(name):
-    """The 512x512 step's attention (bf16 cache: the dual-block kernel; FP8: the lockstep
-    one) called three times on one staged block, memory full: outputs and LSE bit-identical
+    """The 512x512 step's attention (bf16 cache: k_attn_bf16_d128_dual; FP8:
+    k_attn_f8v_d128_dual) called three times on one staged block, memory full: outputs and LSE bit-identical
     (the kernels have fixed reduction orders, so a difference would mean a race in the LDS
     ring or a result used before its MFMA wrote it), and no query tile handed to the exact
     pass on these inputs."""
@@ -639,13 +643,20 @@ def test_bf16_d128_max_key_frames():
     assert_ref_bitexact(run)
 
 
-def test_bf16_d128_late_preferred_key_goes_to_exact_pass():
-    """A late key that every query prefers by ~60 nats (finite probabilities near 2^85 under
-    the first tile's reference): the bf16-V fast pass sees its tile sums pass 2^64, flags
-    the query tiles instead of rescaling O in place, and the exact pass's result matches
-    the oracle."""
-    w = synth.workload("s512_bf16", heads=2, grid_h=8, grid_w=8, window_frames=4,
+@pytest.mark.parametrize("name, key, flagged", [("s512_bf16", 7.0, False), ("fp8_kv", 7.0, False),
+                                                 ("fp8_kv", 2000.0, True)],
+                         ids=["bf16-60nats", "fp8-60nats", "fp8-overflow"])
+def test_d128_late_preferred_key(name, key, flagged):
+    """A late key that every query prefers (its channels set to `key`, the queries' to
+    their magnitudes), by ~60 nats: probabilities near 2^35 under the reference, which
+    lies 56 log2 units above the first tile's row maximum, so the fast kernels keep every
+    tile (FP8: the per-row tile scales reach E ~ 30); or (key 2000) by far more than the
+    f32 range: the FP8 fast kernel flags its query tiles and the exact pass redoes them
+    (the bf16 case is test_bf16_d128_overflow_falls_back_to_exact_pass).  The result
+    matches the oracle either way."""
+    w = synth.workload(name, heads=2, grid_h=8, grid_w=8, window_frames=4,
                        mem_slots=4, max_block_frames=4)
+    kv = w["kv_dtype"]
     run = Runner(w)
     for _ in range(6):
         run.step(2, attend=False)
@@ -653,7 +664,7 @@ def test_bf16_d128_late_preferred_key_goes_to_exact_pass():
     T = w["tokens"]
     last = 4 * T - 1
     qh[:, :, :] = np.abs(qh)
-    kh[last, :, :] = 7.0
+    kh[last, :, :] = key
     q = torch.from_numpy(qh).to(torch.bfloat16).cuda()
     k = torch.from_numpy(kh).to(torch.bfloat16).cuda()
     qh, kh = q.float().cpu().numpy(), k.float().cpu().numpy()
@@ -663,11 +674,12 @@ def test_bf16_d128_late_preferred_key_goes_to_exact_pass():
     flags = run.cache.buf[run.cache.layout.attn_flags:].view(torch.int32)[: w["heads"]].cpu().numpy()
     ref = run.oc.attention(qh, kh, vh)
     err, dl = run.compare_attention(dict(out=out, lse=lse, ref=ref))
-    say(f"late preferred key: flags {flags.tolist()}, rel L2 {err:.3e}, max dLSE {dl:.2e}")
-    assert flags.min() == 1, "the fast pass should have handed these tiles to the exact pass"
     O_ref, LSE_ref, heads, rows = ref
-    assert err <= ATTN_TOL[BF16]
-    assert float(np.abs(lse.cpu().numpy()[heads, rows] - LSE_ref).max() / np.abs(LSE_ref).max()) <= 2e-3
+    rel_lse = float(np.abs(lse.cpu().numpy()[heads, rows] - LSE_ref).max() / np.abs(LSE_ref).max())
+    say(f"late preferred key {key} ({name}): flags {flags.tolist()}, rel L2 {err:.3e}, "
+        f"max dLSE {dl:.2e}, rel dLSE {rel_lse:.2e}")
+    assert flags.tolist() == [1 if flagged else 0] * w["heads"]
+    assert err <= ATTN_TOL[kv] and rel_lse <= 2e-3
 
 
 def test_bf16_d128_overflow_falls_back_to_exact_pass():
