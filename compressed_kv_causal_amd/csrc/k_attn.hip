@@ -9,8 +9,8 @@
 // Kernels:
 //   k_attn_bf16_d128_dual  the D = 128 production kernel for a bf16 V (described at its
 //                     definition).
-//   k_attn_bf16_d128<true>  the D = 128 production kernel for an FP8 cache's e4m3 V; its
-//                     tile ring, copies and fragment layouts are shared with the above.
+//   k_attn_f8v_d128_dual  the D = 128 production kernel for an FP8 cache's e4m3 V (fp8
+//                     MFMAs for PV); the key-tile ring of both is described above them.
 //   k_attn_bf16<D, F8V>  exact online-softmax flash attention on v_mfma_f32_32x32x16_bf16,
 //                     4 waves x 32 query rows, 64-key tiles staged in LDS (K row-major, V
 //                     transposed by the staging threads, an FP8 cache's V codes widened to
@@ -240,21 +240,20 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// k_attn_bf16_d128<F8>: the D = 128 kernel in the lockstep layout (T >= 64), launched for
-// an FP8 cache's V (F8 = true).  Its bf16-V form (F8 = false) is not launched:
-// k_attn_bf16_d128_dual below replaces it for a bf16 V.
-//
-//   * 256 query rows per workgroup, 8 waves x 32 rows: two waves per SIMD, so one wave's
-//     softmax (VALU) and barrier waits overlap the other's MFMAs.
+// The D = 128 key-tile ring of the two production kernels below (T >= 64):
 //   * Key tiles of BN = 64 rows are copied global -> LDS with global_load_lds (16 B per
-//     lane, no registers) into a ring of NS = 4 stages: tile j + 3 is in flight while tile
-//     j is computed.  Rows are stored with an XOR swizzle of their 16-byte chunks:
+//     lane, no registers) into a ring of NS = 4 stages: the copies of tile j + 3 are in
+//     flight while tile j is computed; a constant "s_waitcnt vmcnt + barrier" per tile
+//     orders them with the fragment reads (tiles past the end are copied too, clamped, so
+//     the count never changes).  bf16 rows (K, and a bf16 cache's V) are stored with an XOR
+//     swizzle of their 16-byte chunks:
 //         chunk c of key row r sits at position c ^ swz(r), swz(r) = ((r & 3) << 2) | ((r >> 2) & 3)
 //     swz is a bijection over 16 consecutive rows (K fragment reads, ds_read_b128 of 16 rows
 //     x one chunk, hit 16 distinct 16-byte slots) and puts the low row bits above the chunk
 //     bits (a V^T fragment read, ds_read_b64_tr_b16 of 4 rows x 4 chunks per 32 lanes, hits
-//     16 distinct slots), so neither read has bank conflicts.
-//   * V^T fragments come from the transposing LDS read: within each 16-lane group, lanes
+//     16 distinct slots), so neither read has bank conflicts.  An FP8 cache's e4m3 V rows
+//     (128 B) use chunk c ^ (r mod 8) and the 8-bit transposing read (k_attn_f8v_d128_dual).
+//   * V^T fragments come from the transposing LDS reads: within each 16-lane group, lanes
 //     4t..4t+3 address key row t (16 consecutive channels) and lane i receives channel i
 //     of rows 0..3 -- the consecutive keys of one channel the MFMA A operand needs.
 //   * Addressing costs almost no VALU work per tile.  Copies: the tile's first key frame
@@ -263,41 +262,11 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const AttnArgs a) {
 //     the two (a 64-key tile spans at most two frames since T >= 64).  Fragment reads: the
 //     per-lane LDS offsets of all K and V^T fragments are loop invariants; the ring slot
 //     and the fragment's key block or chunk are the instruction's immediate offset, with
-//     the unmasked tile loop unrolled by NS so the slot is a compile-time constant.
-//   * Softmax with a lazily raised reference: m = the row's max over the first key tile.
-//     The staged queries carry log2(e)/sqrt(D), and every QK^T MFMA chain starts from the
-//     broadcast -m instead of 0, so the chain's output q.k - m is already the base-2
-//     exponent of the probability: the softmax spends one v_exp per score and nothing
-//     else.  There is no running max and no per-tile rescale of O; since m never exceeds
-//     the true row max, terms are
-//     only ever too large, never lost.  Only when a lane's tile sum reaches 2^64 (scores
-//     far above m, e.g. from outlier channels) does the wave raise m by a power of two and
-//     scale O and l exactly (see tile()).  If l or O still ends up not finite, the
-//     workgroup marks itself in `flags` and the exact online-softmax kernel redoes its rows.
+//     the free-tile loop unrolled by NS so the slot is a compile-time constant.
 //   * Workgroup -> (head, query tile) mapping keeps each XCD (every 8th workgroup id) on
 //     the tiles of one head at a time, so that head's K/V stream once through one L2.
 // ---------------------------------------------------------------------------------------
 namespace d128 {
-
-constexpr int D = 128, BM = 256, BN = 64, NS = 4, WAVES = 8;
-constexpr int ROW_BYTES = D * 2;
-constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
-constexpr int V_RING = NS * TILE_BYTES;     // V slots follow the K slots in LDS
-constexpr int VMEM_PER_TILE = 4;            // copy instructions per wave per tile:
-                                            // K 2, V 2 (bf16) or K 2, V 1, V scales 1 (FP8)
-// FP8 cache: V tiles of e4m3 rows (128 B), then per tile the keys' 1/s_v and log2(s_v)
-// pairs, in groups of 8 keys: [8 x 1/s_v | 8 x (hi, lo)] = 64 B per group
-constexpr int V8_ROW = D;
-constexpr int V8_TILE = BN * V8_ROW;        // 8 KiB
-constexpr int S_RING = V_RING + NS * V8_TILE;
-constexpr int S_TILE = BN * 8;
-constexpr int LDS_BF16 = 2 * NS * TILE_BYTES;
-constexpr int LDS_F8 = S_RING + NS * S_TILE;
-// FP8 probabilities: P~ = 2^(s + log2 s_v - m_ref) = P' s_v, P' = 2^(s - m_ref) the
-// probability, with m_ref = (the first tile's largest s + log2 s_v) - KSHIFT, so that
-// P~ <= 2^KSHIFT there; later tiles keep P~ < 448 through the raise (a lane's sum of P'
-// below 448 * 2^-E_h, 2^E_h the power of two above the head's largest s_v)
-constexpr int KSHIFT = 3;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -350,34 +319,6 @@ __device__ __forceinline__ const char* frame_base(const Geo& g, int f) {
   return f < g.ref_len ? fb : (f < g.mem_end ? mb : (f < g.nh ? rb : cb));
 }
 
-struct Ctx {
-  Geo g;
-  const char* kbase;  // this head's rotated keys [Lk][128]
-  char* lds;
-  unsigned lds_u32;   // LDS address of the ring (for M0)
-  int h, wave, lane, hi, lr, kvis;
-  int64_t hrow;       // bytes between consecutive tokens of one V frame (H * V row bytes)
-  // copies: the two 4-row groups of a tile this lane copies
-  int crow[2];        // row inside the tile
-  int koff[2];        // crow * 256 + chunk * 16 (bytes from the tile's first K row)
-  int voff[2];        // (crow * H + h) * 256 + chunk * 16 (bytes from the V row of token 0)
-  // fragment reads: LDS byte offsets from the ring base (slot 0)
-  int kread[8];       // K fragment kk of key block 0 (+ 8 KiB for block 1)
-  int vread[4][2];    // the two transposed reads of V^T fragment db, chunk 0 (+ 4 KiB per chunk)
-  // FP8 V: the one 8-row group of a tile this lane copies, its V^T fragment reads and the
-  // V scale terms of its keys
-  int vrow8;          // row inside the tile
-  int voff8;          // (vrow8 * H + h) * 128 + chunk * 16
-  int vread8[4];      // first of the four 8-key transposed reads of V^T fragment db
-  int sread;          // 1/s_v of the lane's probabilities' keys (S_RING + hi * 64)
-  int lread[2];       // log2(s_v) pair of the A-operand key row of key block kb
-  const char* vsbase; // the copy source of this lane: 1/s_v (lanes 0-7) or log2 pairs
-                      // (lanes 8-15) of this head, attention order, at key lane & 7
-  float thr;          // raise threshold 448 * 2^-E_h on a lane's 32-key sum of P'
-  int thr_exp;        // frexp exponent of thr
-  bf16x8_t augb;      // B operand of the log2(s_v) step
-};
-
 // Scalar stream state of the copies: frame and token of the first key of the next tile,
 // and the V bases of that frame and the next (recomputed when a tile crosses a frame).
 struct Stream {
@@ -386,501 +327,13 @@ struct Stream {
   const char* baseB;
 };
 
-// Copy tile t's 64 key rows of K and V (and, FP8, their V scales) into ring slot t % NS,
-// then advance the stream.
-template <bool F8>
-__device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
-  const Geo& a = c.g;
-  const unsigned slot = (unsigned)(t % NS);
-  const unsigned kdst = c.lds_u32 + slot * TILE_BYTES + (unsigned)c.wave * 8 * ROW_BYTES;
-  const unsigned vdst = F8 ? c.lds_u32 + V_RING + slot * V8_TILE + (unsigned)c.wave * 8 * V8_ROW
-                           : kdst + V_RING;
-  if ((t + 1) * BN <= a.Lk) {
-    const char* ktile = c.kbase + (int64_t)t * TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) copy_to_lds(ktile + c.koff[i], kdst + i * 4 * ROW_BYTES);
-  } else {  // rows past the last key repeat it
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int key = t * BN + c.crow[i];
-      key = key < a.Lk ? key : a.Lk - 1;
-      copy_to_lds(c.kbase + (int64_t)key * ROW_BYTES + (c.koff[i] & (ROW_BYTES - 1)), kdst + i * 4 * ROW_BYTES);
-    }
-  }
-  const char* vA = st.baseA + st.u0 * c.hrow;
-  if (F8) {
-    if (st.u0 + BN <= a.T) {
-      copy_to_lds(vA + c.voff8, vdst);
-    } else {
-      const char* vB = st.baseB + (st.u0 - a.T) * c.hrow;
-      copy_to_lds((st.u0 + c.vrow8 >= a.T ? vB : vA) + c.voff8, vdst);
-    }
-    // scale terms of keys 8 wave .. 8 wave + 7 of the tile: lanes 0-7 1/s_v, lanes 8-15
-    // the log2 pairs.  The planes are zero-padded to a multiple of 64 keys, so a tile's
-    // groups never need a bound check; tiles copied past the end re-read the last group.
-    if (c.lane < 16) {
-      const int key0 = min(t * BN + c.wave * 8, a.s_last);  // wave-uniform; vsbase has lane & 7
-      copy_dword_to_lds(c.vsbase + (int64_t)key0 * 4, c.lds_u32 + S_RING + slot * S_TILE + (unsigned)c.wave * 64);
-    }
-  } else if (st.u0 + BN <= a.T) {  // the whole tile lies in frame f0
-#pragma unroll
-    for (int i = 0; i < 2; ++i) copy_to_lds(vA + c.voff[i], vdst + i * 4 * ROW_BYTES);
-  } else {
-    const char* vB = st.baseB + (st.u0 - a.T) * c.hrow;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      copy_to_lds((st.u0 + c.crow[i] >= a.T ? vB : vA) + c.voff[i], vdst + i * 4 * ROW_BYTES);
-  }
-  st.u0 += BN;  // T >= BN: at most one frame boundary per tile
-  if (st.u0 >= a.T) {
-    st.u0 -= a.T;
-    st.f0 += 1;
-    st.baseA = st.baseB;
-    st.baseB = frame_base(c.g, st.f0 + 1);
-  }
-}
-
-// LDS address helpers: SLOT >= 0 is a compile-time ring slot, SLOT < 0 takes tile j's.
-template <int SLOT>
-__device__ __forceinline__ int slot_of(int j) { return SLOT >= 0 ? SLOT : j % NS; }
-
-template <bool MASK>
-__device__ __forceinline__ void mask_block(f32x16_t& s, int key0, int hi, int kvis) {
-  if (MASK) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + perm32(((r >> 2) << 3) + (hi << 2) + (r & 3));
-      if (key >= kvis) s[r] = -INFINITY;
-    }
-  }
-}
-
 // Scheduling fence between pipeline steps (no instruction crosses it): without it the
 // compiler moves each MFMA up next to its fragment read and reuses one fragment register,
 // exposing the full LDS latency on every MFMA.
 __device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// S^T of one 64-key tile (two 32-key blocks) from the K rows in LDS, masked, on top of
-// `init` (the broadcast -m_ref of the lane's row: the chains then produce the exponents
-// of the probabilities directly).  The two key blocks are independent MFMA chains,
-// interleaved; K fragments are read three steps ahead of their MFMAs.
-template <bool F8, bool MASK, int SLOT>
-__device__ __forceinline__ void qk_tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], const f32x16_t& init,
-                                        f32x16_t (&s)[2]) {
-  const char* kb = c.lds + slot_of<SLOT>(j) * TILE_BYTES;
-  auto kfrag = [&](int kk, int kb2) {
-    return *reinterpret_cast<const bf16x8_t*>(kb + c.kread[kk] + kb2 * 32 * ROW_BYTES);
-  };
-  constexpr int AHEAD = 3;  // steps of two MFMAs (64 cycles) between a read and its use
-  bf16x8_t kf[AHEAD + 1][2];
-#pragma unroll
-  for (int kk = 0; kk < AHEAD; ++kk) {
-    kf[kk][0] = kfrag(kk, 0);
-    kf[kk][1] = kfrag(kk, 1);
-  }
-  step_fence();
-  s[0] = init;
-  s[1] = init;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    if (kk + AHEAD < 8) {
-      kf[(kk + AHEAD) % (AHEAD + 1)][0] = kfrag(kk + AHEAD, 0);
-      kf[(kk + AHEAD) % (AHEAD + 1)][1] = kfrag(kk + AHEAD, 1);
-    }
-    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % (AHEAD + 1)][0], qf[kk], s[0], 0, 0, 0);
-    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % (AHEAD + 1)][1], qf[kk], s[1], 0, 0, 0);
-    step_fence();
-  }
-  if (F8) {
-    // one more 16-channel step adds log2(s_v) of each key row: A = (hi, lo, 0, ...) of the
-    // row's key, B = (1, 1, 0, ...) in the lanes of channels 0..7 and 0 in the others
-    // (the constant c.augb)
-    const char* sb = c.lds + slot_of<SLOT>(j) * S_TILE;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t pair = *reinterpret_cast<const uint32_t*>(sb + c.lread[kb]);
-      const u32x4_t w = {pair, 0u, 0u, 0u};
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), c.augb, s[kb],
-                                                      0, 0, 0);
-    }
-  }
-  mask_block<MASK>(s[0], j * BN, c.hi, c.kvis);
-  mask_block<MASK>(s[1], j * BN + 32, c.hi, c.kvis);
-}
-
-// V^T fragment (16 keys of chunk ch, channels 32 db .. 32 db + 31).
-__device__ __forceinline__ bf16x8_t vfrag(const char* vb, const Ctx& c, int ch, int db) {
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + c.vread[db][0] + ch * 16 * ROW_BYTES));
-  const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + c.vread[db][1] + ch * 16 * ROW_BYTES));
-  bf16x8_t vf;
-  __builtin_memcpy(&vf, &lo, 8);
-  __builtin_memcpy(reinterpret_cast<char*>(&vf) + 8, &up, 8);
-  return vf;
-}
-
-// FP8: P~ = exp2(s - sub) in place; returns this lane's sum of P' = P~ / s_v over its 32
-// keys (the probabilities themselves, for l), in four partial sums.
-template <bool SUB>
-__device__ __forceinline__ float exp_tile_f8(f32x16_t (&s)[2], float sub, const char* sb, const Ctx& c) {
-  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int ch = 0; ch < 4; ++ch) {
-    const float4 i0 = *reinterpret_cast<const float4*>(sb + c.sread + ch * 128);
-    const float4 i1 = *reinterpret_cast<const float4*>(sb + c.sread + ch * 128 + 16);
-    const float inv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-    const int kb = ch >> 1, b0 = 8 * (ch & 1);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float e = __builtin_amdgcn_exp2f(SUB ? s[kb][b0 + t] - sub : s[kb][b0 + t]);
-      s[kb][b0 + t] = e;
-      part[t & 3] = __builtin_fmaf(e, inv[t], part[t & 3]);
-    }
-  }
-  return (part[0] + part[1]) + (part[2] + part[3]);
-}
-
-// V^T fragment of FP8 V (channels 32 db .. 32 db + 31, the 32 keys of this lane's half):
-// four transposing 8-bit reads of 8 keys each.  Within each 16-lane group, lanes 2r and
-// 2r + 1 address the two 8-byte halves of key row r's 16-channel chunk, and lane i
-// receives channel i of the 8 rows, i.e. 8 consecutive keys of its channel.  Byte b of
-// the fragment is key 16 (b / 8) + 8 half + (b mod 8) -- the key order of the lane's
-// probabilities, so A and B pair up in the fp8 MFMA.
-__device__ __forceinline__ v8i32 vfrag8(const char* vb, const Ctx& c, int db) {
-  v8i32 f;
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    const v2i32 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(vb + c.vread8[db] + cc * 16 * V8_ROW));
-    f[2 * cc] = x[0];
-    f[2 * cc + 1] = x[1];
-  }
-  return f;
-}
-
-// p = exp2(s - sub) in place (sub = 0 when s already holds the exponents); returns this
-// lane's sum of the 32 probabilities.
-template <bool SUB>
-__device__ __forceinline__ float exp_tile(f32x16_t (&s)[2], float sub) {
-  float sum = 0.0f;
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(SUB ? s[kb2][r] - sub : s[kb2][r]);
-      s[kb2][r] = e;
-      sum += e;
-    }
-  return sum;
-}
-
-// Tile j: issue the copy of tile j + NS - 1 into the slot tile j - 1 used (every wave was
-// done with it before the last barrier), compute tile j, then wait until tile j + 1 has
-// landed (the copies of tiles j + 2 .. j + NS - 1 stay in flight) and sync.  Tiles past
-// the end are copied too (clamped rows, harmless), so the wait count is a constant.
-//
-// O^T += V^T P^T on bf16 V: 16 MFMAs (chunk ch, channel block db) in 4 independent chains,
-// V^T fragments read four MFMAs (128 cycles) ahead
-__device__ __forceinline__ void pv_tile_bf16(const Ctx& c, const char* vb, const f32x16_t (&s)[2],
-                                             f32x16_t (&o)[4]) {
-  bf16x8_t p[4];
-#pragma unroll
-  for (int ch = 0; ch < 4; ++ch)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) p[ch][t] = (__bf16)s[ch >> 1][8 * (ch & 1) + t];
-  constexpr int VAHEAD = 4;
-  bf16x8_t vf[VAHEAD + 1];
-#pragma unroll
-  for (int i = 0; i < VAHEAD; ++i) vf[i] = vfrag(vb, c, i >> 2, i & 3);
-  step_fence();
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i + VAHEAD < 16) vf[(i + VAHEAD) % (VAHEAD + 1)] = vfrag(vb, c, (i + VAHEAD) >> 2, (i + VAHEAD) & 3);
-    o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (VAHEAD + 1)], p[i >> 2], o[i & 3], 0, 0, 0);
-    step_fence();
-  }
-}
-
-// O^T += V^T P~^T on FP8 V: P~ = P' * s_v (P' the probability, s_v the key's V row scale)
-// rounded to e4m3 (the raise keeps it <= 448), against the stored e4m3 codes: 4 MFMAs of
-// 32 channels x 64 keys on v_mfma_f32_32x32x64_f8f6f4 (unit block scales).  The lane's 32
-// values are keys 16 ch + 8 hi + t (ch < 4, t < 8), the B operand's byte 8 ch + t.
-// pt: the previous tile's P~ registers, whose old contents the conversions merge into
-// (both halves of every word are written, so nothing has to be cleared first).
-__device__ __forceinline__ void pv_tile_f8(const Ctx& c, const char* vb, const f32x16_t (&s)[2],
-                                           f32x16_t (&o)[4], v8i32& pt) {
-  v8i32 vf[2];
-  vf[0] = vfrag8(vb, c, 0);
-  vf[1] = vfrag8(vb, c, 1);
-#pragma unroll
-  for (int ch = 0; ch < 4; ++ch) {
-    const f32x16_t& sk = s[ch >> 1];
-    const int b0 = 8 * (ch & 1);
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 0], sk[b0 + 1], pt[2 * ch], false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 2], sk[b0 + 3], w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 4], sk[b0 + 5], pt[2 * ch + 1], false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sk[b0 + 6], sk[b0 + 7], w1, true);
-    pt[2 * ch] = w0;
-    pt[2 * ch + 1] = w1;
-  }
-  step_fence();
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    if (db + 2 < 4) {
-      const v8i32 nx = vfrag8(vb, c, db + 2);
-      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db & 1], pt, o[db], 0, 0, 0, 0, 0, 0);
-      vf[db & 1] = nx;
-    } else {
-      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db & 1], pt, o[db], 0, 0, 0, 0, 0, 0);
-    }
-    step_fence();
-  }
-}
-
-// Reference raise: a lane sum of 2^64 (bf16 V) or of 448 * 2^-E_h (FP8 V, where P' * s_v
-// must stay a finite e4m3 value) or more means a row met scores far above its reference.
-// The wave then finds for each such row a power of two 2^e -- bf16: the tile's largest
-// probability is 2^e * [1, 2); FP8: the one that brings the row's larger 32-key sum back
-// under the threshold -- and divides that row's probabilities, O and l by 2^e (exact
-// power-of-two scaling) while m_ref moves up by e.  Ordinary data never takes this branch
-// on bf16 and rarely on FP8; scores with large outliers take it a few times per row at
-// most.  A probability that is already infinite (a score >= 128 above the reference)
-// cannot be rescaled: l and O become infinite and the workgroup hands its rows to the
-// exact pass.
-template <bool F8, bool MASK, bool FIRST, int SLOT>
-__device__ __forceinline__ void tile(const Ctx& c, int j, const bf16x8_t (&qf)[8], f32x16_t (&o)[4],
-                                     float& m_ref, f32x16_t& negm, float& l_part, Stream& st,
-                                     v8i32& pt) {
-  // K slot base; V^T reads add vread / vread8 (which hold V_RING) to their slot's base
-  const char* vb = c.lds + slot_of<SLOT>(j) * (F8 ? V8_TILE : TILE_BYTES);
-  issue<F8>(c, j + NS - 1, st);
-  f32x16_t s[2];
-  qk_tile<F8, MASK, SLOT>(c, j, qf, negm, s);  // tile 0: negm = 0
-  const char* sb = c.lds + slot_of<SLOT>(j) * S_TILE;  // FP8 scale terms (+ sread)
-  float sum;
-  if (FIRST) {
-    float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    m_ref = fmaxf(mx, __shfl_xor(mx, 32));
-    if (F8) m_ref -= (float)KSHIFT;  // P~ <= 2^KSHIFT on this tile
-#pragma unroll
-    for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
-    sum = F8 ? exp_tile_f8<true>(s, m_ref, sb, c) : exp_tile<true>(s, m_ref);
-  } else {
-    sum = F8 ? exp_tile_f8<false>(s, 0.0f, sb, c) : exp_tile<false>(s, 0.0f);
-  }
-  if (!FIRST && __builtin_expect(__any(!(sum < (F8 ? c.thr : 0x1p64f))), 0)) {
-    int e;
-    if (F8) {
-      const float smax = fmaxf(sum, __shfl_xor(sum, 32));
-      e = (smax >= c.thr && smax < INFINITY) ? __builtin_amdgcn_frexp_expf(smax) - c.thr_exp + 1 : 0;
-    } else {
-      float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // e = floor(log2(mx)) for a finite mx >= 2, else 0
-      e = (mx >= 2.0f && mx < INFINITY) ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;
-    }
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb2][r] = __builtin_ldexpf(s[kb2][r], -e);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = __builtin_ldexpf(o[db][r], -e);
-    l_part = __builtin_ldexpf(l_part, -e);
-    sum = __builtin_ldexpf(sum, -e);
-    m_ref += (float)e;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
-  }
-  l_part += sum;
-  if (F8) {
-    pv_tile_f8(c, vb, s, o, pt);
-  } else {
-    pv_tile_bf16(c, vb, s, o);
-  }
-  static_assert((NS - 2) * VMEM_PER_TILE == 8, "the wait count below assumes 4 stages");
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  __syncthreads();
-}
-
 }  // namespace d128
 
-template <bool F8>
-__global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
-  using namespace d128;
-  __shared__ __align__(1024) char lds[F8 ? LDS_F8 : LDS_BF16];
-  constexpr int VROW = F8 ? V8_ROW : ROW_BYTES;  // bytes of one stored V row
-
-  // XCD-aware mapping: workgroup id b runs on XCD b % 8; give each XCD a contiguous range
-  // of (head, query tile) items so one head's tiles run on one XCD together.
-  const int n_qt = (a.Lq + BM - 1) / BM;
-  const int total = n_qt * a.H;
-  const int b = blockIdx.x;
-  const int x = b & 7, jx = b >> 3;
-  const int q8 = total >> 3, r8 = total & 7;
-  const int item = x < r8 ? x * (q8 + 1) + jx : r8 * (q8 + 1) + (x - r8) * q8 + jx;
-  const int h = item / n_qt, qt = item - h * n_qt;
-
-  Ctx c;
-  c.g.v_mem = static_cast<const char*>(a.v_mem);
-  c.g.v_ring = static_cast<const char*>(a.v_ring);
-  c.g.v_cur = static_cast<const char*>(a.v_cur);
-  c.g.v_ref = static_cast<const char*>(a.v_ref);
-  c.g.frame_bytes = (int64_t)a.T * a.H * VROW;
-  c.g.T = a.T;
-  c.g.Lk = a.Lk;
-  c.g.nf = a.Lk / a.T;
-  c.g.ref_len = a.hist.ref_len;
-  c.g.mem_end = a.hist.ref_len + a.hist.mem_len;
-  c.g.nh = a.hist.ref_len + a.hist.mem_len + a.hist.win_len;
-  c.g.M = a.hist.M;
-  c.g.R = a.hist.R;
-  c.g.mem_slot0 = a.hist.mem_slot0;
-  c.g.ring_slot0 = a.hist.ring_slot0;
-  c.g.s_last = (a.Lk + BN - 1) / BN * BN - 8;
-  c.h = h;
-  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  c.lane = threadIdx.x & 63;
-  c.hi = c.lane >> 5;
-  c.lr = c.lane & 31;
-  c.lds = lds;
-  c.lds_u32 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  c.kbase = static_cast<const char*>(a.k) + (int64_t)h * a.k_head_stride * 2;
-  c.hrow = (int64_t)a.H * VROW;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = c.wave * 8 + i * 4 + (c.lane >> 4);
-    const int chunk = (c.lane & 15) ^ swz(r);
-    c.crow[i] = r;
-    c.koff[i] = r * ROW_BYTES + chunk * 16;
-    c.voff[i] = (r * a.H + h) * ROW_BYTES + chunk * 16;
-  }
-  {
-    const int m = perm32(c.lr);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) c.kread[kk] = m * ROW_BYTES + (((2 * kk + c.hi) ^ swz(m)) * 16);
-    const int g = c.lane >> 4, i = c.lane & 15;
-    const int row = c.hi * 8 + (i >> 2);
-    const int half = (i & 1) * 8;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int chunk = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
-      c.vread[db][0] = V_RING + row * ROW_BYTES + ((chunk ^ swz(row)) * 16) + half;
-      c.vread[db][1] = V_RING + (row + 4) * ROW_BYTES + ((chunk ^ swz(row + 4)) * 16) + half;
-    }
-  }
-  if (F8) {
-    // copies: lane l moves 16 B of key row 8 wave + l / 8; its LDS position l mod 8 holds
-    // the row's chunk (l mod 8) ^ (row mod 8), so the transposed reads below (8 consecutive
-    // rows, one chunk) hit 8 different 16-byte positions
-    c.vrow8 = c.wave * 8 + (c.lane >> 3);
-    const int chunk = (c.lane & 7) ^ (c.vrow8 & 7);
-    c.voff8 = (c.vrow8 * a.H + h) * V8_ROW + chunk * 16;
-    // V^T reads: 16-lane group g covers channels 16 (g mod 2) of the 32-channel block and
-    // keys 8 (g / 2) of each 16-key chunk; lane i addresses row i / 2, byte half i mod 2
-    const int g = c.lane >> 4, i = c.lane & 15;
-    const int vr = (g >> 1) * 8 + (i >> 1);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-      c.vread8[db] = V_RING + vr * V8_ROW + (((2 * db + (g & 1)) ^ (vr & 7)) * 16) + (i & 1) * 8;
-    c.sread = S_RING + c.hi * 64;
-    const int m = perm32(c.lr);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = kb * 32 + m;
-      c.lread[kb] = S_RING + (key >> 3) * 64 + 32 + (key & 7) * 4;
-    }
-    c.vsbase = reinterpret_cast<const char*>(a.vscale + (c.lane < 8 ? 1 : 2) * a.vs_plane +
-                                             (int64_t)h * a.vs_head_stride + (c.lane & 7));
-    float smax = 0.0f;
-#pragma unroll
-    for (int p = 0; p < kVmaxParts; ++p) smax = fmaxf(smax, a.vmax[h * kVmaxParts + p]);
-    const int eh = (smax > 0.0f && smax < INFINITY) ? __builtin_amdgcn_frexp_expf(smax) : 0;
-    c.thr = __builtin_ldexpf(448.0f, -eh);
-    c.thr_exp = __builtin_amdgcn_frexp_expf(c.thr);
-    const u32x4_t ones = {c.hi ? 0u : 0x3F803F80u, 0u, 0u, 0u};  // bf16 (1, 1, 0, ...)
-    c.augb = __builtin_bit_cast(bf16x8_t, ones);
-  }
-  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.q_head_stride;
-  const int q0 = qt * BM;
-
-  const int row = q0 + c.wave * 32 + c.lr;
-  const int rr = row < a.Lq ? row : a.Lq - 1;
-  c.kvis = a.Lhist + a.block_end[block_of_row(a, rr)];
-  bf16x8_t qf[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    qf[kk] = row < a.Lq ? *reinterpret_cast<const bf16x8_t*>(qb + (int64_t)row * D + kk * 16 + c.hi * 8)
-                        : bf16x8_t{};
-  const int last = (q0 + BM < a.Lq ? q0 + BM : a.Lq) - 1;
-  const int kend = a.Lhist + a.block_end[block_of_row(a, last)];
-  const int kfree = a.Lhist + a.block_end[block_of_row(a, q0)];
-  const int nt = (kend + BN - 1) / BN;
-  const int n_free = kfree / BN;  // tiles every row of the workgroup sees completely
-
-  f32x16_t o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
-  float m_ref = 0.0f, l_part = 0.0f;
-  f32x16_t negm = f32x16_t{};  // -m_ref in every element (the QK^T chains' starting value)
-  v8i32 pt = v8i32{};          // FP8: the last tile's e4m3 P~
-  Stream st{0, 0, frame_base(c.g, 0), frame_base(c.g, 1)};
-  for (int t = 0; t < NS - 1; ++t) issue<F8>(c, t, st);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile 0 landed
-  __syncthreads();
-
-  if (n_free > 0)
-    tile<F8, false, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st, pt);
-  else
-    tile<F8, true, true, 0>(c, 0, qf, o, m_ref, negm, l_part, st, pt);
-  int j = 1;
-  const int free_end = n_free < nt ? n_free : nt;
-  static_assert(NS == 4, "the unrolled loop below walks the slots 1, 2, 3, 0");
-  for (; j + 4 <= free_end; j += 4) {
-    tile<F8, false, false, 1>(c, j, qf, o, m_ref, negm, l_part, st, pt);
-    tile<F8, false, false, 2>(c, j + 1, qf, o, m_ref, negm, l_part, st, pt);
-    tile<F8, false, false, 3>(c, j + 2, qf, o, m_ref, negm, l_part, st, pt);
-    tile<F8, false, false, 0>(c, j + 3, qf, o, m_ref, negm, l_part, st, pt);
-  }
-  for (; j < free_end; ++j) tile<F8, false, false, -1>(c, j, qf, o, m_ref, negm, l_part, st, pt);
-  for (; j < nt; ++j) tile<F8, true, false, -1>(c, j, qf, o, m_ref, negm, l_part, st, pt);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
-
-  const float l = l_part + __shfl_xor(l_part, 32);
-  const float inv = 1.0f / l;
-  bool ok = l > 0.0f && l < 3.0e38f;
-  float outv[4][16];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      outv[db][r] = o[db][r] * inv;
-      ok = ok && (fabsf(outv[db][r]) < 3.0e38f);
-    }
-  int bad = 0;
-  if (row < a.Lq) {
-    bad = ok ? 0 : 1;
-    uint16_t* ob = static_cast<uint16_t*>(a.out) + ((int64_t)row * a.H + h) * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d0 = db * 32 + jg * 8 + c.hi * 4;
-        uint2 w2;
-        w2.x = (uint32_t)f32_to_bf16(outv[db][jg * 4 + 0]) | ((uint32_t)f32_to_bf16(outv[db][jg * 4 + 1]) << 16);
-        w2.y = (uint32_t)f32_to_bf16(outv[db][jg * 4 + 2]) | ((uint32_t)f32_to_bf16(outv[db][jg * 4 + 3]) << 16);
-        *reinterpret_cast<uint2*>(ob + d0) = w2;
-      }
-    if (c.hi == 0 && a.lse) a.lse[(int64_t)h * a.Lq + row] = (m_ref + log2f(l)) * 0.6931471805599453f;
-  }
-  bad = __syncthreads_or(bad);
-  if (threadIdx.x == 0 && a.flags) a.flags[item] = bad;
-}
-
-// Plain f32 kernel: one lane per query row, 32-key tiles of K and V in LDS.
 // ---------------------------------------------------------------------------------------
 // k_attn_bf16_d128_dual: the D = 128 kernel for a bf16 V (T >= 64).  One wave per SIMD
 // (4 waves, 256 query rows per workgroup) and two 32-row query blocks per wave, A and B,
@@ -892,15 +345,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16_d128(const AttnArgs a) {
 //           beside A's exponentials, row sum and bf16 packing of tile i + 1
 //
 // Per MFMA step the wave issues one exponential, one add and every other step one packing;
-// the fragment reads are half those of the two-waves-per-SIMD layout of k_attn_bf16_d128.
-// Key tile ring, copies, swizzles, fragment layouts, the lazy reference (the first tile's
-// row maximum, folded into the start of every QK^T chain) and the flags are those of
-// k_attn_bf16_d128.  Differences:
-//   * the reference lies a fixed margin above the first tile's row maximum, and a tile
-//     sum that still threatens the f32 range (scores far above the reference) is not
-//     rescaled in place: the wave records it, finishes, and the workgroup flags its rows
-//     for the exact pass (the margin and threshold at MDELTA, OVF);
-//   * the free tiles run in pipelined passes of four (ring slots as compile-time
+// each K and V^T fragment read from LDS feeds two MFMAs (one per block), half the reads
+// of a layout with two 32-row waves per SIMD.  The key tiles come through the ring above.
+//   * Softmax against a fixed reference instead of a running maximum: m = the row's
+//     largest score over the first key tile plus a margin.  The staged queries carry
+//     log2(e)/sqrt(D), and every QK^T chain starts from the broadcast -m instead of 0, so
+//     the chain's output is the base-2 exponent of the probability: one v_exp per score,
+//     no per-tile rescale of O.  A tile sum that still threatens the f32 range (scores
+//     far above m) is not rescaled in place: the wave records it, finishes, and the
+//     workgroup flags its rows in `flags`, and the exact online-softmax kernel redoes
+//     them, as it does rows whose l or O came out not finite (margin and threshold at
+//     MDELTA, OVF).
+//   * The free tiles run in pipelined passes of four (ring slots as compile-time
 //     constants); the pass remainder and the tiles that need a per-element mask run
 //     unpipelined after them.
 // Register use is the point of the layout: O (2 x 64) and the Q fragments (2 x 32) stay in
@@ -1442,9 +898,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16_d128_dual(const AttnArgs a
 // the P~ operand multiplies 2^E back in.  O is never rescaled: the reference m lies a
 // fixed margin above the row's largest s + log2 s_v over the first tile, and only a tile
 // sum of P' that threatens f32 range flags the rows for the exact pass (the margin and
-// the threshold at the constants MDELTA, OVF).  Copies, swizzles and fragment
-// layouts are those of k_attn_bf16_d128 (FP8 form); the pipelining, registers and
-// inline-asm MFMAs those of k_attn_bf16_d128_dual.
+// the threshold at the constants MDELTA, OVF).  Key tiles come through the ring above;
+// the pipelining, registers and inline-asm MFMAs are those of k_attn_bf16_d128_dual.
+// Per ring slot the LDS holds K (16 KiB), the V codes (8 KiB) and the keys' 1/s_v and
+// log2 s_v pairs in groups of 8 keys: [8 x 1/s_v | 8 x (hi, lo) bf16] = 64 B per group.
 // ---------------------------------------------------------------------------------------
 namespace d128dual8 {
 
@@ -2059,6 +1516,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_f8v_d128_dual(const AttnArgs a)
   if (threadIdx.x == 0 && a.flags) a.flags[item] = bad;
 }
 
+// Plain f32 kernel: one lane per query row, 32-key tiles of K and V in LDS.
 template <int D>
 __global__ __launch_bounds__(64) void k_attn_f32(const AttnArgs a) {
   constexpr int BN = 32;
@@ -2135,8 +1593,9 @@ hipError_t launch_attention(const AttnArgs& a, int32_t op_dtype, hipStream_t s) 
   if (a.Lq <= 0) return hipSuccess;
   if (op_dtype == DT_BF16) {
     dim3 grid((a.Lq + 127) / 128, a.H);
-    if (a.D == 128 && a.T >= d128::BN && a.flags) {
-      const int items = ((a.Lq + d128::BM - 1) / d128::BM) * a.H;
+    if (a.D == 128 && a.T >= d128dual::BN && a.flags) {
+      static_assert(d128dual::BM == d128dual8::BM && d128dual::BN == d128dual8::BN, "one item layout");
+      const int items = ((a.Lq + d128dual::BM - 1) / d128dual::BM) * a.H;
       if (a.v_fp8) {
         hipLaunchKernelGGL(k_attn_f8v_d128_dual, dim3(items), dim3(64 * d128dual8::WAVES), 0, s, a);
       } else {
