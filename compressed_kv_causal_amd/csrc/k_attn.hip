@@ -1042,10 +1042,12 @@ __device__ __forceinline__ void conv_word(const f32x16_t (&s)[2], v8i32& p, int 
   const float scale = __builtin_bit_cast(float, eb << 23);
   const f32x16_t& v = s[w >> 2];
   const int b0 = 4 * (w & 3);
-  v2i16 x = __builtin_bit_cast(v2i16, p[w]);
-  x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, v[b0], v[b0 + 1], scale, false);
-  x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, v[b0 + 2], v[b0 + 3], scale, true);
-  p[w] = __builtin_bit_cast(int, x);
+  int x;
+  asm volatile("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %5\n\t"
+               "v_cvt_scalef32_pk_fp8_f32 %0, %3, %4, %5 op_sel:[0,0,0,1]"
+               : "=&v"(x)
+               : "v"(v[b0]), "v"(v[b0 + 1]), "v"(v[b0 + 2]), "v"(v[b0 + 3]), "v"(scale));
+  p[w] = x;
 }
 
 __device__ __forceinline__ bf16x8_t kfrag(const char* kb, const Ctx& c, int kk, int kb2) {

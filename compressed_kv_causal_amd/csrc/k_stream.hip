@@ -88,15 +88,18 @@ __device__ __forceinline__ CompressPtrs compress_ptrs(const CompressArgs& a) {
 // biases in registers and issues every load of its TOK tokens x R frames before the first
 // use, so a wave has TOK * R * 1 KiB in flight (a store to the memory slot cannot alias
 // the ring in this kernel, but the compiler cannot know that and would otherwise wait for
-// each token's loads in turn).
-template <int LPR, int R, int TOK, int KV>
-__global__ __launch_bounds__(64) void k_compress_r(const CompressArgs a) {
+// each token's loads in turn).  A workgroup is WY waves on consecutive token runs of one
+// channel block: (TOK, WY) = (2, 4) keeps 115 VGPRs (four waves per SIMD) and moved a
+// 512x512 group 2 % (bf16) and 6 % (FP8) faster than (4, 1), while (8, 1), (2, 1) and
+// (4, 4) were slower or the same.
+template <int LPR, int R, int TOK, int WY, int KV>
+__global__ __launch_bounds__(64 * WY) void k_compress_r(const CompressArgs a) {
   using Raw = typename std::conditional<KV == DT_FP8, uint2, uint4>::type;  // 8 stored elements
   const int32_t C = a.H * a.D;
   // (channel block, token run) of this workgroup, the head groups of a token run on one
   // XCD (they share the FP8 row scales' cache lines)
   const int32_t item = xcd_item(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
-  const int32_t bx = item % gridDim.x, by = item / gridDim.x;
+  const int32_t bx = item % gridDim.x, by = (item / gridDim.x) * WY + threadIdx.y;
   const int32_t c0 = (bx * 64 + threadIdx.x) * 8;          // first channel of this lane
   if (c0 >= C) return;                                     // whole LPR groups leave together
   const CompressPtrs p = compress_ptrs(a);
@@ -441,21 +444,21 @@ hipError_t launch_ring_write(const RingWriteArgs& a, int64_t rows, hipStream_t s
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n_groups <= 0) return hipSuccess;
   const int32_t chunks = a.H * a.D / 8;
-  constexpr int TOK = 4;
+  constexpr int TOK = 2, WY = 4;
+  // token runs past T (the last workgroup's upper waves) load the last token and store nothing
+  const dim3 grid_r((chunks + 63) / 64, (a.T + TOK * WY - 1) / (TOK * WY), 2 * a.n_groups * a.members);
   if (a.D == 128 && a.r == 5 && a.kv_dtype != DT_F32) {
-    dim3 grid((chunks + 63) / 64, (a.T + TOK - 1) / TOK, 2 * a.n_groups * a.members);
     if (a.kv_dtype == DT_BF16)
-      hipLaunchKernelGGL((k_compress_r<16, 5, TOK, DT_BF16>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((k_compress_r<16, 5, TOK, WY, DT_BF16>), grid_r, dim3(64, WY), 0, s, a);
     else
-      hipLaunchKernelGGL((k_compress_r<16, 5, TOK, DT_FP8>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((k_compress_r<16, 5, TOK, WY, DT_FP8>), grid_r, dim3(64, WY), 0, s, a);
     return hipGetLastError();
   }
   if (a.D == 64 && a.r == 5 && a.kv_dtype != DT_F32) {
-    dim3 grid((chunks + 63) / 64, (a.T + TOK - 1) / TOK, 2 * a.n_groups * a.members);
     if (a.kv_dtype == DT_BF16)
-      hipLaunchKernelGGL((k_compress_r<8, 5, TOK, DT_BF16>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((k_compress_r<8, 5, TOK, WY, DT_BF16>), grid_r, dim3(64, WY), 0, s, a);
     else
-      hipLaunchKernelGGL((k_compress_r<8, 5, TOK, DT_FP8>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((k_compress_r<8, 5, TOK, WY, DT_FP8>), grid_r, dim3(64, WY), 0, s, a);
     return hipGetLastError();
   }
   dim3 grid((chunks + 63) / 64, (a.T + 15) / 16, 2 * a.n_groups * a.members);
