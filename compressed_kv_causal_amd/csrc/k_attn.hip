@@ -285,6 +285,11 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 __device__ __forceinline__ void copy_to_lds(const void* src, unsigned m0) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
+// The same from a wave-uniform base (an SGPR pair) plus the lane's 32-bit byte offset:
+// the address needs no 64-bit add per lane.
+__device__ __forceinline__ void copy_to_lds_s(const void* base, unsigned off, unsigned m0) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
 // The same with 4 B per lane (lane l lands at m0 + 4 l).
 __device__ __forceinline__ void copy_dword_to_lds(const void* src, unsigned m0) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
@@ -388,6 +393,7 @@ constexpr float OVF = 0x1p108f;
 using d128::Geo;
 using d128::Stream;
 using d128::copy_to_lds;
+using d128::copy_to_lds_s;
 using d128::frame_base;
 using d128::step_fence;
 using d128::swz;
@@ -421,7 +427,7 @@ __device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
   if ((t + 1) * BN <= a.Lk) {
     const char* ktile = c.kbase + (int64_t)t * TILE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) copy_to_lds(ktile + c.koff[i], kdst + i * 4 * ROW_BYTES);
+    for (int i = 0; i < 4; ++i) copy_to_lds_s(ktile, (unsigned)c.koff[i], kdst + i * 4 * ROW_BYTES);
   } else {  // rows past the last key repeat it
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -433,7 +439,7 @@ __device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
   const char* vA = st.baseA + st.u0 * c.hrow;
   if (st.u0 + BN <= a.T) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) copy_to_lds(vA + c.voff[i], vdst + i * 4 * ROW_BYTES);
+    for (int i = 0; i < 4; ++i) copy_to_lds_s(vA, (unsigned)c.voff[i], vdst + i * 4 * ROW_BYTES);
   } else {
     const char* vB = st.baseB + (st.u0 - a.T) * c.hrow;
 #pragma unroll
@@ -921,6 +927,7 @@ using d128::Geo;
 using d128::Stream;
 using d128::copy_dword_to_lds;
 using d128::copy_to_lds;
+using d128::copy_to_lds_s;
 using d128::frame_base;
 using d128::lds_v2i32;
 using d128::step_fence;
@@ -970,7 +977,7 @@ __device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
   if ((t + 1) * BN <= a.Lk) {
     const char* ktile = c.kbase + (int64_t)t * TILE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) copy_to_lds(ktile + c.koff[i], kdst + i * 4 * ROW_BYTES);
+    for (int i = 0; i < 4; ++i) copy_to_lds_s(ktile, (unsigned)c.koff[i], kdst + i * 4 * ROW_BYTES);
   } else {  // rows past the last key repeat it
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -982,7 +989,7 @@ __device__ __forceinline__ void issue(const Ctx& c, int t, Stream& st) {
   const char* vA = st.baseA + st.u0 * c.hrow;
   if (st.u0 + BN <= a.T) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) copy_to_lds(vA + c.voff[i], vdst + i * 8 * V8_ROW);
+    for (int i = 0; i < 2; ++i) copy_to_lds_s(vA, (unsigned)c.voff[i], vdst + i * 8 * V8_ROW);
   } else {
     const char* vB = st.baseB + (st.u0 - a.T) * c.hrow;
 #pragma unroll
