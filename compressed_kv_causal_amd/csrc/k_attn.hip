@@ -357,8 +357,9 @@ __device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0)
 //     log2(e)/sqrt(D), and every QK^T chain starts from the broadcast -m instead of 0, so
 //     the chain's output is the base-2 exponent of the probability: one v_exp per score,
 //     no per-tile rescale of O.  A tile sum that still threatens the f32 range (scores
-//     far above m) is not rescaled in place: the wave records it, finishes, and the
-//     workgroup flags its rows in `flags`, and the exact online-softmax kernel redoes
+//     far above m) is not rescaled in place: the wave finishes, a test of its rows'
+//     accumulated sums at the end (which any such tile sum passes on to them) makes the
+//     workgroup flag its rows in `flags`, and the exact online-softmax kernel redoes
 //     them, as it does rows whose l or O came out not finite (margin and threshold at
 //     MDELTA, OVF).
 //   * The free tiles run in pipelined passes of four (ring slots as compile-time
@@ -380,8 +381,9 @@ constexpr int LDS_BYTES = 2 * NS * TILE_BYTES;
 constexpr int VMEM_PER_TILE = 8;            // copy instructions per wave per tile: K 4, V 4
 constexpr int KAHEAD = 2;                   // K fragment pairs read ahead of their MFMAs
 constexpr int VAHEAD = 2;                   // V^T fragments read ahead (each feeds two MFMAs)
-// The reference starts MDELTA above the row's largest score of the first tile, and a tile
-// sum of probabilities of OVF = 2^108 or more flags the rows for the exact pass: scores up
+// The reference starts MDELTA above the row's largest score of the first tile, and a sum
+// of probabilities of OVF = 2^108 or more (a tile's, hence the row's) flags the rows for
+// the exact pass: scores up
 // to about 108 + MDELTA - 6 above the first tile's largest stay in the kernel (keys with
 // outlier channels reach well past 64), the first tile's largest probability is 2^-MDELTA,
 // far from f32 underflow, and l and O (at most l times the largest |V|) stay far below
@@ -535,7 +537,7 @@ __device__ __forceinline__ void exp_finish(const f32x16_t (&s)[2], u32x4_t (&p)[
 
 // X phase on K slot KS: sn[b] = Q_b K(t)^T - m_b for both blocks (from the broadcast
 // -m_ref of the rows, negm; INIT0: from 0), beside (EXPB) block B's exponentials of its
-// current tile sb, packed into pb, and their sum.  mid() runs after the second MFMA (the
+// current tile sb, packed into pb, and added to the row sum sumb.  mid() runs after the second MFMA (the
 // copies); VS >= 0: the last steps also read the first VAHEAD V^T fragments of the Y phase
 // that follows (V slot VS) into vf.  ASM: the inline-asm MFMAs of the pipelined passes;
 // otherwise builtins, whose hazards the compiler handles (prologue and tail).
@@ -551,7 +553,6 @@ __device__ __forceinline__ void phase_x(const Ctx& c, int t, const bf16x8_t (&qf
     kf[kk][0] = kfrag(kb, c, kk, 0);
     kf[kk][1] = kfrag(kb, c, kk, 1);
   }
-  if (EXPB) sumb = 0.0f;
   step_fence();
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -584,7 +585,7 @@ __device__ __forceinline__ void phase_x(const Ctx& c, int t, const bf16x8_t (&qf
 
 // Y phase on V slot VS: o[b] += V^T P_b^T for both blocks from the current tile's packed
 // probabilities pc, beside (EXPA) block A's exponentials of the next tile sa, packed into
-// pa, and their sum.  PRE: the first VAHEAD fragments are already in vf.  ASM: as for
+// pa, and added to the row sum suma.  PRE: the first VAHEAD fragments are already in vf.  ASM: as for
 // phase_x.
 template <int VS, bool EXPA, bool PRE = false, bool ASM = true>
 __device__ __forceinline__ void phase_y(const Ctx& c, int t, const u32x4_t (&pc)[2][4], f32x16_t (&o)[2][4],
@@ -595,7 +596,6 @@ __device__ __forceinline__ void phase_y(const Ctx& c, int t, const u32x4_t (&pc)
 #pragma unroll
     for (int i = 0; i < VAHEAD; ++i) vf[i] = vfrag(vb, c, i >> 2, i & 3);
   }
-  if (EXPA) suma = 0.0f;
   step_fence();
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -640,11 +640,13 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int key0, int hi, in
     }
 }
 
-// True when some lane's tile sum reached OVF (or is not finite): its row met scores far
-// above the reference.  The kernel then finishes its tiles (their results are discarded)
-// and flags its rows for the exact pass.
-__device__ __forceinline__ bool overflow(const float (&sum)[2]) {
-  return __builtin_expect(__any(!(sum[0] < OVF) || !(sum[1] < OVF)), 0);
+// True when the lane's accumulated sums reached OVF (or are not finite).  The sums are of
+// non-negative terms, so this holds whenever some tile's sum did: the lane's rows met
+// scores far above the reference, and the workgroup flags its rows for the exact pass.
+// (Tested once at the end instead of after every tile: the test took 4 VALU instructions
+// per tile.)
+__device__ __forceinline__ bool overflow(const float (&l_part)[2]) {
+  return !(l_part[0] < OVF) || !(l_part[1] < OVF);
 }
 
 // End of a tile: every copy but the last tile's (VMEM_PER_TILE per wave) has landed, and
@@ -657,32 +659,32 @@ __device__ __forceinline__ void tile_end() {
 
 // One pipelined iteration: X on tile i + 1's K (slot KS), Y on tile i's V (slot VS).
 // sc: the scores of tile i (block B's not yet exponentiated), sn: tile i + 1's; pc: tile
-// i's packed probabilities (A's on entry, B's from X), pn[0]: A's of tile i + 1.
+// i's packed probabilities (A's on entry, B's from X), pn[0]: A's of tile i + 1.  The
+// exponentials go straight into the row sums l_part (no per-tile sum is needed).
 template <int KS, int VS>
 __device__ __forceinline__ void iteration(const Ctx& c, int i, Stream& st, const bf16x8_t (&qf)[2][8],
                                           f32x16_t (&o)[2][4], f32x16_t (&sc)[2][2], f32x16_t (&sn)[2][2],
-                                          u32x4_t (&pc)[2][4], u32x4_t (&pn)[2][4], float (&sum)[2],
-                                          float (&l_part)[2], const f32x16_t (&negm)[2], bool& ovf) {
+                                          u32x4_t (&pc)[2][4], u32x4_t (&pn)[2][4], float (&l_part)[2],
+                                          const f32x16_t (&negm)[2]) {
   bf16x8_t vf[VAHEAD + 1];
-  phase_x<KS, true, VS>(c, i + 1, qf, negm, sn, sc[1], pc[1], sum[1], vf, [&]() { issue(c, i + NS - 1, st); });
-  ovf |= overflow(sum);
-  l_part[0] += sum[0];
-  l_part[1] += sum[1];
-  phase_y<VS, true, true>(c, i, pc, o, sn[0], pn[0], sum[0], vf);
+  phase_x<KS, true, VS>(c, i + 1, qf, negm, sn, sc[1], pc[1], l_part[1], vf, [&]() { issue(c, i + NS - 1, st); });
+  // Y's first exponentials read scores from X's last MFMA steps: two more wait states keep
+  // them the 24 the hazard check asks of every asm MFMA result (the MFMA needs about 11)
+  step_fence();
+  asm volatile("s_nop 1");
+  phase_y<VS, true, true>(c, i, pc, o, sn[0], pn[0], l_part[0], vf);
   tile_end();
 }
 
-// Tile i (V in slot 0) after the pipelined passes: block B's exponentials, then PV.
+// Tile i (V in slot 0) after the pipelined passes: block B's exponentials, then PV (A's
+// exponentials of tile i are already in l_part[0]).
 __device__ __forceinline__ void finish_tile(const Ctx& c, int i, Stream& st, f32x16_t (&o)[2][4],
-                                            f32x16_t (&sc)[2][2], u32x4_t (&pc)[2][4], float (&sum)[2],
-                                            float (&l_part)[2], bool& ovf) {
+                                            f32x16_t (&sc)[2][2], u32x4_t (&pc)[2][4], float (&l_part)[2]) {
   issue(c, i + NS - 1, st);
-  sum[1] = exp_all(sc[1], pc[1]);
-  ovf |= overflow(sum);
-  l_part[0] += sum[0];
-  l_part[1] += sum[1];
+  l_part[1] += exp_all(sc[1], pc[1]);
   bf16x8_t vf[VAHEAD + 1];
-  phase_y<0, false, false, false>(c, i, pc, o, sc[0], pc[0], sum[0], vf);
+  float unused_sum;
+  phase_y<0, false, false, false>(c, i, pc, o, sc[0], pc[0], unused_sum, vf);
   tile_end();
 }
 
@@ -691,8 +693,7 @@ __device__ __forceinline__ void finish_tile(const Ctx& c, int i, Stream& st, f32
 template <int SLOT>
 __device__ __forceinline__ void single_tile(const Ctx& c, int i, Stream& st, const bf16x8_t (&qf)[2][8],
                                             f32x16_t (&o)[2][4], f32x16_t (&s)[2][2], u32x4_t (&p)[2][4],
-                                            float (&sum)[2], float (&l_part)[2], const f32x16_t (&negm)[2],
-                                            bool& ovf) {
+                                            float (&sum)[2], float (&l_part)[2], const f32x16_t (&negm)[2]) {
   issue(c, i + NS - 1, st);
   f32x16_t unused_s[2];
   u32x4_t unused_p[4];
@@ -703,7 +704,6 @@ __device__ __forceinline__ void single_tile(const Ctx& c, int i, Stream& st, con
     mask_tile(s[b], i * BN, c.hi, c.kvis[b]);
     sum[b] = exp_all(s[b], p[b]);
   }
-  ovf |= overflow(sum);
   l_part[0] += sum[0];
   l_part[1] += sum[1];
   phase_y<SLOT, false, false, false>(c, i, p, o, unused_s, unused_p, sum[0], vf);
@@ -819,35 +819,35 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16_d128_dual(const AttnArgs a
       s0[b][1][r] -= m_ref[b];
     }
   }
-  sum[0] = exp_all(s0[0], p0[0]);
+  l_part[0] = exp_all(s0[0], p0[0]);
 
   // Free tiles, pipelined, in passes of four (the ring slots are compile-time constants;
   // the state alternates between (s0, p0) and (s1, p1) and is back in (s0, p0) after a
-  // pass).  An overflowing tile sum only sets `raised`.
+  // pass).  A tile sum that overflows is caught by the test of the accumulated sums at the end.
   int i = 0;
-  bool raised = false;
   static_assert(NS == 4, "the unrolled loop below walks the slots 0, 1, 2, 3");
   while (i + 4 < n_free) {
-    iteration<1, 0>(c, i, st, qf, o, s0, s1, p0, p1, sum, l_part, negm, raised);
-    iteration<2, 1>(c, i + 1, st, qf, o, s1, s0, p1, p0, sum, l_part, negm, raised);
-    iteration<3, 2>(c, i + 2, st, qf, o, s0, s1, p0, p1, sum, l_part, negm, raised);
-    iteration<0, 3>(c, i + 3, st, qf, o, s1, s0, p1, p0, sum, l_part, negm, raised);
+    iteration<1, 0>(c, i, st, qf, o, s0, s1, p0, p1, l_part, negm);
+    iteration<2, 1>(c, i + 1, st, qf, o, s1, s0, p1, p0, l_part, negm);
+    iteration<3, 2>(c, i + 2, st, qf, o, s0, s1, p0, p1, l_part, negm);
+    iteration<0, 3>(c, i + 3, st, qf, o, s1, s0, p1, p0, l_part, negm);
     i += 4;
   }
   drain_o(o);
   // tile i (slot 0); then the rest -- the last free tiles and those past n_free, which
   // need the per-element mask -- unpipelined
-  finish_tile(c, i, st, o, s0, p0, sum, l_part, raised);
+  finish_tile(c, i, st, o, s0, p0, l_part);
   for (++i; i < nt; ++i) {
     switch (i & 3) {
-      case 0: single_tile<0>(c, i, st, qf, o, s0, p0, sum, l_part, negm, raised); break;
-      case 1: single_tile<1>(c, i, st, qf, o, s0, p0, sum, l_part, negm, raised); break;
-      case 2: single_tile<2>(c, i, st, qf, o, s0, p0, sum, l_part, negm, raised); break;
-      default: single_tile<3>(c, i, st, qf, o, s0, p0, sum, l_part, negm, raised); break;
+      case 0: single_tile<0>(c, i, st, qf, o, s0, p0, sum, l_part, negm); break;
+      case 1: single_tile<1>(c, i, st, qf, o, s0, p0, sum, l_part, negm); break;
+      case 2: single_tile<2>(c, i, st, qf, o, s0, p0, sum, l_part, negm); break;
+      default: single_tile<3>(c, i, st, qf, o, s0, p0, sum, l_part, negm); break;
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
 
+  const bool raised = overflow(l_part);
   int bad = 0;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -1271,11 +1271,10 @@ template <int KS, int VS>
 __device__ __forceinline__ void iteration(const Ctx& c, int i, Stream& st, const bf16x8_t (&qf)[2][8],
                                           f32x16_t (&o)[2][4], f32x16_t (&sc)[2][2], f32x16_t (&sn)[2][2],
                                           v8i32 (&pc)[2], int (&eb)[2], float (&sum)[2], float (&l_part)[2],
-                                          const f32x16_t (&negm)[2], bool& ovf, int one) {
+                                          const f32x16_t (&negm)[2], int one) {
   static_assert(KS == (VS + 1) % NS, "X reads the slot after Y's");
   v8i32 vf[2];
   phase_x<KS, true, VS>(c, i + 1, qf, negm, sn, sc, pc, eb, sum, vf, [&]() { issue(c, i + NS - 1, st); });
-  ovf |= overflow(sum);
   l_part[0] += sum[0];
   l_part[1] += sum[1];
   phase_y<VS, true, true>(c, i, pc, eb, o, sn[0], sum[0], vf, one);
@@ -1285,7 +1284,7 @@ __device__ __forceinline__ void iteration(const Ctx& c, int i, Stream& st, const
 // Tile i (slot 0) after the pipelined passes: A's codes, B's exponentials and codes, PV.
 __device__ __forceinline__ void finish_tile(const Ctx& c, int i, Stream& st, f32x16_t (&o)[2][4],
                                             f32x16_t (&sc)[2][2], v8i32 (&pc)[2], int (&eb)[2], float (&sum)[2],
-                                            float (&l_part)[2], bool& ovf, int one) {
+                                            float (&l_part)[2], int one) {
   issue(c, i + NS - 1, st);
   const char* sb = c.lds;  // slot 0's scale terms: S_RING is in the offsets
   eb[0] = tile_scale(sum[0], c.eh8);
@@ -1293,7 +1292,6 @@ __device__ __forceinline__ void finish_tile(const Ctx& c, int i, Stream& st, f32
   sum[1] = exp_all(sb, c, sc[1]);
   eb[1] = tile_scale(sum[1], c.eh8);
   conv_all(sc[1], pc[1], eb[1]);
-  ovf |= overflow(sum);
   l_part[0] += sum[0];
   l_part[1] += sum[1];
   v8i32 vf[2];
@@ -1307,7 +1305,7 @@ template <int SLOT>
 __device__ __forceinline__ void single_tile(const Ctx& c, int i, Stream& st, const bf16x8_t (&qf)[2][8],
                                             f32x16_t (&o)[2][4], f32x16_t (&s)[2][2], v8i32 (&pc)[2], int (&eb)[2],
                                             float (&sum)[2], float (&l_part)[2], const f32x16_t (&negm)[2],
-                                            bool& ovf, int one) {
+                                            int one) {
   issue(c, i + NS - 1, st);
   f32x16_t unused_s[2][2];
   v8i32 vf[2];
@@ -1320,7 +1318,6 @@ __device__ __forceinline__ void single_tile(const Ctx& c, int i, Stream& st, con
     eb[b] = tile_scale(sum[b], c.eh8);
     conv_all(s[b], pc[b], eb[b]);
   }
-  ovf |= overflow(sum);
   l_part[0] += sum[0];
   l_part[1] += sum[1];
   float unused_sum;
@@ -1469,27 +1466,27 @@ __global__ __launch_bounds__(256, 1) void k_attn_f8v_d128_dual(const AttnArgs a)
 
   // Free tiles, pipelined, in passes of four (state in (s0, pc) between passes).
   int i = 0;
-  bool raised = false;
   static_assert(NS == 4, "the unrolled loop below walks the slots 0, 1, 2, 3");
   while (i + 4 < n_free) {
-    iteration<1, 0>(c, i, st, qf, o, s0, s1, pc, eb, sum, l_part, negm, raised, one);
-    iteration<2, 1>(c, i + 1, st, qf, o, s1, s0, pc, eb, sum, l_part, negm, raised, one);
-    iteration<3, 2>(c, i + 2, st, qf, o, s0, s1, pc, eb, sum, l_part, negm, raised, one);
-    iteration<0, 3>(c, i + 3, st, qf, o, s1, s0, pc, eb, sum, l_part, negm, raised, one);
+    iteration<1, 0>(c, i, st, qf, o, s0, s1, pc, eb, sum, l_part, negm, one);
+    iteration<2, 1>(c, i + 1, st, qf, o, s1, s0, pc, eb, sum, l_part, negm, one);
+    iteration<3, 2>(c, i + 2, st, qf, o, s0, s1, pc, eb, sum, l_part, negm, one);
+    iteration<0, 3>(c, i + 3, st, qf, o, s1, s0, pc, eb, sum, l_part, negm, one);
     i += 4;
   }
   drain_o(o);
-  finish_tile(c, i, st, o, s0, pc, eb, sum, l_part, raised, one);
+  finish_tile(c, i, st, o, s0, pc, eb, sum, l_part, one);
   for (++i; i < nt; ++i) {
     switch (i & 3) {
-      case 0: single_tile<0>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, raised, one); break;
-      case 1: single_tile<1>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, raised, one); break;
-      case 2: single_tile<2>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, raised, one); break;
-      default: single_tile<3>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, raised, one); break;
+      case 0: single_tile<0>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, one); break;
+      case 1: single_tile<1>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, one); break;
+      case 2: single_tile<2>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, one); break;
+      default: single_tile<3>(c, i, st, qf, o, s0, pc, eb, sum, l_part, negm, one); break;
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
 
+  const bool raised = overflow(l_part);
   int bad = 0;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
