@@ -960,7 +960,7 @@ struct Ctx {
   int sread;           // 1/s_v of the lane's keys, chunk 0 (+ 128 B per 8-key chunk)
   int lread[2];        // log2 s_v pair of the A-operand key row of key block kb
   const char* vsbase;  // scale-term copy source of this lane (1/s_v or log2 pairs)
-  int eh8;             // E_h - 8
+  int eb0;             // E_h - 7
   bf16x8_t augb;       // B operand of the log2 s_v step: bf16 (1, 1) in channels 0, 1
 };
 
@@ -1037,9 +1037,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // E8M0 byte 127 + E of a block's tile from the lane's sum of P' (see above), clamped to
-// the finite scales (the clamp only ever lowers the codes).
-__device__ __forceinline__ int tile_scale(float sum, int eh8) {
-  const int e = __builtin_amdgcn_frexp_expf(pair_sum(sum)) + eh8 + 127;
+// the finite scales (the clamp only ever lowers the codes).  The exponent is read from the
+// bits of the row's sum: for a normal sum, frexp's exponent e is its biased exponent field
+// minus 126, so 127 + E = 127 + E_h + e - 8 = field + eb0 with eb0 = E_h - 7 (one shift,
+// one add and one clamp).  A zero sum (a tile the mask hides from the row: its codes are
+// all zero) clamps to 1.
+__device__ __forceinline__ int tile_scale(float sum, int eb0) {
+  const int e = (int)(__builtin_bit_cast(unsigned, pair_sum(sum)) >> 23) + eb0;
   return min(max(e, 1), 254);
 }
 
@@ -1115,7 +1119,7 @@ __device__ __forceinline__ void soft_x(const Ctx& c, const char* sv, f32x16_t (&
   if (j < 32) exp_step(sv, c, sc[1], sum[1], inv, j);
   if (j == 32) {
     exp_finish(sc[1], sum[1], inv);
-    eb[1] = tile_scale(sum[1], c.eh8);
+    eb[1] = tile_scale(sum[1], c.eb0);
   }
   if (j == 33) {
     conv_word(sc[1], pc[1], 0, eb[1]);
@@ -1161,7 +1165,7 @@ __device__ __forceinline__ void phase_x(const Ctx& c, int t, const bf16x8_t (&qf
   }
   if (SOFT) {
     read_inv(sv, c, 0, inv[0]);
-    eb[0] = tile_scale(sum[0], c.eh8);
+    eb[0] = tile_scale(sum[0], c.eb0);
     sum[1] = 0.0f;
   }
   step_fence();
@@ -1287,10 +1291,10 @@ __device__ __forceinline__ void finish_tile(const Ctx& c, int i, Stream& st, f32
                                             float (&l_part)[2], int one) {
   issue(c, i + NS - 1, st);
   const char* sb = c.lds;  // slot 0's scale terms: S_RING is in the offsets
-  eb[0] = tile_scale(sum[0], c.eh8);
+  eb[0] = tile_scale(sum[0], c.eb0);
   conv_all(sc[0], pc[0], eb[0]);
   sum[1] = exp_all(sb, c, sc[1]);
-  eb[1] = tile_scale(sum[1], c.eh8);
+  eb[1] = tile_scale(sum[1], c.eb0);
   conv_all(sc[1], pc[1], eb[1]);
   l_part[0] += sum[0];
   l_part[1] += sum[1];
@@ -1315,7 +1319,7 @@ __device__ __forceinline__ void single_tile(const Ctx& c, int i, Stream& st, con
   for (int b = 0; b < 2; ++b) {
     mask_tile(s[b], i * BN, c.hi, c.kvis[b]);
     sum[b] = exp_all(sb, c, s[b]);
-    eb[b] = tile_scale(sum[b], c.eh8);
+    eb[b] = tile_scale(sum[b], c.eb0);
     conv_all(s[b], pc[b], eb[b]);
   }
   l_part[0] += sum[0];
@@ -1401,7 +1405,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_f8v_d128_dual(const AttnArgs a)
     for (int p = 0; p < kVmaxParts; ++p) smax = fmaxf(smax, a.vmax[h * kVmaxParts + p]);
     // s_v < 2^E_h for every key of the head
     const int eh = (smax > 0.0f && smax < INFINITY) ? __builtin_amdgcn_frexp_expf(smax) : 0;
-    c.eh8 = eh - 8;
+    c.eb0 = eh - 7;
     const u32x4_t ones = {c.hi ? 0u : 0x3F803F80u, 0u, 0u, 0u};  // bf16 (1, 1, 0, ...)
     c.augb = __builtin_bit_cast(bf16x8_t, ones);
   }
