@@ -277,3 +277,19 @@ def test_print_table(budget, capsys):
         print()
         for name, v in budget.items():
             print(f"  {name:32s} {v:.3e}" if isinstance(v, float) else f"  {name:32s} {v}")
+
+
+def test_tile_scale_exponent_from_bits():
+    """The FP8 kernel reads the exponent of a row's tile sum from its bits: for a positive
+    normal f32 x, the biased exponent field (bits >> 23) equals frexp's exponent + 126, so
+    the E8M0 byte 127 + E_h + e - 8 is field + E_h - 7.  Checked over every exponent and a
+    spread of mantissas, and at the edges (the smallest normal, the largest finite); a zero
+    sum reads field 0, below every normal, and the kernel clamps it to 1."""
+    rng = np.random.default_rng(3)
+    exps = np.arange(-126, 128)
+    mant = rng.uniform(1.0, 2.0, size=(exps.size, 64))
+    x = (mant * np.exp2(exps)[:, None]).astype(np.float32).ravel()
+    x = np.concatenate([x, np.array([np.finfo(np.float32).tiny, np.finfo(np.float32).max], np.float32)])
+    field = (x.view(np.uint32) >> 23).astype(np.int64)
+    assert np.array_equal(field, np.frexp(x)[1].astype(np.int64) + 126)
+    assert (np.float32(0.0).view(np.uint32) >> 23) == 0
