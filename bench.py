@@ -213,8 +213,10 @@ def main():
     peak = PEAK[op]
     # algorithmic bytes of the streaming kernels (per step)
     hist_k = n_hist * (fe * (kvb + ob) + sb)         # stored K read, rotated operand written
-    # the block: q, k, v read; qrot, krot written in the operand dtype, v in the kv dtype
-    cur = B * (fe * (5 * ob + kvb) + sb)
+    # the block: q, k read and qrot, krot written in the operand dtype; an FP8 cache's V
+    # also read and written as codes + row scales (a bf16 or f32 cache's attention reads the
+    # block's V where the caller passed it, so the pass does not touch it)
+    cur = B * (fe * (5 * ob + kvb) + sb) if dt == "fp8" else B * fe * 4 * ob
     # FP8: every key's V scale read, its three attention-order terms written
     vstage = Lk * H * 16 if dt == "fp8" else 0
     rope_bytes = hist_k + cur + vstage

@@ -379,6 +379,7 @@ class Cache:
         self.T = c.grid_h * c.grid_w
         self.H, self.D = c.heads, c.head_dim
         self.io_dtype = _TORCH_DTYPE[c.q_dtype]
+        self._v_held = None   # v_cur of the last RoPE call (see rope_reset_apply)
 
     def close(self):
         if self.h:
@@ -406,6 +407,9 @@ class Cache:
             lact_rope_reset_apply(self.h, q, k_cur, v_cur, n, stream)
         else:
             lact_member_rope_reset_apply(self.h, member, q, k_cur, v_cur, n, stream)
+        # a bf16 or f32 cache's attention reads the block's V from v_cur: hold the tensor so
+        # its memory is not handed to another tensor before that attention call has run
+        self._v_held = v_cur
 
     def block_attention(self, q_block_frames=None, out=None, lse=None, stream=None, member=0):
         st = self.state()

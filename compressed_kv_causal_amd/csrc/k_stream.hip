@@ -276,10 +276,12 @@ __device__ __forceinline__ void rope_rotate8(const float2* cs, float* x) {
 // rotated at t = fi into krot[h][fi*T + u] (only when the history is rebuilt, else the grid
 // starts at the block's frames); frames after are the block's frames i = fi - n_hist at
 // t = fi: q -> qrot (times q_scale = log2(e)/sqrt(D), so that q . k is the base-2 exponent
-// of the softmax), k -> krot[h][t*T + u], v -> vcur.  krot and qrot are in the operand
-// dtype (in_dtype); an FP8 cache's keys are read as code * row scale.  An FP8 cache's
-// attention reads V as stored (codes), so the pass leaves history V alone and quantises
-// the block's V like the cache stores it (codes to vcur, row scales to vcur_scale).
+// of the softmax), k -> krot[h][t*T + u].  krot and qrot are in the operand dtype
+// (in_dtype); an FP8 cache's keys are read as code * row scale.  V is never copied as it
+// is: history V is read by the attention where the cache stores it, and so is the block's
+// V of a bf16 or f32 cache, in the caller's buffer (the same layout and dtype).  An FP8
+// cache's attention reads V as e4m3 codes, so the pass quantises the block's V like the
+// cache will store it (codes to vcur, row scales to vcur_scale).
 //
 // Work split: blockIdx.x = a run of TPB tokens, so the tokens and their grid coordinates
 // are scalars; the workgroup's lanes cover a token's H x D/8 chunks (LPR consecutive lanes
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
       float2 cs[4];
       load8_in(a.q, IN, crow * D + li * 8, xq);
       load8_in(a.k_cur, IN, crow * D + li * 8, xk);
-      load8_in(a.v_cur, IN, crow * D + li * 8, xv);
+      if (fp8) load8_in(a.v_cur, IN, crow * D + li * 8, xv);
       rope_cs(a, fi, u[t], gr[t], gc[t], li, cs);
       rope_rotate8(cs, xq);
 #pragma unroll
@@ -352,8 +354,6 @@ __global__ __launch_bounds__(1024) void k_rope(const RopeArgs a) {
       if (fp8) {
         const float sc = store8_kv<LPR>(a.vcur, DT_FP8, crow * D + li * 8, xv);
         if (li == 0) a.vcur_scale[crow] = sc;
-      } else {
-        store8_op(a.vcur, IN, crow * D + li * 8, xv);
       }
     }
   }

@@ -147,6 +147,7 @@ struct lact_cache {
   uint64_t staged_version = 0;  // ... of this state version
   int32_t staged_frames = 0;
   int32_t staged_member = 0;
+  const void* staged_v = nullptr;  // the block's V as passed to the RoPE call (bf16, f32)
   bool hist_built = false;    // the staged history (krot, FP8 vscale) is hist_member's ...
   uint64_t hist_version = 0;  // ... at this version
   int32_t hist_member = 0;
@@ -361,6 +362,7 @@ lact_status lact_member_rope_reset_apply(lact_cache* c, int32_t member, const vo
   c->staged_version = c->plan.version();
   c->staged_frames = n_frames;
   c->staged_member = member;
+  c->staged_v = v_cur;
   return LACT_OK;
 }
 
@@ -460,7 +462,9 @@ static lact_status block_attention_impl(lact_cache* c, int32_t member, const int
   }
   a.q = c->at(c->lay.qrot);
   a.k = c->at(c->lay.krot);
-  a.v_cur = c->at(c->lay.vcur);
+  // the block's V: an FP8 cache's as staged e4m3 codes, otherwise where the caller passed
+  // it to the RoPE call (same layout and dtype as the staging; see lact.h)
+  a.v_cur = g.kv_dtype == LACT_FP8_E4M3 ? static_cast<const void*>(c->at(c->lay.vcur)) : c->staged_v;
   a.out = out;
   a.lse = lse;
   if (static_queue) {

@@ -229,7 +229,10 @@ lact_status lact_member_ref_set(lact_cache* cache, int32_t member, const void* k
  * ref_frames); (h, w) = the token's grid cell.  Rotation of interleaved channel pairs
  * (2i, 2i+1) of each part by pos * theta^(-2i/d_part).
  * Writes krot (reference + memory + window + current keys) and qrot in the operand dtype
- * (q_dtype), and the block's V to vcur in the kv dtype.  The stored history keys are read
+ * (q_dtype).  A BF16 or F32 cache copies no V: the attention reads the block's V in v_cur
+ * itself, which must therefore stay unchanged until the lact_block_attention call that
+ * follows has run on the stream (the same V goes to lact_kv_ring_append after it).  The
+ * stored history keys are read
  * as stored (FP8_E4M3: code * per-(token, head) scale; the model card's FP8 KV cache option
  * keeps K/V in FP8 and dequantises them for use).  An FP8 cache's V stays in e4m3 for the
  * attention: the pass quantises the block's V per (token, head) row as the cache stores it
@@ -255,6 +258,8 @@ lact_status lact_member_rope_reset_apply(lact_cache* cache, int32_t member, cons
  *   q_block_frames: HOST array of n_q_blocks block sizes in frames, summing to the staged
  *                   frame count; NULL means one block of all staged frames.
  *   out: [n*T][H][D] in q_dtype.  lse: [H][n*T] f32 natural-log log-sum-exp, or NULL.
+ * The block's V is read from the v_cur of the RoPE call (BF16, F32 caches) or from its
+ * staged e4m3 codes (FP8_E4M3).
  * LACT_E_STATE unless lact_rope_reset_apply ran at the present state version. */
 lact_status lact_block_attention(lact_cache* cache, const int32_t* q_block_frames,
                                  int32_t n_q_blocks, void* out, float* lse, void* stream);
